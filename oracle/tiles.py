@@ -1,0 +1,89 @@
+"""Tile classes and unmasked-entry counts (oracle; test infrastructure only).
+
+The FlashMask article ("FlashMask技术：大模型训练中的高效注意力掩码优化",
+§2.2) decides, for every pair of a query block and a key/value block, one of
+three cases: skip the block, compute it as a plain (full) GEMM, or compute it
+with the per-row mask applied.  The printed code is garbled (it compares
+only one row's start and never looks at the right-hand side), so the reading
+used here is the plain one that the section's text and its "about half of
+the causal work is skipped" claim support:
+
+* SKIP    when the key block lies entirely left of every row's start or
+          entirely right of every row's end:
+              khi < min_r col_start[r]   or   klo > max_r col_end[r];
+* FULL    when the key block lies inside every row's interval:
+              klo >= max_r col_start[r]  and  khi <= min_r col_end[r];
+* PARTIAL otherwise,
+
+with klo = j*Bc, khi = min(klo + Bc, N) - 1 and r over the rows
+[t*Br, min(t*Br + Br, N) - 1] of query block t.  Encoding (page order):
+SKIP = 0, FULL = 1, PARTIAL = 2, table row-major [n_q][n_kv].
+
+``classes_dense`` is a second, independent rule used to guard the first:
+count the attended entries of the dense mask inside the tile (0 -> SKIP,
+all -> FULL, else PARTIAL).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import dense_mask
+
+SKIP, FULL, PARTIAL = 0, 1, 2
+
+
+def classes_minmax(col_start, col_end, N: int, Br: int, Bc: int) -> np.ndarray:
+    """Min/max rule over one sequence's valid intervals (0 <= s <= e <= N-1)."""
+    s = [int(x) for x in col_start]
+    e = [int(x) for x in col_end]
+    n_q = -(-N // Br)
+    n_kv = -(-N // Bc)
+    out = np.empty((n_q, n_kv), dtype=np.uint8)
+    for t in range(n_q):
+        rows = range(t * Br, min(t * Br + Br, N))
+        min_s = min(s[r] for r in rows)
+        max_s = max(s[r] for r in rows)
+        min_e = min(e[r] for r in rows)
+        max_e = max(e[r] for r in rows)
+        for j in range(n_kv):
+            klo = j * Bc
+            khi = min(klo + Bc, N) - 1
+            if khi < min_s or klo > max_e:
+                out[t, j] = SKIP
+            elif klo >= max_s and khi <= min_e:
+                out[t, j] = FULL
+            else:
+                out[t, j] = PARTIAL
+    return out
+
+
+def classes_dense(col_start, col_end, N: int, Br: int, Bc: int) -> np.ndarray:
+    """Dense-exact rule: classify each tile by counting its attended entries."""
+    n_q = -(-N // Br)
+    n_kv = -(-N // Bc)
+    out = np.empty((n_q, n_kv), dtype=np.uint8)
+    for t in range(n_q):
+        rows = np.arange(t * Br, min(t * Br + Br, N))
+        M = dense_mask(col_start, col_end, N, rows)
+        for j in range(n_kv):
+            klo = j * Bc
+            khi = min(klo + Bc, N) - 1
+            block = M[:, klo:khi + 1]
+            count = int(block.sum())
+            if count == 0:
+                out[t, j] = SKIP
+            elif count == block.size:
+                out[t, j] = FULL
+            else:
+                out[t, j] = PARTIAL
+    return out
+
+
+def unmasked_count(col_start, col_end, N: int) -> int:
+    """Number of attended (query, key) pairs of one sequence, counted from the dense mask
+    one row block at a time."""
+    total = 0
+    for r0 in range(0, N, 1024):
+        rows = np.arange(r0, min(r0 + 1024, N))
+        total += int(dense_mask(col_start, col_end, N, rows).sum())
+    return total

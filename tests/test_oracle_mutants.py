@@ -1,0 +1,77 @@
+"""Planted mistakes: every plausible slip in the oracle must be caught by a pin (CPU).
+
+Each mutant is a textual change to a copy of an oracle module's source,
+executed in a fresh namespace; the real oracle files are never touched.
+"""
+import importlib
+import os
+import types
+
+import pytest
+
+import test_oracle
+import test_oracle_tiles
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+
+def _mutant(module_file, old, new, extra_globals=None):
+    with open(os.path.join(ORACLE_DIR, module_file), encoding="utf-8") as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation site not found: {old!r}"
+    src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    mod.__dict__.update(extra_globals or {})
+    code = compile(src.replace("from .attention import dense_mask", ""), module_file, "exec")
+    exec(code, mod.__dict__)
+    return mod
+
+
+def _caught(pins, fn):
+    for pin in pins:
+        try:
+            pin(fn)
+        except Exception:          # a failed assertion or a crash both expose the mutant
+            return True
+    return False
+
+
+ATTN_MUTANTS = {
+    "exclusive_end": ("(j[None, :] <= e[:, None])", "(j[None, :] < e[:, None])"),
+    "exclusive_start": ("(j[None, :] >= s[:, None])", "(j[None, :] > s[:, None])"),
+    "dropped_scale": ("S = scale64 * (qh @ kh.T)", "S = (qh @ kh.T)"),
+    "scale_squared": ("S = scale64 * (qh @ kh.T)", "S = scale64 * scale64 * (qh @ kh.T)"),
+    "lse_without_max": ("m[ok] + np.log(l[ok])", "np.log(l[ok])"),
+    "unnormalised": ("num[ok] / l[ok][:, None]", "num[ok]"),
+    "k_for_v": ("vh = np.asarray(v[b, h][support]", "vh = np.asarray(k[b, h][support]"),
+    "mask_ignored": ("S = np.where(Ms, S, -np.inf)", "S = S"),
+    "off_by_one_row": ("qh = np.asarray(q[b, h][rr]", "qh = np.asarray(q[b, h][np.maximum(rr - 1, 0)]"),
+    "log2_lse": ("m[ok] + np.log(l[ok])", "m[ok] + np.log2(l[ok])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attention_mutant_is_caught(name):
+    old, new = ATTN_MUTANTS[name]
+    mod = _mutant("attention.py", old, new)
+    assert _caught(test_oracle.ALL_PINS, mod.attention), f"mutant {name} survived every pin"
+
+
+TILE_MUTANTS = {
+    "skip_left_inclusive": ("if khi < min_s or klo > max_e:", "if khi <= min_s or klo > max_e:"),
+    "skip_right_inclusive": ("if khi < min_s or klo > max_e:", "if khi < min_s or klo >= max_e:"),
+    "no_right_skip": ("if khi < min_s or klo > max_e:", "if khi < min_s:"),
+    "khi_exclusive": ("khi = min(klo + Bc, N) - 1\n            if khi < min_s", "khi = min(klo + Bc, N)\n            if khi < min_s"),
+    "full_swapped_bounds": ("elif klo >= max_s and khi <= min_e:", "elif klo >= min_s and khi <= max_e:"),
+    "full_start_only": ("elif klo >= max_s and khi <= min_e:", "elif klo >= max_s:"),
+    "page_literal_skip": ("if khi < min_s or klo > max_e:", "if khi + 1 <= s[rows[-1]]:"),
+    "rows_not_clipped": ("rows = range(t * Br, min(t * Br + Br, N))", "rows = range(t * Br, min(t * Br + Br, N - 1))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TILE_MUTANTS))
+def test_tile_mutant_is_caught(name):
+    import oracle
+    old, new = TILE_MUTANTS[name]
+    mod = _mutant("tiles.py", old, new, {"dense_mask": oracle.dense_mask})
+    assert _caught(test_oracle_tiles.ALL_PINS, mod.classes_minmax), f"mutant {name} survived every pin"
