@@ -1,0 +1,244 @@
+"""Benchmark of the FlashMask forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2] [--no-per-config]
+                    [--no-cpu-baseline]
+
+A step is one fm_attn_fwd call (interval preprocessor + scheduler + attention
+kernel) over one batch of the workload, inputs resident in HBM.  Prints ONE
+JSON line: effective TFLOP/s counting 4*d FLOPs per attended (query, key)
+pair, the attention kernel's roofline figures (its own duration measured with
+HIP events the library records on its stream), the other workloads' figures
+under "per_config", and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "effective masked-attn fwd TFLOP/s (unmasked FLOPs) + % of bf16 MFMA peak"
+DEFAULT_CONFIG = "C2"
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def tile_stats(fm, spec, cfg, dev):
+    """Skip / partial ratios at the kernel's tile shape, from the GPU class table."""
+    import torch
+    Br, Bc = fm.fm_attn_tile_shape(cfg.d)
+    skip = part = total = 0
+    nonskip = 0
+    for b in range(cfg.B):
+        s = torch.from_numpy(spec.col_start[b]).to(dev)
+        e = torch.from_numpy(spec.col_end[b]).to(dev)
+        tab = fm.fm_classify_tiles(s, e, Br, Bc).cpu().numpy()
+        skip += int((tab == fm.FM_TILE_SKIP).sum())
+        part += int((tab == fm.FM_TILE_PARTIAL).sum())
+        total += tab.size
+        nonskip += int((tab != fm.FM_TILE_SKIP).sum())
+    executed = 4 * cfg.d * Br * Bc * nonskip * cfg.H
+    return {"Br": Br, "Bc": Bc, "skip_ratio": skip / total, "partial_ratio": part / total,
+            "tile_executed_flops": executed}
+
+
+def time_config(cfg, steps, warmup, with_kernel_timer=True):
+    import torch
+    from masked_attention_fm_amd import flashmask as fm
+    from masked_attention_fm_amd import inputs, metrics
+
+    dev = torch.device("cuda:0")
+    spec = inputs.config_intervals(cfg)
+    t0 = time.time()
+    q, k, v = inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    q, k, v = (x.to(dev) for x in (q, k, v))
+    cs = torch.from_numpy(spec.col_start).to(dev)
+    ce = torch.from_numpy(spec.col_end).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
+    scale = inputs.default_scale(cfg.d)
+    log(f"{cfg.key}: inputs ready in {time.time() - t0:.1f}s ({cfg.describe()})")
+
+    U = metrics.attended_pairs(spec.col_start, spec.col_end, cfg.N) * cfg.H
+    flops = 4 * cfg.d * U
+    stream = torch.cuda.current_stream()
+
+    for _ in range(warmup):
+        fm.fm_attn_fwd(q, k, v, cs, ce, scale, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    fm.fm_profile_read()                       # drop anything recorded before
+    if with_kernel_timer:
+        fm.fm_profile_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fm.fm_attn_fwd(q, k, v, cs, ce, scale, out=out, lse=lse, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    fm.fm_profile_enable(False)
+    total_ms = start.elapsed_time(stop)
+    kern_ms, launches = fm.fm_profile_read()
+    ms_step = total_ms / steps
+    res = {
+        "key": cfg.key,
+        "workload": cfg.name,
+        "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "mask": cfg.mask, "seed": cfg.seed,
+        "attended_pairs": U,
+        "effective_flops": flops,
+        "ms_per_step": ms_step,
+        "effective_tflops": flops / (ms_step * 1e-3) / 1e12,
+    }
+    if launches:
+        kms = kern_ms / launches
+        res["attn_kernel_ms"] = kms
+        res["attn_kernel_tflops"] = flops / (kms * 1e-3) / 1e12
+    res["pct_of_bf16_peak"] = 100.0 * res["effective_tflops"] / metrics.MI355X_BF16_DENSE_TFLOPS
+    res.update(tile_stats(fm, spec, cfg, dev))
+    res["tile_executed_tflops"] = res["tile_executed_flops"] / (ms_step * 1e-3) / 1e12
+    if cfg.mask.startswith("doc"):
+        res["documents"] = [len(L) for L in spec.doc_lengths]
+    if cfg.mask == "prefix_lm":
+        res["prefix"] = spec.prefix
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, target_s):
+    """The float64 oracle on whole heads of the workload until about target_s seconds."""
+    import oracle
+    from masked_attention_fm_amd import inputs, metrics
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    spec = inputs.config_intervals(cfg)
+    scale = inputs.default_scale(cfg.d)
+    done = []
+    t0 = time.time()
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            sl = [inputs.qkv_slice(cfg.seed, n, b, h, cfg.N, cfg.d).float().numpy()[None, None]
+                  for n in "qkv"]
+            t1 = time.time()
+            oracle.attention(*sl, spec.col_start[b:b + 1], spec.col_end[b:b + 1], scale)
+            done.append((b, h, time.time() - t1))
+            if sum(x[2] for x in done) >= target_s:
+                break
+        if sum(x[2] for x in done) >= target_s:
+            break
+    secs = sum(x[2] for x in done)
+    per_head_pairs = {b: metrics.attended_pairs(spec.col_start[b], spec.col_end[b], cfg.N) for b in range(cfg.B)}
+    flops = sum(4 * cfg.d * per_head_pairs[b] for b, _, _ in done)
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {cfg.B * cfg.H} (b,h) heads of {cfg.key}, all rows, "
+                      f"{secs:.1f}s float64 numpy (dense mask per 128-row block)",
+            "seconds": secs, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, HERE)
+    import torch
+    from masked_attention_fm_amd import inputs, metrics
+    from masked_attention_fm_amd import flashmask as fm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if not os.path.exists(fm.LIB_PATH):
+        from masked_attention_fm_amd import build as _build
+        _build.build()
+    fm.lib()
+
+    cfg = inputs.CONFIGS[args.config]
+    main_res = time_config(cfg, args.steps, args.warmup)
+    log(f"{cfg.key}: {main_res['effective_tflops']:.1f} TFLOP/s effective, {main_res['ms_per_step']:.4f} ms/step")
+
+    per_config = {}
+    if not args.no_per_config:
+        for key, c in inputs.CONFIGS.items():
+            if key == cfg.key:
+                continue
+            steps = 200 if c.N <= 1024 else max(5, min(args.steps, 20))
+            r = time_config(c, steps, min(args.warmup, 5))
+            log(f"{key}: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
+            per_config[key] = {k: r[k] for k in ("workload", "ms_per_step", "effective_tflops",
+                                                 "pct_of_bf16_peak", "attn_kernel_ms", "attn_kernel_tflops",
+                                                 "skip_ratio", "partial_ratio", "tile_executed_tflops")
+                               if k in r}
+
+    kms = main_res.get("attn_kernel_ms")
+    roofline = {
+        "bound": "mfma",
+        "achieved": main_res.get("attn_kernel_tflops"),
+        "peak": metrics.MI355X_BF16_DENSE_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": (main_res["attn_kernel_tflops"] / metrics.MI355X_BF16_DENSE_TFLOPS) if kms else None,
+        "traffic": None,
+        "kernel": "attn_fwd_kernel<128>" if cfg.d == 128 else "attn_fwd_kernel<64>",
+        "kernel_ms": kms,
+        "algorithmic_flops_per_launch": main_res["effective_flops"],
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": main_res["effective_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.key} {cfg.name}", "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d,
+                   "mask": cfg.mask, "seed": cfg.seed, "global_batch": cfg.B, "seq_len": cfg.N,
+                   "parallelism": "single-gpu"},
+        "pct_of_bf16_peak": main_res["pct_of_bf16_peak"],
+        "skip_ratio": main_res["skip_ratio"],
+        "partial_ratio": main_res["partial_ratio"],
+        "tile_shape": [main_res["Br"], main_res["Bc"]],
+        "tile_executed_tflops": main_res["tile_executed_tflops"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * flashmask.h -- C ABI of the FlashMask forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * The method (web page "FlashMask技术：大模型训练中的高效注意力掩码优化", the
+ * FlashMask article):
+ *   - the attention mask is not stored as an N x N matrix; each query row i
+ *     attends the inclusive key range [col_start[i], col_end[i]] (§1, §2.1,
+ *     and the inclusive element compare of §4.1 item 3);
+ *   - every (query block, key/value block) pair is classified as skip, full
+ *     or partial (§2.2); skipped blocks are never loaded (§4.1 item 2), full
+ *     blocks run the plain fused product, partial blocks also apply the
+ *     element compare fused into the score (§4.1 item 3);
+ *   - the softmax is the max-subtracted one of the FlashAttention article
+ *     ("FlashAttention优化：高效训练长上下文GPT的技术突破", §2 item 2), evaluated
+ *     blockwise with rescaling so the result equals dense masked attention
+ *     (FlashMask article §2.2, last paragraph).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *     owned by the caller.  The library keeps no pointer after returning.
+ *   - Return value: an fm_status code.  No call throws or aborts.
+ *   - Intervals are int32; row r of batch b is element b*N + r.
+ */
+#ifndef FLASHMASK_H
+#define FLASHMASK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define FM_API __attribute__((visibility("default")))
+#else
+#define FM_API
+#endif
+
+typedef enum fm_status {
+    FM_OK = 0,
+    FM_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer, bad scale   */
+    FM_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128                      */
+    FM_ERR_BAD_INTERVAL = 3,  /* fm_classify_tiles: some row violates 0 <= s <= e <= N-1  */
+    FM_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed               */
+} fm_status;
+
+/* Tile classes, in the order the FlashMask article §2.2 lists the cases. */
+enum { FM_TILE_SKIP = 0, FM_TILE_FULL = 1, FM_TILE_PARTIAL = 2 };
+
+/*
+ * fm_classify_tiles -- the tile-class table of one sequence (FlashMask article §2.2).
+ *
+ *   col_start, col_end : int32[N] device, the intervals of one sequence
+ *                        (for batch b pass col_start + b*N).
+ *   N                  : sequence length, N >= 1.
+ *   Br, Bc             : query and key block sizes, >= 1 (any value, not only
+ *                        the attention kernel's own).
+ *   class_out          : uint8[ceil(N/Br)][ceil(N/Bc)] device, row-major.
+ *
+ * For query block t (rows t*Br .. min(t*Br+Br, N)-1) and key block j
+ * (klo = j*Bc, khi = min(klo+Bc, N)-1):
+ *   SKIP    if khi < min col_start  or  klo > max col_end over the block's rows,
+ *   FULL    if klo >= max col_start and khi <= min col_end,
+ *   PARTIAL otherwise.
+ * Synchronous: runs on the null stream and returns after the table is
+ * written, so the caller must have finished writing the intervals.
+ * Returns FM_ERR_BAD_INTERVAL when any row breaks 0 <= s <= e <= N-1 (the
+ * table is still written, from the intervals clamped to [0, N-1]).
+ */
+FM_API int fm_classify_tiles(const int32_t* col_start, const int32_t* col_end, int64_t N,
+                             int32_t Br, int32_t Bc, uint8_t* class_out);
+
+/*
+ * fm_attn_fwd -- masked attention forward: O = softmax(scale * Q K^T + M) V and
+ * LSE = ln sum_j exp(scale * q_i . k_j) over the attended keys.
+ *
+ *   q, k, v   : bfloat16 [B][H][N][d] device, contiguous, 16-byte aligned.
+ *   col_start, col_end : int32 [B][N] device, shared by all H heads; row i of
+ *               batch b attends keys j in [0, N) with col_start <= j <= col_end.
+ *               Any int32 values are accepted: a row whose range holds no key
+ *               of [0, N) attends nothing and gets O = 0, LSE = -inf.
+ *   B, H, N   : >= 1, N <= 2^28, B*H*ceil(N/128) < 2^31.
+ *   d         : head dimension, 64 or 128 (else FM_ERR_UNSUPPORTED).
+ *   scale     : finite and > 0 (typically 1/sqrt(d)).
+ *   out       : bfloat16 [B][H][N][d] device, 16-byte aligned (round to nearest even).
+ *   lse       : float32  [B][H][N] device, natural log.
+ *   stream    : HIP stream the work is queued on (0 = null stream).
+ *
+ * Asynchronous on `stream`: returns once the three kernels (interval
+ * preprocessor, scheduler, attention) are queued.  Inputs must not alias the
+ * outputs.  The library keeps a small internal workspace per (device, stream),
+ * grown in stream order; the call never synchronizes the device.
+ * Errors: argument checks happen on the host before any HIP call
+ * (FM_ERR_INVALID_ARG / FM_ERR_UNSUPPORTED); a failed allocation or launch
+ * returns FM_ERR_HIP (see fm_last_hip_error).
+ */
+FM_API int fm_attn_fwd(const void* q, const void* k, const void* v,
+                       const int32_t* col_start, const int32_t* col_end,
+                       int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       void* out, float* lse, hipStream_t stream);
+
+/* The query and key block sizes the attention kernel uses for head dimension d
+ * (the shape at which tiles are skipped).  FM_ERR_UNSUPPORTED for other d. */
+FM_API int fm_attn_tile_shape(int64_t d, int32_t* Br, int32_t* Bc);
+
+/*
+ * fm_tile_schedule -- inspection of the work ordering fm_attn_fwd uses
+ * (FlashMask article §4.3 item 3: hand out work by each query block's
+ * number of effective key blocks).
+ *
+ *   col_start, col_end : int32 [B][N] device.
+ *   work_out  : int32 [B*ceil(N/Br)] device; non-skip key blocks of query
+ *               block t of batch b at index b*ceil(N/Br) + t.
+ *   order_out : int32 [B*ceil(N/Br)] device; those indices sorted by work,
+ *               largest first, ties by increasing index.
+ * Br, Bc are fm_attn_tile_shape(d).  Synchronous (null stream).
+ */
+FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end,
+                            int64_t B, int64_t N, int64_t d,
+                            int32_t* work_out, int32_t* order_out);
+
+/* Process-wide options (not synchronized with calls in flight on other threads). */
+enum {
+    FM_OPT_SCHEDULE = 1       /* 0: longest-first order (default), 1: natural (b, t) order */
+};
+FM_API int fm_set_option(int option, int64_t value);
+
+/*
+ * Timing of the attention kernel alone, for measurement.  While enabled,
+ * fm_attn_fwd records a HIP event pair on its stream around the attention
+ * kernel launch.  fm_profile_read waits for the recorded events, returns
+ * the summed kernel time in milliseconds and the number of launches, and
+ * clears the record.
+ */
+FM_API int fm_profile_enable(int enable);
+FM_API int fm_profile_read(double* total_ms, int64_t* launches);
+
+/* Text for a status code, and the HIP error code of the last failing HIP call
+ * made by this thread inside the library (0 if none). */
+FM_API const char* fm_status_string(int status);
+FM_API int fm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHMASK_H */

@@ -1,0 +1,242 @@
+// C ABI of libflashmask: argument checks, workspace, kernel launches.
+// The operations and their contracts are stated in include/flashmask.h.
+
+#include <math.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "flashmask.h"
+#include "fm_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return FM_ERR_HIP;
+}
+
+#define FM_HIP(call)                          \
+    do {                                      \
+        hipError_t e_ = (call);               \
+        if (e_ != hipSuccess) return hip_fail(e_); \
+    } while (0)
+
+constexpr int64_t kMaxN = int64_t(1) << 28;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// ---------------------------------------------------------------- options
+
+int g_schedule_mode = 0;   // 0 longest first, 1 natural order
+
+// ---------------------------------------------------------------- workspace
+//
+// fm_attn_fwd needs per query block: 16 B of tile metadata, its work count
+// and its place in the launch order.  One buffer per (device, stream) is
+// kept and grown in stream order, so back-to-back calls on a stream reuse it
+// and calls on different streams never share it.
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.bytes < bytes) {
+        if (w.ptr != nullptr) {
+            e = hipFreeAsync(w.ptr, stream);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        size_t nb = std::max(bytes, size_t(64) << 10);
+        nb = (nb + 0xFFFF) & ~size_t(0xFFFF);
+        e = hipMallocAsync(&w.ptr, nb, stream);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = nb;
+    }
+    *out = w.ptr;
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------- timing
+
+struct Timing {
+    std::mutex mu;
+    bool enabled = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+} g_timing;
+
+}  // namespace
+
+extern "C" {
+
+FM_API const char* fm_status_string(int status) {
+    switch (status) {
+        case FM_OK: return "ok";
+        case FM_ERR_INVALID_ARG: return "invalid argument";
+        case FM_ERR_UNSUPPORTED: return "unsupported head dimension";
+        case FM_ERR_BAD_INTERVAL: return "interval outside 0 <= col_start <= col_end <= N-1";
+        case FM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+FM_API int fm_last_hip_error(void) { return g_last_hip_error; }
+
+FM_API int fm_attn_tile_shape(int64_t d, int32_t* Br, int32_t* Bc) {
+    if (Br == nullptr || Bc == nullptr) return FM_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
+    *Br = fm::kBr;
+    *Bc = fm::kBc;
+    return FM_OK;
+}
+
+FM_API int fm_set_option(int option, int64_t value) {
+    if (option == FM_OPT_SCHEDULE) {
+        if (value != 0 && value != 1) return FM_ERR_INVALID_ARG;
+        g_schedule_mode = (int)value;
+        return FM_OK;
+    }
+    return FM_ERR_INVALID_ARG;
+}
+
+FM_API int fm_profile_enable(int enable) {
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    g_timing.enabled = enable != 0;
+    return FM_OK;
+}
+
+FM_API int fm_profile_read(double* total_ms, int64_t* launches) {
+    if (total_ms == nullptr || launches == nullptr) return FM_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    double sum = 0.0;
+    int status = FM_OK;
+    for (auto& ev : g_timing.pending) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(ev.second);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev.first, ev.second);
+        if (e != hipSuccess) status = hip_fail(e);
+        sum += ms;
+        g_timing.pool.push_back(ev);
+    }
+    *launches = (int64_t)g_timing.pending.size();
+    *total_ms = sum;
+    g_timing.pending.clear();
+    return status;
+}
+
+FM_API int fm_classify_tiles(const int32_t* col_start, const int32_t* col_end, int64_t N, int32_t Br,
+                             int32_t Bc, uint8_t* class_out) {
+    if (col_start == nullptr || col_end == nullptr || class_out == nullptr) return FM_ERR_INVALID_ARG;
+    if (N < 1 || N > kMaxN || Br < 1 || Bc < 1 || Br > kMaxN || Bc > kMaxN) return FM_ERR_INVALID_ARG;
+    if (!aligned(col_start, 4) || !aligned(col_end, 4)) return FM_ERR_INVALID_ARG;
+    const int64_t n_q = (N + Br - 1) / Br;
+    const int64_t n_kv = (N + Bc - 1) / Bc;
+    void* buf = nullptr;
+    FM_HIP(hipMalloc(&buf, (size_t)n_q * sizeof(fm::TileMeta) + 16));
+    auto* meta = static_cast<fm::TileMeta*>(buf);
+    auto* bad = reinterpret_cast<int32_t*>(static_cast<char*>(buf) + n_q * sizeof(fm::TileMeta));
+    int bad_host = 0;
+    hipError_t e = hipMemsetAsync(bad, 0, sizeof(int32_t), 0);
+    if (e == hipSuccess) e = fm::launch_preprocess(col_start, col_end, 1, N, Br, Bc, meta, nullptr, bad, 0);
+    if (e == hipSuccess) e = fm::launch_class_table(meta, n_q, n_kv, class_out, 0);
+    if (e == hipSuccess) e = hipMemcpy(&bad_host, bad, sizeof(int32_t), hipMemcpyDeviceToHost);
+    hipError_t ef = hipFree(buf);
+    if (e != hipSuccess) return hip_fail(e);
+    if (ef != hipSuccess) return hip_fail(ef);
+    return bad_host ? FM_ERR_BAD_INTERVAL : FM_OK;
+}
+
+FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
+                            int64_t d, int32_t* work_out, int32_t* order_out) {
+    if (col_start == nullptr || col_end == nullptr || work_out == nullptr || order_out == nullptr)
+        return FM_ERR_INVALID_ARG;
+    if (B < 1 || N < 1 || N > kMaxN) return FM_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
+    const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
+    if (B * n_q >= (int64_t(1) << 31)) return FM_ERR_INVALID_ARG;
+    void* buf = nullptr;
+    FM_HIP(hipMalloc(&buf, (size_t)(B * n_q) * sizeof(fm::TileMeta)));
+    hipError_t e = fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc,
+                                         static_cast<fm::TileMeta*>(buf), work_out, nullptr, 0);
+    if (e == hipSuccess) e = fm::launch_schedule(work_out, B * n_q, order_out, 0);
+    if (e == hipSuccess) e = hipStreamSynchronize(0);
+    hipError_t ef = hipFree(buf);
+    if (e != hipSuccess) return hip_fail(e);
+    if (ef != hipSuccess) return hip_fail(ef);
+    return FM_OK;
+}
+
+FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_t* col_start,
+                       const int32_t* col_end, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       void* out, float* lse, hipStream_t stream) {
+    // ---- host-side checks, before any HIP call
+    if (q == nullptr || k == nullptr || v == nullptr || col_start == nullptr || col_end == nullptr ||
+        out == nullptr || lse == nullptr)
+        return FM_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN) return FM_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
+    if (!(scale > 0.f) || !isfinite(scale)) return FM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4) || !aligned(col_start, 4) || !aligned(col_end, 4))
+        return FM_ERR_INVALID_ARG;
+    const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
+    if (B * H * n_q >= (int64_t(1) << 31) || B * N >= (int64_t(1) << 40)) return FM_ERR_INVALID_ARG;
+
+    // ---- workspace: meta[M] | work[M] | order[M]
+    const int64_t M = B * n_q;
+    const size_t meta_bytes = ((size_t)M * sizeof(fm::TileMeta) + 255) & ~size_t(255);
+    const size_t int_bytes = ((size_t)M * sizeof(int32_t) + 255) & ~size_t(255);
+    void* ws = nullptr;
+    FM_HIP(get_workspace(stream, meta_bytes + 2 * int_bytes, &ws));
+    auto* meta = static_cast<fm::TileMeta*>(ws);
+    auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes);
+    auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes + int_bytes);
+
+    FM_HIP(fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc, meta, work, nullptr, stream));
+    const bool natural = g_schedule_mode == 1;
+    if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream));
+
+    std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+    {
+        std::lock_guard<std::mutex> lock(g_timing.mu);
+        if (g_timing.enabled) {
+            if (!g_timing.pool.empty()) {
+                ev = g_timing.pool.back();
+                g_timing.pool.pop_back();
+            } else {
+                FM_HIP(hipEventCreate(&ev.first));
+                FM_HIP(hipEventCreate(&ev.second));
+            }
+        }
+    }
+    if (ev.first != nullptr) FM_HIP(hipEventRecord(ev.first, stream));
+    FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, meta, natural ? nullptr : order, B, H, N, d,
+                                scale, out, lse, stream));
+    if (ev.first != nullptr) {
+        FM_HIP(hipEventRecord(ev.second, stream));
+        std::lock_guard<std::mutex> lock(g_timing.mu);
+        g_timing.pending.push_back(ev);
+    }
+    return FM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,363 @@
+// Masked attention forward kernel for gfx950 (MI355X).
+//
+// Method: FlashMask article ("FlashMask技术：大模型训练中的高效注意力掩码优化")
+//   §2.2  skip / full / partial decision per (query block, key block);
+//   §4.1  intervals cached on chip (item 1), skip decided before any key or
+//         value is loaded (item 2), inclusive interval compare fused into the
+//         score of boundary blocks only (item 3);
+// FlashAttention article ("FlashAttention优化：高效训练长上下文GPT的技术突破")
+//   §2 items 1-3  blocks of keys streamed through on-chip memory, softmax
+//         with the running maximum subtracted and earlier blocks rescaled,
+//         both products fused in one kernel on the matrix units.
+//
+// Design (one workgroup = one query block of kBr = 128 rows of one (b, h)):
+//   * 4 wavefronts, each owns 32 query rows.  Its Q rows stay in registers
+//     for the whole key loop as the B operand of v_mfma_f32_32x32x16_bf16.
+//   * The score block is computed transposed, S^T = K Q^T, so that in the
+//     MFMA result layout lane l holds 16 keys of query row l % 32.  A row
+//     maximum is then 15 register max operations and one exchange with the
+//     other half-wave; the row sum needs no exchange until the end.
+//   * The output is also accumulated transposed, O^T = V^T P^T, so that the
+//     same lane holds the same query row in O: the rescale factor of a row
+//     never leaves its lane.  P^T is taken straight from the S^T registers
+//     (converted to bf16) as the B operand; the contraction index of the two
+//     operands is permuted consistently so no data moves between lanes.
+//   * K (row-major) and V^T (transposed while staging) pass through a
+//     double-buffered LDS ring: while block j is computed, block j+1 is
+//     loaded from HBM with 128-bit loads into registers and then written to
+//     the other buffer; one barrier per key block.
+//   * Key blocks outside the query block's non-skip range are never visited
+//     (range from the interval preprocessor).  Inside the range each
+//     wavefront tests its own 32 rows: it skips blocks none of its rows
+//     attends and applies the interval compare only when the block is not
+//     inside all of its rows' intervals.
+
+#include <math.h>
+
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = kBr / kWaves;     // 32
+constexpr int kKPad = 8;                       // bf16 padding per K row in LDS (16 B)
+constexpr int kVPad = 8;                       // bf16 padding per V^T row in LDS (16 B)
+constexpr int kEmptyStart = -(1 << 30);        // start of a row that attends nothing
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+static_assert(kRowsPerWave == 32, "one 32x32 MFMA column block per wavefront");
+static_assert(kBc % 32 == 0 && kBc % 16 == 0, "key block is a multiple of the MFMA shapes");
+
+// Position of key j (within a key block) in a V^T row of LDS.  The PV product
+// consumes, in contraction step ks and half-wave h, keys 16ks + 8a + 4h + q
+// (a = 0,1; q = 0..3) -- the keys that half-wave holds in its S^T registers.
+// Swapping bits 2 and 3 of j makes those eight keys contiguous.
+__device__ __forceinline__ int vt_pos(int j) {
+    return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+}
+
+// acc + the sum of eight bf16 values, two per v_dot2 against (1, 1).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p, bf16x2 ones, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), ones, acc, false);
+    return acc;
+}
+
+template <int D>
+struct Smem {
+    uint16_t k[2][kBc][D + kKPad];      // K block, row-major
+    uint16_t vt[2][D][kBc + kVPad];     // V block, transposed, keys permuted by vt_pos
+    int start[kBr];                     // clamped start of each query row (kEmptyStart: none)
+    int width[kBr];                     // end - start (0 for rows that attend nothing)
+};
+
+template <int D>
+struct Staging {
+    static constexpr int kChunksK = kBc * D / 8 / kThreads;   // 16-byte K chunks per thread
+    static constexpr int kItemsV = (kBc / 4) * (D / 8);       // 4 keys x 8 columns per item
+    static_assert(kChunksK * kThreads * 8 == kBc * D, "K block splits evenly");
+    static_assert(kItemsV <= kThreads, "one V item per thread at most");
+    u32x4 k[kChunksK];
+    u32x4 v[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(Staging<D>& st, const uint16_t* __restrict__ Kbh,
+                                           const uint16_t* __restrict__ Vbh, int kv0, int N,
+                                           int tid) {
+#pragma unroll
+    for (int c = 0; c < Staging<D>::kChunksK; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int row = chunk / (D / 8);
+        const int col8 = chunk % (D / 8);
+        const int g = kv0 + row;
+        st.k[c] = g < N ? *reinterpret_cast<const u32x4*>(Kbh + (int64_t)g * D + col8 * 8)
+                        : u32x4{0, 0, 0, 0};
+    }
+    if (tid < Staging<D>::kItemsV) {
+        const int j0 = 4 * (tid % (kBc / 4));
+        const int n0 = 8 * (tid / (kBc / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = kv0 + j0 + r;
+            st.v[r] = g < N ? *reinterpret_cast<const u32x4*>(Vbh + (int64_t)g * D + n0)
+                            : u32x4{0, 0, 0, 0};
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D>& sm, int buf, int tid) {
+#pragma unroll
+    for (int c = 0; c < Staging<D>::kChunksK; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int row = chunk / (D / 8);
+        const int col8 = chunk % (D / 8);
+        *reinterpret_cast<u32x4*>(&sm.k[buf][row][col8 * 8]) = st.k[c];
+    }
+    if (tid < Staging<D>::kItemsV) {
+        const int j0 = 4 * (tid % (kBc / 4));
+        const int n0 = 8 * (tid / (kBc / 4));
+        const int p = vt_pos(j0);
+        // 4 keys x 8 columns -> 8 columns x 4 keys (bf16 pairs regrouped).
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t a0 = st.v[0][w], a1 = st.v[1][w], a2 = st.v[2][w], a3 = st.v[3][w];
+            const u32x2 even = {(a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16)};
+            const u32x2 odd = {(a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u)};
+            *reinterpret_cast<u32x2*>(&sm.vt[buf][n0 + 2 * w][p]) = even;
+            *reinterpret_cast<u32x2*>(&sm.vt[buf][n0 + 2 * w + 1][p]) = odd;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
+    const TileMeta* __restrict__ meta, const int32_t* __restrict__ order, int H, int N, int n_q,
+    float c, uint16_t* __restrict__ O, float* __restrict__ LSE) {
+    __shared__ Smem<D> sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;      // which 32-lane half of the wavefront
+    const int r32 = lane & 31;       // query row of this lane inside the wavefront's 32
+
+    // Work item: blockIdx.x = item * H + h, so the H heads of one query block
+    // are adjacent in launch order.
+    const int h = blockIdx.x % H;
+    const int q_item = blockIdx.x / H;
+    const int bt = order != nullptr ? order[q_item] : q_item;
+    const int b = bt / n_q;
+    const int t = bt - b * n_q;
+    const TileMeta tm = meta[bt];
+
+    const int64_t bh = (int64_t)b * H + h;
+    const uint16_t* Qbh = Q + bh * N * D;
+    const uint16_t* Kbh = K + bh * N * D;
+    const uint16_t* Vbh = V + bh * N * D;
+    const int row0 = t * kBr;
+
+    // Stage the block's intervals on chip, clamped to the key range [0, N).
+    if (tid < kBr) {
+        const int r = row0 + tid;
+        int s = kEmptyStart, w = 0;
+        if (r < N) {
+            const int s_raw = col_start[(int64_t)b * N + r];
+            const int e_raw = col_end[(int64_t)b * N + r];
+            const int sc = max(s_raw, 0);
+            const int ec = min(e_raw, N - 1);
+            if (sc <= ec) {
+                s = sc;
+                w = ec - sc;
+            }
+        }
+        sm.start[tid] = s;
+        sm.width[tid] = w;
+    }
+
+    // Q rows of this lane as MFMA B operands: Q[row][16 cs + 8 half .. +7].
+    const int qrow = row0 + wave * kRowsPerWave + r32;
+    bf16x8 qreg[D / 16];
+#pragma unroll
+    for (int cs = 0; cs < D / 16; ++cs) {
+        if (qrow < N)
+            qreg[cs] = *reinterpret_cast<const bf16x8*>(Qbh + (int64_t)qrow * D + cs * 16 + half * 8);
+        else
+            qreg[cs] = bf16x8{};
+    }
+
+    floatx16 oacc[D / 32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) oacc[nb] = floatx16{};
+    float m_run = -INFINITY;   // running row maximum, in log2 units (score * scale * log2 e)
+    float l_run = 0.f;         // this lane's share of the running row sum (fp32 weights) -> LSE
+    float l16_run = 0.f;       // the same sum over the bf16-rounded weights the PV product uses -> O
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    __syncthreads();
+    const int my_s = sm.start[wave * kRowsPerWave + r32];
+    const int my_w = sm.width[wave * kRowsPerWave + r32];
+    const bool my_any = my_s != kEmptyStart;
+    // Bounds of this wavefront's rows (the half-waves hold the same rows).
+    const int w_min_s = wave_min(my_any ? my_s : INT_MAX);
+    const int w_max_e = wave_max(my_any ? my_s + my_w : INT_MIN);
+    const int w_max_s = wave_max(my_any ? my_s : (qrow < N ? INT_MAX : INT_MIN));
+    const int w_min_e = wave_min(my_any ? my_s + my_w : (qrow < N ? INT_MIN : INT_MAX));
+
+    const int kv_first = tm.x;
+    const int kv_last = tm.y;
+    if (kv_first <= kv_last) {
+        Staging<D> stage;
+        load_block<D>(stage, Kbh, Vbh, kv_first * kBc, N, tid);
+        store_block<D>(stage, sm, 0, tid);
+        __syncthreads();
+
+        for (int j = kv_first; j <= kv_last; ++j) {
+            const int buf = (j - kv_first) & 1;
+            const bool has_next = j < kv_last;
+            if (has_next) load_block<D>(stage, Kbh, Vbh, (j + 1) * kBc, N, tid);
+
+            const int klo = j * kBc;
+            const int khi = min(klo + kBc, N) - 1;
+            const bool wave_skip = khi < w_min_s || klo > w_max_e;
+            if (!wave_skip) {
+                // ---- S^T = K Q^T: lane holds S[q = r32][key = 32 jb + 8 (v/4) + 4 half + v%4]
+                floatx16 st[kBc / 32];
+#pragma unroll
+                for (int jb = 0; jb < kBc / 32; ++jb) st[jb] = floatx16{};
+#pragma unroll
+                for (int cs = 0; cs < D / 16; ++cs) {
+#pragma unroll
+                    for (int jb = 0; jb < kBc / 32; ++jb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            &sm.k[buf][jb * 32 + r32][cs * 16 + half * 8]);
+                        st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
+                    }
+                }
+
+                // ---- interval compare, only where some row of the wavefront
+                // does not attend the whole key block (boundary blocks).
+                const bool full = (klo + kBc <= N) && klo >= w_max_s && khi <= w_min_e;
+                if (!full) {
+                    const int base = klo + 4 * half - my_s;
+#pragma unroll
+                    for (int jb = 0; jb < kBc / 32; ++jb) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int off = jb * 32 + 8 * (v >> 2) + (v & 3);
+                            const bool ok = (uint32_t)(base + off) <= (uint32_t)my_w;
+                            st[jb][v] = ok ? st[jb][v] : -INFINITY;
+                        }
+                    }
+                }
+
+                // ---- online softmax (exp2 with scale * log2 e folded in)
+                float mx = st[0][0];
+#pragma unroll
+                for (int jb = 0; jb < kBc / 32; ++jb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[jb][v]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run, mx * c);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                float rs = 0.f;
+#pragma unroll
+                for (int jb = 0; jb < kBc / 32; ++jb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(st[jb][v], c, -m_use));
+                        st[jb][v] = p;
+                        rs += p;
+                    }
+                l_run = l_run * alpha + rs;
+                m_run = m_new;
+#pragma unroll
+                for (int nb = 0; nb < D / 32; ++nb) oacc[nb] *= alpha;
+
+                // ---- O^T += V^T P^T.  O is later divided by the sum of the same
+                // bf16-rounded weights, so the rounding of P perturbs the weights
+                // of a proper weighted mean instead of biasing its scale.
+                float rs16 = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < kBc / 16; ++ks) {
+                    bf16x8 pb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)st[ks >> 1][8 * (ks & 1) + e];
+                    rs16 = sum_bf16x8(pb, ones, rs16);
+#pragma unroll
+                    for (int nb = 0; nb < D / 32; ++nb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            &sm.vt[buf][nb * 32 + r32][16 * ks + 8 * half]);
+                        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
+                    }
+                }
+                l16_run = l16_run * alpha + rs16;
+            }
+
+            if (has_next) store_block<D>(stage, sm, buf ^ 1, tid);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: O = O_acc / l16 (bf16, nearest even), LSE = ln(sum) in natural log.
+    const float l = l_run + __shfl_xor(l_run, 32);
+    const float l16 = l16_run + __shfl_xor(l16_run, 32);
+    if (qrow < N) {
+        const float inv = l16 > 0.f ? 1.f / l16 : 0.f;
+        uint16_t* orow = O + bh * N * D + (int64_t)qrow * D;
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 o4;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o4[q] = (__bf16)(oacc[nb][4 * g + q] * inv);
+                *reinterpret_cast<bf16x4*>(orow + nb * 32 + 8 * g + 4 * half) = o4;
+            }
+        }
+        if (half == 0) LSE[bh * N + qrow] = l > 0.f ? m_run * kLn2 + logf(l) : -INFINITY;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
+                            const int32_t* col_end, const TileMeta* meta, const int32_t* order,
+                            int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
+                            float* lse, hipStream_t stream) {
+    const int64_t n_q = (N + kBr - 1) / kBr;
+    const int64_t grid = B * H * n_q;
+    const float c = scale * kLog2e;
+    const auto* Qp = static_cast<const uint16_t*>(q);
+    const auto* Kp = static_cast<const uint16_t*>(k);
+    const auto* Vp = static_cast<const uint16_t*>(v);
+    auto* Op = static_cast<uint16_t*>(out);
+    if (d == 128) {
+        hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, Qp,
+                           Kp, Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, Op,
+                           lse);
+    } else {
+        hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, Qp,
+                           Kp, Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, Op,
+                           lse);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fm

@@ -1,0 +1,54 @@
+// Work ordering for the attention kernel (gfx950).
+//
+// FlashMask article ("FlashMask技术：大模型训练中的高效注意力掩码优化") §4.3
+// item 3: hand out the work by each query block's number of effective
+// (non-skipped) key blocks, and §4.2 (several query blocks per processor).
+// Under document or sliding masks the per-block work is very uneven (a
+// query block at the end of a long document needs many key blocks, one at
+// the start of a short document needs one), so the blocks are issued
+// longest first: the long ones start early and the short ones fill the
+// tail.  The order is a stable sort by decreasing work; each item's rank is
+// counted directly (items ranked ahead of x: larger work, or equal work and
+// smaller index), which is deterministic and needs no atomics.  The order
+// never changes a result: every query block's output depends only on its
+// own fixed sequence of key blocks.
+
+#include <climits>
+
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __restrict__ work, int M,
+                                                            int32_t* __restrict__ order) {
+    __shared__ int s_work[kThreads];
+    const int x = blockIdx.x * kThreads + threadIdx.x;
+    const int wx = x < M ? work[x] : INT_MIN;
+    int rank = 0;
+    for (int base = 0; base < M; base += kThreads) {
+        const int y = base + threadIdx.x;
+        s_work[threadIdx.x] = y < M ? work[y] : INT_MIN;
+        __syncthreads();
+        const int lim = min(kThreads, M - base);
+        for (int i = 0; i < lim; ++i) {
+            const int wy = s_work[i];
+            rank += (wy > wx) | ((wy == wx) & (base + i < x));
+        }
+        __syncthreads();
+    }
+    if (x < M) order[rank] = x;
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream) {
+    const int64_t blocks = (M + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, work,
+                       (int)M, order);
+    return hipGetLastError();
+}
+
+}  // namespace fm

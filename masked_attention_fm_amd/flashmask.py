@@ -1,0 +1,181 @@
+"""ctypes binding of libflashmask (include/flashmask.h), argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor metadata, passes device pointers and the current HIP
+stream, and turns status codes into exceptions.  It never falls back to
+another implementation: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libflashmask.so")
+
+FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_BAD_INTERVAL, FM_ERR_HIP = range(5)
+FM_TILE_SKIP, FM_TILE_FULL, FM_TILE_PARTIAL = 0, 1, 2
+FM_OPT_SCHEDULE = 1
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+# name -> (restype, argtypes); the same names and argument order as the header.
+SIGNATURES = {
+    "fm_classify_tiles": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P]),
+    "fm_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                   _P, _P, _P]),
+    "fm_attn_tile_shape": (ctypes.c_int, [_I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "fm_tile_schedule": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P]),
+    "fm_set_option": (ctypes.c_int, [ctypes.c_int, _I64]),
+    "fm_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "fm_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
+    "fm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fm_last_hip_error": (ctypes.c_int, []),
+}
+
+
+class FlashMaskError(RuntimeError):
+    def __init__(self, func: str, status: int, detail: str = ""):
+        self.status = status
+        super().__init__(f"{func} failed with status {status}{': ' + detail if detail else ''}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m masked_attention_fm_amd.build` (needs hipcc)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(func: str, status: int):
+    if status != FM_OK:
+        L = lib()
+        detail = L.fm_status_string(status).decode()
+        if status == FM_ERR_HIP:
+            detail += f" (hipError {L.fm_last_hip_error()})"
+        raise FlashMaskError(func, status, detail)
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_tensor(x: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fm_attn_tile_shape(d: int) -> Tuple[int, int]:
+    br, bc = _I32(), _I32()
+    _check("fm_attn_tile_shape", lib().fm_attn_tile_shape(int(d), ctypes.byref(br), ctypes.byref(bc)))
+    return br.value, bc.value
+
+
+def fm_classify_tiles(col_start: torch.Tensor, col_end: torch.Tensor, Br: int, Bc: int,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """uint8 [ceil(N/Br), ceil(N/Bc)] class table of one sequence (synchronous)."""
+    _dev_tensor(col_start, "col_start", torch.int32)
+    _dev_tensor(col_end, "col_end", torch.int32)
+    if col_start.dim() != 1 or col_end.shape != col_start.shape:
+        raise ValueError("col_start / col_end must be 1-D of equal length")
+    N = col_start.shape[0]
+    shape = (-(-N // Br), -(-N // Bc)) if Br > 0 and Bc > 0 else (0, 0)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=col_start.device)
+    else:
+        _dev_tensor(out, "out", torch.uint8)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must have shape {shape}")
+    torch.cuda.current_stream(col_start.device).synchronize()
+    _check("fm_classify_tiles", lib().fm_classify_tiles(col_start.data_ptr(), col_end.data_ptr(), N,
+                                                         int(Br), int(Bc), out.data_ptr()))
+    return out
+
+
+def fm_tile_schedule(col_start: torch.Tensor, col_end: torch.Tensor, d: int):
+    """(work, order) int32 [B * ceil(N/Br)] of the attention kernel's scheduler (synchronous)."""
+    _dev_tensor(col_start, "col_start", torch.int32)
+    _dev_tensor(col_end, "col_end", torch.int32)
+    if col_start.dim() != 2 or col_end.shape != col_start.shape:
+        raise ValueError("col_start / col_end must be [B, N]")
+    B, N = col_start.shape
+    br, _ = fm_attn_tile_shape(d)
+    M = B * (-(-N // br))
+    work = torch.empty(M, dtype=torch.int32, device=col_start.device)
+    order = torch.empty(M, dtype=torch.int32, device=col_start.device)
+    torch.cuda.current_stream(col_start.device).synchronize()
+    _check("fm_tile_schedule", lib().fm_tile_schedule(col_start.data_ptr(), col_end.data_ptr(), B, N,
+                                                       int(d), work.data_ptr(), order.data_ptr()))
+    return work, order
+
+
+def fm_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: torch.Tensor,
+                col_end: torch.Tensor, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Masked attention forward; returns (out bf16 [B,H,N,d], lse fp32 [B,H,N]).  Asynchronous."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(x, name, torch.bfloat16)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    _dev_tensor(col_start, "col_start", torch.int32)
+    _dev_tensor(col_end, "col_end", torch.int32)
+    if tuple(col_start.shape) != (B, N) or tuple(col_end.shape) != (B, N):
+        raise ValueError("col_start / col_end must be [B, N]")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor(out, "out", torch.bfloat16)
+        if out.shape != q.shape:
+            raise ValueError("out must match q's shape")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _dev_tensor(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be [B, H, N]")
+    status = lib().fm_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), col_start.data_ptr(),
+                               col_end.data_ptr(), B, H, N, d, float(scale), out.data_ptr(),
+                               lse.data_ptr(), _stream_handle(stream))
+    _check("fm_attn_fwd", status)
+    return out, lse
+
+
+def fm_set_option(option: int, value: int) -> None:
+    _check("fm_set_option", lib().fm_set_option(int(option), int(value)))
+
+
+def fm_profile_enable(enable: bool) -> None:
+    _check("fm_profile_enable", lib().fm_profile_enable(1 if enable else 0))
+
+
+def fm_profile_read() -> Tuple[float, int]:
+    """(summed attention-kernel milliseconds, launches) since the last read."""
+    ms, n = ctypes.c_double(), _I64()
+    _check("fm_profile_read", lib().fm_profile_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,29 @@
+"""Work accounting for the masked attention forward pass (host side).
+
+The throughput metric counts 4*d floating-point operations per attended
+(query, key) pair: 2*d for the score dot product and 2*d for the weighted
+sum of values.  Masked pairs are not counted, so skipped work earns nothing.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# AMD's published dense (no sparsity) bf16 matrix peak of the MI355X, TFLOP/s.
+MI355X_BF16_DENSE_TFLOPS = 2500.0
+MI355X_HBM_TBPS = 8.0
+
+
+def attended_pairs(col_start: np.ndarray, col_end: np.ndarray, N: int) -> int:
+    """Number of attended (row, key) pairs over [B, N] intervals (keys limited to [0, N))."""
+    s = np.maximum(np.asarray(col_start, np.int64), 0)
+    e = np.minimum(np.asarray(col_end, np.int64), N - 1)
+    return int(np.maximum(e - s + 1, 0).sum())
+
+
+def effective_flops(col_start: np.ndarray, col_end: np.ndarray, N: int, H: int, d: int) -> int:
+    return 4 * d * H * attended_pairs(col_start, col_end, N)
+
+
+def algorithmic_bytes(B: int, H: int, N: int, d: int) -> int:
+    """Q, K, V read once, O written once (bf16), LSE written once (fp32), intervals read once."""
+    return 4 * B * H * N * d * 2 + B * H * N * 4 + 2 * B * N * 4

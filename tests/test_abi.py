@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every entry point the header declares, and
+rejects bad arguments on the host before touching the GPU (CPU-only)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from masked_attention_fm_amd import flashmask as fmb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashmask.h")
+
+# Pointers that are never dereferenced: every call below fails its host-side
+# checks first.  They are 16-byte aligned unless a test says otherwise.
+FAKE = 0x10000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fmb.LIB_PATH):
+        from masked_attention_fm_amd import build
+        build.build()
+    return fmb.lib()
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return re.findall(r"FM_API\s+[\w\s\*]+?\b(fm_\w+)\s*\(", text)
+
+
+def test_header_lists_the_entry_points():
+    names = header_functions()
+    assert {"fm_classify_tiles", "fm_attn_fwd", "fm_attn_tile_shape"} <= set(names)
+    assert set(names) == set(fmb.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", fmb.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+    # nothing else with the fm_ prefix leaks out
+    assert {n for n in exported if n.startswith("fm_")} == set(header_functions())
+
+
+def attn(L, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cs=FAKE, ce=FAKE, B=1, H=1, N=128, d=128, scale=0.125,
+                out=FAKE, lse=FAKE)
+    args.update(kw)
+    return L.fm_attn_fwd(args["q"], args["k"], args["v"], args["cs"], args["ce"], args["B"], args["H"],
+                         args["N"], args["d"], args["scale"], args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(v=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(cs=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(lse=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(B=0), fmb.FM_ERR_INVALID_ARG),
+    (dict(H=-1), fmb.FM_ERR_INVALID_ARG),
+    (dict(N=0), fmb.FM_ERR_INVALID_ARG),
+    (dict(N=(1 << 28) + 1), fmb.FM_ERR_INVALID_ARG),
+    (dict(d=96), fmb.FM_ERR_UNSUPPORTED),
+    (dict(d=256), fmb.FM_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fmb.FM_ERR_INVALID_ARG),
+    (dict(scale=-0.1), fmb.FM_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fmb.FM_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fmb.FM_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), fmb.FM_ERR_INVALID_ARG),
+    (dict(out=FAKE + 2), fmb.FM_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fmb.FM_ERR_INVALID_ARG),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 14), fmb.FM_ERR_INVALID_ARG),
+])
+def test_attn_fwd_rejects_bad_arguments(L, kw, status):
+    assert attn(L, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, 100, 16, 16, FAKE), fmb.FM_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 100, 16, 16, None), fmb.FM_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 0, 16, 16, FAKE), fmb.FM_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 100, 0, 16, FAKE), fmb.FM_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 100, 16, -3, FAKE), fmb.FM_ERR_INVALID_ARG),
+    ((FAKE + 2, FAKE, 100, 16, 16, FAKE), fmb.FM_ERR_INVALID_ARG),
+])
+def test_classify_rejects_bad_arguments(L, args, status):
+    assert L.fm_classify_tiles(*args) == status
+
+
+def test_schedule_rejects_bad_arguments(L):
+    assert L.fm_tile_schedule(FAKE, FAKE, 1, 100, 96, FAKE, FAKE) == fmb.FM_ERR_UNSUPPORTED
+    assert L.fm_tile_schedule(None, FAKE, 1, 100, 128, FAKE, FAKE) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_tile_schedule(FAKE, FAKE, 0, 100, 128, FAKE, FAKE) == fmb.FM_ERR_INVALID_ARG
+
+
+def test_tile_shape(L):
+    for d in (64, 128):
+        br, bc = fmb.fm_attn_tile_shape(d)
+        assert br > 0 and bc > 0 and br % 32 == 0 and bc % 32 == 0
+    with pytest.raises(fmb.FlashMaskError) as ei:
+        fmb.fm_attn_tile_shape(80)
+    assert ei.value.status == fmb.FM_ERR_UNSUPPORTED
+    assert L.fm_attn_tile_shape(128, None, None) == fmb.FM_ERR_INVALID_ARG
+
+
+def test_options_and_strings(L):
+    assert L.fm_set_option(fmb.FM_OPT_SCHEDULE, 7) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_set_option(999, 0) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_set_option(fmb.FM_OPT_SCHEDULE, 0) == fmb.FM_OK
+    for s in range(5):
+        assert L.fm_status_string(s)
+    assert b"unknown" in L.fm_status_string(42)
+    assert L.fm_last_hip_error() == 0
+    # nothing recorded: reading the kernel timer touches no GPU
+    assert fmb.fm_profile_read() == (0.0, 0)
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    s = torch.zeros(1, 8, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fmb.fm_attn_fwd(x, x, x, s, s)
