@@ -66,6 +66,16 @@ __device__ __forceinline__ int vt_pos(int j) {
     return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
+// Combine a value with the one held by the other 32-lane half (lane l ^ 32).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // acc + the sum of eight bf16 values, two per v_dot2 against (1, 1).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 p, bf16x2 ones, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), ones, acc, false);
@@ -76,12 +86,14 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, bf16x2 ones, float acc) {
 }
 
 template <int D>
-struct Smem {
-    uint16_t k[2][kBc][D + kKPad];      // K block, row-major
-    uint16_t vt[2][D][kBc + kVPad];     // V block, transposed, keys permuted by vt_pos
-    int start[kBr];                     // clamped start of each query row (kEmptyStart: none)
-    int width[kBr];                     // end - start (0 for rows that attend nothing)
+struct alignas(16) Smem {
+    alignas(16) uint16_t k[2][kBc][D + kKPad];    // K block, row-major
+    alignas(16) uint16_t vt[2][D][kBc + kVPad];   // V block, transposed, keys permuted by vt_pos
+    int start[kBr];                               // clamped start of each query row (kEmptyStart: none)
+    int width[kBr];                               // end - start (0 for rows that attend nothing)
 };
+static_assert(((128 + kKPad) * 2) % 16 == 0 && ((64 + kKPad) * 2) % 16 == 0, "K rows 16-byte aligned");
+static_assert(((kBc + kVPad) * 2) % 16 == 0, "V^T rows 16-byte aligned");
 
 template <int D>
 struct Staging {
@@ -93,6 +105,9 @@ struct Staging {
     u32x4 v[4];
 };
 
+// Loads key block [kv0, kv0 + kBc) into registers.  Rows past N repeat row
+// N-1: their scores are always masked (a block that reaches past N is never
+// treated as full) and their values then meet a weight of exactly 0.
 template <int D>
 __device__ __forceinline__ void load_block(Staging<D>& st, const uint16_t* __restrict__ Kbh,
                                            const uint16_t* __restrict__ Vbh, int kv0, int N,
@@ -102,18 +117,16 @@ __device__ __forceinline__ void load_block(Staging<D>& st, const uint16_t* __res
         const int chunk = tid + c * kThreads;
         const int row = chunk / (D / 8);
         const int col8 = chunk % (D / 8);
-        const int g = kv0 + row;
-        st.k[c] = g < N ? *reinterpret_cast<const u32x4*>(Kbh + (int64_t)g * D + col8 * 8)
-                        : u32x4{0, 0, 0, 0};
+        const int g = min(kv0 + row, N - 1);
+        st.k[c] = *reinterpret_cast<const u32x4*>(Kbh + (int64_t)g * D + col8 * 8);
     }
-    if (tid < Staging<D>::kItemsV) {
+    if (Staging<D>::kItemsV == kThreads || tid < Staging<D>::kItemsV) {
         const int j0 = 4 * (tid % (kBc / 4));
         const int n0 = 8 * (tid / (kBc / 4));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int g = kv0 + j0 + r;
-            st.v[r] = g < N ? *reinterpret_cast<const u32x4*>(Vbh + (int64_t)g * D + n0)
-                            : u32x4{0, 0, 0, 0};
+            const int g = min(kv0 + j0 + r, N - 1);
+            st.v[r] = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)g * D + n0);
         }
     }
 }
@@ -127,7 +140,7 @@ __device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D>& sm, i
         const int col8 = chunk % (D / 8);
         *reinterpret_cast<u32x4*>(&sm.k[buf][row][col8 * 8]) = st.k[c];
     }
-    if (tid < Staging<D>::kItemsV) {
+    if (Staging<D>::kItemsV == kThreads || tid < Staging<D>::kItemsV) {
         const int j0 = 4 * (tid % (kBc / 4));
         const int n0 = 8 * (tid / (kBc / 4));
         const int p = vt_pos(j0);
@@ -272,10 +285,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 for (int jb = 0; jb < kBc / 32; ++jb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[jb][v]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run, mx * c);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                // The accumulator is rescaled only when some row of the wavefront
+                // raised its maximum.  The reference stays the exact running maximum
+                // (not a stale one): the dominant weight of a row is then 1 and
+                // survives the bf16 rounding of P exactly.
+                const float m_blk = halves_max(mx) * c;
+                const bool grow = m_blk > m_run;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    const float m_new = grow ? m_blk : m_run;
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+                    l_run *= alpha;
+                    l16_run *= alpha;
+#pragma unroll
+                    for (int nb = 0; nb < D / 32; ++nb) oacc[nb] *= alpha;
+                    m_run = m_new;
+                }
+                const float m_use = m_run == -INFINITY ? 0.f : m_run;
                 float rs = 0.f;
 #pragma unroll
                 for (int jb = 0; jb < kBc / 32; ++jb)
@@ -285,10 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                         st[jb][v] = p;
                         rs += p;
                     }
-                l_run = l_run * alpha + rs;
-                m_run = m_new;
-#pragma unroll
-                for (int nb = 0; nb < D / 32; ++nb) oacc[nb] *= alpha;
+                l_run += rs;
 
                 // ---- O^T += V^T P^T.  O is later divided by the sum of the same
                 // bf16-rounded weights, so the rounding of P perturbs the weights
@@ -307,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                         oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
                     }
                 }
-                l16_run = l16_run * alpha + rs16;
+                l16_run += rs16;
             }
 
             if (has_next) store_block<D>(stage, sm, buf ^ 1, tid);
@@ -316,8 +338,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
 
     // ---- epilogue: O = O_acc / l16 (bf16, nearest even), LSE = ln(sum) in natural log.
-    const float l = l_run + __shfl_xor(l_run, 32);
-    const float l16 = l16_run + __shfl_xor(l16_run, 32);
+    const float l = halves_sum(l_run);
+    const float l16 = halves_sum(l16_run);
     if (qrow < N) {
         const float inv = l16 > 0.f ? 1.f / l16 : 0.f;
         uint16_t* orow = O + bh * N * D + (int64_t)qrow * D;
