@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB three times "
+                         "(a known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -194,6 +197,16 @@ def main():
                                                  "pct_of_bf16_peak", "attn_kernel_ms", "attn_kernel_tflops",
                                                  "skip_ratio", "partial_ratio", "tile_executed_tflops")
                                if k in r}
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"reference copy: 3 x {args.copy_mib} MiB")
+        del src, dst
 
     kms = main_res.get("attn_kernel_ms")
     roofline = {

@@ -80,7 +80,7 @@ FM_API int fm_classify_tiles(const int32_t* col_start, const int32_t* col_end, i
  *               batch b attends keys j in [0, N) with col_start <= j <= col_end.
  *               Any int32 values are accepted: a row whose range holds no key
  *               of [0, N) attends nothing and gets O = 0, LSE = -inf.
- *   B, H, N   : >= 1, N <= 2^28, B*H*ceil(N/128) < 2^31.
+ *   B, H, N   : >= 1, N <= 2^22, B*H*ceil(N/128) < 2^31.
  *   d         : head dimension, 64 or 128 (else FM_ERR_UNSUPPORTED).
  *   scale     : finite and > 0 (typically 1/sqrt(d)).
  *   out       : bfloat16 [B][H][N][d] device, 16-byte aligned (round to nearest even).

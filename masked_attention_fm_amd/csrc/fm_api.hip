@@ -28,6 +28,9 @@ int hip_fail(hipError_t e) {
     } while (0)
 
 constexpr int64_t kMaxN = int64_t(1) << 28;
+// The attention kernel addresses one (b, h) slice of K or V with 32-bit byte
+// offsets: N * d * 2 must stay below 2^31.
+constexpr int64_t kMaxAttnN = int64_t(1) << 22;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -192,7 +195,7 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
     if (q == nullptr || k == nullptr || v == nullptr || col_start == nullptr || col_end == nullptr ||
         out == nullptr || lse == nullptr)
         return FM_ERR_INVALID_ARG;
-    if (B < 1 || H < 1 || N < 1 || N > kMaxN) return FM_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || N > kMaxAttnN) return FM_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
     if (!(scale > 0.f) || !isfinite(scale)) return FM_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||

@@ -105,29 +105,35 @@ struct Staging {
     u32x4 v[4];
 };
 
-// Loads key block [kv0, kv0 + kBc) into registers.  Rows past N repeat row
-// N-1: their scores are always masked (a block that reaches past N is never
-// treated as full) and their values then meet a weight of exactly 0.
+// Buffer descriptor over one (b, h) slice of K or V: 32-bit byte offsets from
+// a scalar base, and the hardware returns zeros for any offset at or past
+// num_records, so rows past N need no clamp or branch.
+constexpr uint32_t kRawBufferFlags = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint16_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, kRawBufferFlags);
+}
+
+// Loads key block [kv0, kv0 + kBc) into registers.  Rows past N read as zero:
+// their scores are always masked (a block that reaches past N is never
+// treated as full) and their values meet a weight of exactly 0.
 template <int D>
-__device__ __forceinline__ void load_block(Staging<D>& st, const uint16_t* __restrict__ Kbh,
-                                           const uint16_t* __restrict__ Vbh, int kv0, int N,
-                                           int tid) {
+__device__ __forceinline__ void load_block(Staging<D>& st, __amdgpu_buffer_rsrc_t krs,
+                                           __amdgpu_buffer_rsrc_t vrs, int kv0, int tid) {
+    const int base = kv0 * D * 2;
 #pragma unroll
     for (int c = 0; c < Staging<D>::kChunksK; ++c) {
         const int chunk = tid + c * kThreads;
         const int row = chunk / (D / 8);
         const int col8 = chunk % (D / 8);
-        const int g = min(kv0 + row, N - 1);
-        st.k[c] = *reinterpret_cast<const u32x4*>(Kbh + (int64_t)g * D + col8 * 8);
+        st.k[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + row * D * 2 + col8 * 16, 0, 0);
     }
     if (Staging<D>::kItemsV == kThreads || tid < Staging<D>::kItemsV) {
         const int j0 = 4 * (tid % (kBc / 4));
         const int n0 = 8 * (tid / (kBc / 4));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int g = min(kv0 + j0 + r, N - 1);
-            st.v[r] = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)g * D + n0);
-        }
+        for (int r = 0; r < 4; ++r)
+            st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, base + (j0 + r) * D * 2 + n0 * 2, 0, 0);
     }
 }
 
@@ -148,8 +154,9 @@ __device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D>& sm, i
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const uint32_t a0 = st.v[0][w], a1 = st.v[1][w], a2 = st.v[2][w], a3 = st.v[3][w];
-            const u32x2 even = {(a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16)};
-            const u32x2 odd = {(a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u)};
+            // v_perm_b32 byte selects: low halves (even column) / high halves (odd column)
+            const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+            const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
             *reinterpret_cast<u32x2*>(&sm.vt[buf][n0 + 2 * w][p]) = even;
             *reinterpret_cast<u32x2*>(&sm.vt[buf][n0 + 2 * w + 1][p]) = odd;
         }
@@ -181,8 +188,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
     const int64_t bh = (int64_t)b * H + h;
     const uint16_t* Qbh = Q + bh * N * D;
-    const uint16_t* Kbh = K + bh * N * D;
-    const uint16_t* Vbh = V + bh * N * D;
+    const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + bh * N * D, N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + bh * N * D, N * D * 2);
     const int row0 = t * kBr;
 
     // Stage the block's intervals on chip, clamped to the key range [0, N).
@@ -236,14 +243,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const int kv_last = tm.y;
     if (kv_first <= kv_last) {
         Staging<D> stage;
-        load_block<D>(stage, Kbh, Vbh, kv_first * kBc, N, tid);
+        load_block<D>(stage, krs, vrs, kv_first * kBc, tid);
         store_block<D>(stage, sm, 0, tid);
         __syncthreads();
 
         for (int j = kv_first; j <= kv_last; ++j) {
             const int buf = (j - kv_first) & 1;
             const bool has_next = j < kv_last;
-            if (has_next) load_block<D>(stage, Kbh, Vbh, (j + 1) * kBc, N, tid);
+            if (has_next) load_block<D>(stage, krs, vrs, (j + 1) * kBc, tid);
 
             const int klo = j * kBc;
             const int khi = min(klo + kBc, N) - 1;

@@ -63,7 +63,7 @@ def attn(L, **kw):
     (dict(B=0), fmb.FM_ERR_INVALID_ARG),
     (dict(H=-1), fmb.FM_ERR_INVALID_ARG),
     (dict(N=0), fmb.FM_ERR_INVALID_ARG),
-    (dict(N=(1 << 28) + 1), fmb.FM_ERR_INVALID_ARG),
+    (dict(N=(1 << 22) + 1), fmb.FM_ERR_INVALID_ARG),
     (dict(d=96), fmb.FM_ERR_UNSUPPORTED),
     (dict(d=256), fmb.FM_ERR_UNSUPPORTED),
     (dict(scale=0.0), fmb.FM_ERR_INVALID_ARG),
