@@ -128,6 +128,22 @@ def time_config(cfg, steps, warmup, with_kernel_timer=True):
     return res
 
 
+def load_counters(key):
+    """Hardware-counter record of the attention kernel on this workload, if it was taken
+    from the current kernel source (profiles/attn_fwd_<key>_counters.json)."""
+    from masked_attention_fm_amd import counters
+    path = os.path.join(HERE, "profiles", f"attn_fwd_{key}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("attn_source_sha256_16") != counters.attn_source_hash():
+        log(f"{path} was taken from another kernel version: traffic reported as null")
+        return None
+    rec["file"] = os.path.relpath(path, HERE)
+    return rec
+
+
 def cpu_baseline(cfg, target_s):
     """The float64 oracle on whole heads of the workload until about target_s seconds."""
     import oracle
@@ -209,13 +225,17 @@ def main():
         del src, dst
 
     kms = main_res.get("attn_kernel_ms")
+    counters = load_counters(cfg.key)
     roofline = {
         "bound": "mfma",
         "achieved": main_res.get("attn_kernel_tflops"),
         "peak": metrics.MI355X_BF16_DENSE_TFLOPS,
         "unit": "TFLOP/s",
         "frac": (main_res["attn_kernel_tflops"] / metrics.MI355X_BF16_DENSE_TFLOPS) if kms else None,
-        "traffic": None,
+        "traffic": counters.get("hbm_bytes_per_launch") if counters else None,
+        "traffic_source": counters.get("file") if counters else None,
+        "mfma_busy": counters.get("mfma_busy_per_cu_busy") if counters else None,
+        "lds_bank_conflict_cycles": counters.get("lds_bank_conflict_cycles") if counters else None,
         "kernel": "attn_fwd_kernel<128>" if cfg.d == 128 else "attn_fwd_kernel<64>",
         "kernel_ms": kms,
         "algorithmic_flops_per_launch": main_res["effective_flops"],

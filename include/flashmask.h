@@ -128,10 +128,10 @@ FM_API int fm_set_option(int option, int64_t value);
 
 /*
  * Timing of the attention kernel alone, for measurement.  While enabled,
- * fm_attn_fwd records a HIP event pair on its stream around the attention
- * kernel launch.  fm_profile_read waits for the recorded events, returns
- * the summed kernel time in milliseconds and the number of launches, and
- * clears the record.
+ * fm_attn_fwd launches the attention kernel with a HIP event pair that the
+ * dispatch itself stamps at the kernel's start and end.  fm_profile_read
+ * waits for the recorded events, returns the summed kernel time in
+ * milliseconds and the number of launches, and clears the record.
  */
 FM_API int fm_profile_enable(int enable);
 FM_API int fm_profile_read(double* total_ms, int64_t* launches);

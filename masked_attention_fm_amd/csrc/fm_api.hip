@@ -231,11 +231,9 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
             }
         }
     }
-    if (ev.first != nullptr) FM_HIP(hipEventRecord(ev.first, stream));
     FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, meta, natural ? nullptr : order, B, H, N, d,
-                                scale, out, lse, stream));
+                                scale, out, lse, stream, ev.first, ev.second));
     if (ev.first != nullptr) {
-        FM_HIP(hipEventRecord(ev.second, stream));
         std::lock_guard<std::mutex> lock(g_timing.mu);
         g_timing.pending.push_back(ev);
     }

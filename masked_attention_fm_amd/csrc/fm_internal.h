@@ -32,10 +32,11 @@ hipError_t launch_class_table(const TileMeta* meta, int64_t n_q, int64_t n_kv, u
 hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream);
 
 // Attention kernel.  order == nullptr runs query blocks in natural (b, t) order.
+// start/stop (may be null) are stamped at the kernel's own start and end.
 hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
                             const int32_t* col_end, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
-                            float* lse, hipStream_t stream);
+                            float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // ---------------------------------------------------------------- wavefront helpers
 

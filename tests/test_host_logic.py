@@ -1,0 +1,61 @@
+"""Host-side logic of the product path that needs no GPU: the FLOP accounting and the
+rocprofv3 counter summariser."""
+import csv
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from masked_attention_fm_amd import counters, inputs, metrics
+
+
+@pytest.mark.parametrize("key", ["C1", "C2", "C3"])
+def test_attended_pairs_equals_dense_count(key):
+    cfg = inputs.CONFIGS[key]
+    spec = inputs.config_intervals(cfg)
+    for b in range(cfg.B):
+        assert metrics.attended_pairs(spec.col_start[b], spec.col_end[b], cfg.N) == \
+            oracle.unmasked_count(spec.col_start[b], spec.col_end[b], cfg.N)
+
+
+def test_attended_pairs_general_intervals():
+    rng = np.random.default_rng(4)
+    N = 700
+    s = rng.integers(-100, N + 100, size=N)
+    e = s + rng.integers(-20, 300, size=N)
+    assert metrics.attended_pairs(s, e, N) == oracle.unmasked_count(s, e, N)
+
+
+def test_effective_flops_c1_closed_form():
+    cfg = inputs.CONFIGS["C1"]
+    spec = inputs.config_intervals(cfg)
+    # causal: N(N+1)/2 pairs per head, 4*d FLOPs each
+    assert metrics.effective_flops(spec.col_start, spec.col_end, cfg.N, cfg.H, cfg.d) == \
+        4 * 64 * 2 * (512 * 513 // 2)
+
+
+def _write_run(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(["Kernel_Name", "Counter_Name", "Counter_Value"], r)))
+
+
+def test_counter_summary_calibrates_with_the_copy(tmp_path):
+    attn = "void fm::(anonymous namespace)::attn_fwd_kernel<128>(...)"
+    copy = "__amd_rocclr_copyBuffer"
+    _write_run(tmp_path / "fetch", [(attn, "FETCH_SIZE", 1000.0), (attn, "FETCH_SIZE", 1200.0),
+                                    (copy, "FETCH_SIZE", 2.0), (copy, "FETCH_SIZE", 262144.0)])
+    _write_run(tmp_path / "write", [(attn, "WRITE_SIZE", 300.0), (copy, "WRITE_SIZE", 524288.0)])
+    _write_run(tmp_path / "mfma", [(attn, "SQ_VALU_MFMA_BUSY_CYCLES", 400.0), (attn, "SQ_BUSY_CU_CYCLES", 200.0),
+                                   (attn, "SQ_LDS_BANK_CONFLICT", 0.0)])
+    rec = counters.summarise([tmp_path / "fetch", tmp_path / "write", tmp_path / "mfma"], copy_mib=512)
+    assert rec["calibration"]["FETCH_SIZE"] == pytest.approx(2.0)     # the tiny helper copy is ignored
+    assert rec["calibration"]["WRITE_SIZE"] == pytest.approx(1.0)
+    assert rec["hbm_read_bytes_per_launch"] == pytest.approx(1024 * 1100 * 2.0)
+    assert rec["hbm_write_bytes_per_launch"] == pytest.approx(1024 * 300)
+    assert rec["mfma_busy_per_cu_busy"] == pytest.approx(0.5)
+    assert rec["attn_source_sha256_16"] == counters.attn_source_hash()
