@@ -178,9 +178,16 @@ FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, in
     if (B * n_q >= (int64_t(1) << 31)) return FM_ERR_INVALID_ARG;
     void* buf = nullptr;
     FM_HIP(hipMalloc(&buf, (size_t)(B * n_q) * sizeof(fm::TileMeta)));
-    hipError_t e = fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc,
-                                         static_cast<fm::TileMeta*>(buf), work_out, nullptr, 0);
-    if (e == hipSuccess) e = fm::launch_schedule(work_out, B * n_q, order_out, 0);
+    // the same path fm_attn_fwd takes for this size
+    hipError_t e;
+    if (B * n_q <= fm::kPrepSmallMax) {
+        e = fm::launch_prep_small(col_start, col_end, B, N, fm::kBr, fm::kBc, static_cast<fm::TileMeta*>(buf),
+                                  work_out, order_out, 0);
+    } else {
+        e = fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc, static_cast<fm::TileMeta*>(buf),
+                                  work_out, nullptr, 0);
+        if (e == hipSuccess) e = fm::launch_schedule(work_out, B * n_q, order_out, 0);
+    }
     if (e == hipSuccess) e = hipStreamSynchronize(0);
     hipError_t ef = hipFree(buf);
     if (e != hipSuccess) return hip_fail(e);
@@ -214,9 +221,14 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
     auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes);
     auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes + int_bytes);
 
-    FM_HIP(fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc, meta, work, nullptr, stream));
     const bool natural = g_schedule_mode == 1;
-    if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream));
+    if (!natural && M <= fm::kPrepSmallMax) {
+        // one launch: metadata and longest-first order together
+        FM_HIP(fm::launch_prep_small(col_start, col_end, B, N, fm::kBr, fm::kBc, meta, work, order, stream));
+    } else {
+        FM_HIP(fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc, meta, work, nullptr, stream));
+        if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream));
+    }
 
     std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
     {

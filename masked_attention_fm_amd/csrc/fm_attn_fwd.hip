@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
     const TileMeta* __restrict__ meta, const int32_t* __restrict__ order, int H, int N, int n_q,
-    float c, uint16_t* __restrict__ O, float* __restrict__ LSE) {
+    float c, int xcd_heads, uint16_t* __restrict__ O, float* __restrict__ LSE) {
     __shared__ Smem<D> sm;
 
     const int tid = threadIdx.x;
@@ -178,10 +178,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const int half = lane >> 5;      // which 32-lane half of the wavefront
     const int r32 = lane & 31;       // query row of this lane inside the wavefront's 32
 
-    // Work item: blockIdx.x = item * H + h, so the H heads of one query block
-    // are adjacent in launch order.
-    const int h = blockIdx.x % H;
-    const int q_item = blockIdx.x / H;
+    // Work item.  Workgroups are dispatched round-robin over the 8 XCDs, so
+    // XCD x receives launch slots x, x+8, ...  With xcd_heads set (H a
+    // multiple of 8 and enough query blocks per head to fill an XCD), XCD x
+    // runs all query blocks of head x, longest first, then those of head x+8,
+    // and so on: the workgroups resident on one XCD stream one head's K/V
+    // nearly in lockstep and share it through that XCD's L2.  Otherwise the
+    // heads of one query block are adjacent in launch order.
+    int h, q_item;
+    if (xcd_heads) {
+        const int s = blockIdx.x >> 3;
+        const int M = gridDim.x / H;            // query blocks per head
+        h = (blockIdx.x & 7) + 8 * (s / M);
+        q_item = s % M;
+    } else {
+        h = blockIdx.x % H;
+        q_item = blockIdx.x / H;
+    }
     const int bt = order != nullptr ? order[q_item] : q_item;
     const int b = bt / n_q;
     const int t = bt - b * n_q;
@@ -379,10 +392,14 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
     const auto* Vp = static_cast<const uint16_t*>(v);
     auto* Op = static_cast<uint16_t*>(out);
     auto kernel = d == 128 ? attn_fwd_kernel<128> : attn_fwd_kernel<64>;
+    // XCD-local head order needs whole heads per XCD and at least one XCD's
+    // worth of resident workgroups (32 CUs x 2) per head.
+    const int xcd_heads = (H % 8 == 0 && B * n_q >= 128) ? 1 : 0;
     // With an event pair, the dispatch packet itself stamps the kernel's start
     // and end, so the pair measures the kernel alone.
     hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
-                          Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, Op, lse);
+                          Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, xcd_heads, Op,
+                          lse);
     return hipGetLastError();
 }
 

@@ -4,11 +4,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace fm {
 
-// Tile shape of the attention kernel: 4 wavefronts x 32 query rows, 64 keys per step.
-constexpr int kBr = 128;
-constexpr int kBc = 64;
+// Tile shape of the attention kernel: query rows per workgroup, keys per step.
+#ifndef FM_QUERY_TILE
+#define FM_QUERY_TILE 128
+#endif
+#ifndef FM_KEY_TILE
+#define FM_KEY_TILE 64
+#endif
+constexpr int kBr = FM_QUERY_TILE;
+constexpr int kBc = FM_KEY_TILE;
 
 // Per query block (one sequence of one batch), computed from its rows' intervals:
 //   x = first non-skip key block, y = last non-skip key block (y < x: none),
@@ -30,6 +38,13 @@ hipError_t launch_class_table(const TileMeta* meta, int64_t n_q, int64_t n_kv, u
 
 // Longest-first order of M work items (ties by index).
 hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream);
+
+// Preprocessor and scheduler in one launch of one workgroup, for at most
+// kPrepSmallMax query blocks (B * n_q): same meta, work and order outputs.
+constexpr int kPrepSmallMax = 256;
+hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
+                             int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
+                             hipStream_t stream);
 
 // Attention kernel.  order == nullptr runs query blocks in natural (b, t) order.
 // start/stop (may be null) are stamped at the kernel's own start and end.
@@ -64,6 +79,57 @@ __device__ __forceinline__ int wave_max(int v) {
     v = max(v, swizzle_xor<8>(v));
     v = max(v, swizzle_xor<16>(v));
     return max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+}
+
+
+// Tile metadata of query block t of one sequence, reduced by one wavefront
+// (all 64 lanes must call it).  Rows past N are neutral; a row with no key in
+// [0, N) adds nothing to the non-skip range but rules out FULL blocks.
+// `invalid` (per lane) is set when a row breaks 0 <= s <= e <= N-1.
+__device__ __forceinline__ TileMeta query_block_meta(const int32_t* __restrict__ s_row,
+                                                     const int32_t* __restrict__ e_row, int t, int N,
+                                                     int Br, int Bc, int n_kv, int lane, int* invalid) {
+    int min_s = INT_MAX, max_e = INT_MIN;   // non-skip range
+    int max_s = INT_MIN, min_e = INT_MAX;   // full range
+    int bad = 0;
+    const int r_end = min(t * Br + Br, N);
+    for (int r = t * Br + lane; r < r_end; r += 64) {
+        const int s = s_row[r];
+        const int e = e_row[r];
+        bad |= (s < 0) | (e > N - 1) | (s > e);
+        const int sc = max(s, 0);
+        const int ec = min(e, N - 1);
+        if (sc <= ec) {
+            min_s = min(min_s, sc);
+            max_e = max(max_e, ec);
+            max_s = max(max_s, sc);
+            min_e = min(min_e, ec);
+        } else {
+            max_s = INT_MAX;
+            min_e = INT_MIN;
+        }
+    }
+    min_s = wave_min(min_s);
+    max_e = wave_max(max_e);
+    max_s = wave_max(max_s);
+    min_e = wave_min(min_e);
+    *invalid = bad;
+    TileMeta m;
+    if (max_e < min_s) {          // no row attends any key
+        m.x = 0;
+        m.y = -1;
+    } else {
+        m.x = min_s / Bc;
+        m.y = max_e / Bc;
+    }
+    if (max_s <= min_e) {
+        m.z = (max_s + Bc - 1) / Bc;
+        m.w = (min_e == N - 1) ? n_kv - 1 : (min_e + 1) / Bc - 1;
+    } else {
+        m.z = 0;
+        m.w = -1;
+    }
+    return m;
 }
 
 }  // namespace fm

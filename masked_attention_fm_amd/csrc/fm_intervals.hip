@@ -27,53 +27,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void preprocess_kernel(
     if (item >= items) return;  // whole wavefront leaves together
     const int64_t b = item / n_q;
     const int t = (int)(item - b * n_q);
-    const int32_t* s_row = col_start + b * N;
-    const int32_t* e_row = col_end + b * N;
-
-    // Rows that do not exist (past N) are neutral.  A row with no key in
-    // [0, N) contributes nothing to the non-skip range but rules out FULL.
-    int min_s = INT_MAX, max_e = INT_MIN;   // non-skip range
-    int max_s = INT_MIN, min_e = INT_MAX;   // full range
     int invalid = 0;
-    const int r_end = min(t * Br + Br, N);
-    for (int r = t * Br + lane; r < r_end; r += 64) {
-        const int s = s_row[r];
-        const int e = e_row[r];
-        invalid |= (s < 0) | (e > N - 1) | (s > e);
-        const int sc = max(s, 0);
-        const int ec = min(e, N - 1);
-        if (sc <= ec) {
-            min_s = min(min_s, sc);
-            max_e = max(max_e, ec);
-            max_s = max(max_s, sc);
-            min_e = min(min_e, ec);
-        } else {
-            max_s = INT_MAX;
-            min_e = INT_MIN;
-        }
-    }
-    min_s = wave_min(min_s);
-    max_e = wave_max(max_e);
-    max_s = wave_max(max_s);
-    min_e = wave_min(min_e);
+    const TileMeta m = query_block_meta(col_start + b * N, col_end + b * N, t, N, Br, Bc, n_kv, lane,
+                                        &invalid);
     if (bad != nullptr && invalid) *bad = 1;   // vector store; every writer stores 1
-
     if (lane == 0) {
-        TileMeta m;
-        if (max_e < min_s) {          // no row attends any key
-            m.x = 0;
-            m.y = -1;
-        } else {
-            m.x = min_s / Bc;
-            m.y = max_e / Bc;
-        }
-        if (max_s <= min_e) {
-            m.z = (max_s + Bc - 1) / Bc;
-            m.w = (min_e == N - 1) ? n_kv - 1 : (min_e + 1) / Bc - 1;
-        } else {
-            m.z = 0;
-            m.w = -1;
-        }
         meta[item] = m;
         if (work != nullptr) work[item] = m.y >= m.x ? m.y - m.x + 1 : 0;
     }

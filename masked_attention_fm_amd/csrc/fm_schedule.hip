@@ -42,7 +42,55 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __res
     if (x < M) order[rank] = x;
 }
 
+constexpr int kPrepThreads = 1024;
+
+// Small problems: one workgroup computes every query block's metadata (one
+// wavefront per block, as the preprocessor does) and then ranks the blocks
+// from LDS, saving a launch.
+__global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
+    const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int n_q, int n_kv,
+    int Br, int Bc, int M, TileMeta* __restrict__ meta, int32_t* __restrict__ work,
+    int32_t* __restrict__ order) {
+    __shared__ int s_work[kPrepSmallMax];
+    const int lane = threadIdx.x & 63;
+    for (int item = threadIdx.x >> 6; item < M; item += kPrepThreads / 64) {
+        const int b = item / n_q;
+        const int t = item - b * n_q;
+        int invalid = 0;
+        const TileMeta m = query_block_meta(col_start + (int64_t)b * N, col_end + (int64_t)b * N, t, N, Br,
+                                            Bc, n_kv, lane, &invalid);
+        if (lane == 0) {
+            const int w = m.y >= m.x ? m.y - m.x + 1 : 0;
+            meta[item] = m;
+            work[item] = w;
+            s_work[item] = w;
+        }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < M; x += kPrepThreads) {
+        const int wx = s_work[x];
+        int rank = 0;
+        for (int y = 0; y < M; ++y) {
+            const int wy = s_work[y];
+            rank += (wy > wx) | ((wy == wx) & (y < x));
+        }
+        order[rank] = x;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
+                             int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
+                             hipStream_t stream) {
+    const int64_t n_q = (N + Br - 1) / Br;
+    const int64_t n_kv = (N + Bc - 1) / Bc;
+    const int64_t M = B * n_q;
+    if (M > kPrepSmallMax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prep_small_kernel, dim3(1), dim3(kPrepThreads), 0, stream, col_start, col_end, (int)N,
+                       (int)n_q, (int)n_kv, Br, Bc, (int)M, meta, work, order);
+    return hipGetLastError();
+}
 
 hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream) {
     const int64_t blocks = (M + kThreads - 1) / kThreads;

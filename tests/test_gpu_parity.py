@@ -135,6 +135,26 @@ def test_schedule_is_stable_longest_first(key):
     assert np.array_equal(order, np.argsort(-ref_work, kind="stable"))
 
 
+def test_schedule_large_path_is_stable_longest_first():
+    """More query blocks than the one-workgroup path takes: preprocessor + rank kernel."""
+    B, N, d = 3, 1 << 17, 128
+    Br, Bc = fm.fm_attn_tile_shape(d)
+    spec = inputs.make_intervals("doc_lognormal", B, N, 21, median=4096, sigma=1.0, lo=16, hi=32768)
+    assert B * (N // Br) > 256
+    sd, ed = to_dev(spec.col_start, spec.col_end)
+    work, order = fm.fm_tile_schedule(sd, ed, d)
+    work, order = work.cpu().numpy(), order.cpu().numpy()
+    ref_work = []
+    for b in range(B):
+        s, e = spec.col_start[b], spec.col_end[b]
+        for t in range(N // Br):
+            rows = slice(t * Br, (t + 1) * Br)
+            ref_work.append(int(e[rows].max()) // Bc - int(s[rows].min()) // Bc + 1)
+    ref_work = np.array(ref_work)
+    assert np.array_equal(work, ref_work)
+    assert np.array_equal(order, np.argsort(-ref_work, kind="stable"))
+
+
 # ---------------------------------------------------------------- attention, small cases
 
 
