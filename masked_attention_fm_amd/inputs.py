@@ -63,6 +63,18 @@ def prefix_lm_intervals(N: int, p: int) -> Tuple[np.ndarray, np.ndarray]:
     return np.zeros(N, np.int32), end.astype(np.int32)
 
 
+def sinks_window_intervals(N: int, w: int, sinks: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Two ranges per row (FlashMask article §5.2 item 4): the first `sinks`
+    tokens, causally, and a causal window of w keys: [0, min(sinks-1, i)] and
+    [max(0, i-w+1), i].  Returned as [2, N] arrays."""
+    if w < 1 or sinks < 0:
+        raise ValueError("window must be >= 1 and sinks >= 0")
+    i = np.arange(N, dtype=np.int64)
+    s = np.stack([np.zeros(N, np.int64), np.maximum(0, i - w + 1)])
+    e = np.stack([np.minimum(sinks - 1, i), i])
+    return s.astype(np.int32), e.astype(np.int32)
+
+
 def doc_causal_intervals(doc_lengths: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
     """Packed documents, causal inside each document and blind across them."""
     starts: List[np.ndarray] = []
@@ -241,6 +253,16 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int,
 def default_scale(d: int) -> float:
     """1/sqrt(d) rounded to float32 (the value a caller passes as a C float)."""
     return float(np.float32(1.0 / np.sqrt(np.float32(d))))
+
+
+def random_multi_intervals(rng: np.random.Generator, B: int, K: int, N: int, empty_frac: float = 0.0,
+                           max_width: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """K independent random ranges per row: [B, K, N] arrays."""
+    cs = np.empty((B, K, N), np.int32)
+    ce = np.empty((B, K, N), np.int32)
+    for k in range(K):
+        cs[:, k], ce[:, k] = random_intervals(rng, B, N, empty_frac, max_width)
+    return cs, ce
 
 
 def random_intervals(rng: np.random.Generator, B: int, N: int, empty_frac: float = 0.0,

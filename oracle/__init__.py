@@ -27,9 +27,9 @@ pages or by mathematics (closed forms, invariants, brute force, library
 routines); none is "parity unpinned".
 """
 from .attention import attention, attention_weights, dense_mask, bf16_round
-from .tiles import (SKIP, FULL, PARTIAL, classes_minmax, classes_dense,
+from .tiles import (SKIP, FULL, PARTIAL, classes_minmax, classes_minmax_multi, classes_dense,
                     unmasked_count)
 
 __all__ = ["attention", "attention_weights", "dense_mask", "bf16_round",
-           "SKIP", "FULL", "PARTIAL", "classes_minmax", "classes_dense",
+           "SKIP", "FULL", "PARTIAL", "classes_minmax", "classes_minmax_multi", "classes_dense",
            "unmasked_count"]

@@ -4,7 +4,9 @@ Definition followed (see the package docstring for the pages):
 
 * mask      M[i, j] = col_start[i] <= j <= col_end[i] for key columns
             j in [0, N)  -- FlashMask article §1 (per-query key range) and
-            §4.1 item 3 (both ends of the compare inclusive);
+            §4.1 item 3 (both ends of the compare inclusive).  With several
+            ranges per row (§6.1 item 1, several disjoint column ranges; §5.2
+            item 4, attention sinks plus a window) M is their union;
 * scores    S[i, j] = scale * (q_i . k_j), and -inf where M[i, j] is false
             -- FlashMask article §4.1 item 3 (mask added to the score);
 * softmax   p[i, j] = exp(S[i, j] - max_j S[i, j]) / sum_j exp(...)
@@ -31,14 +33,22 @@ import numpy as np
 
 def dense_mask(col_start: np.ndarray, col_end: np.ndarray, N: int,
                rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Boolean [R, N] mask of one sequence: M[r, j] = s[r] <= j <= e[r]."""
+    """Boolean [R, N] mask of one sequence: M[r, j] = s[r] <= j <= e[r].
+
+    col_start / col_end are [N] (one range per row) or [K, N] (K ranges per
+    row, united)."""
     s = np.asarray(col_start, dtype=np.int64)
     e = np.asarray(col_end, dtype=np.int64)
+    if s.ndim == 1:
+        s, e = s[None], e[None]
     if rows is not None:
-        s = s[rows]
-        e = e[rows]
+        s = s[:, rows]
+        e = e[:, rows]
     j = np.arange(N, dtype=np.int64)
-    return (j[None, :] >= s[:, None]) & (j[None, :] <= e[:, None])
+    M = np.zeros((s.shape[1], N), dtype=bool)
+    for k in range(s.shape[0]):
+        M |= (j[None, :] >= s[k][:, None]) & (j[None, :] <= e[k][:, None])
+    return M
 
 
 def attention(q, k, v, col_start, col_end, scale: float,
@@ -48,7 +58,8 @@ def attention(q, k, v, col_start, col_end, scale: float,
 
     q, k, v   : real arrays [B, H, N, d] (bfloat16 values held exactly in
                 float32 or float64); slices are promoted to float64.
-    col_start, col_end : integer arrays [B, N], shared by all heads.
+    col_start, col_end : integer arrays [B, N], shared by all heads, or
+                [B, K, N] for K ranges per row (the row attends their union).
     scale     : the float32 scale value.
     rows      : query rows to evaluate (the same for every b); default all.
 

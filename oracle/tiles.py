@@ -79,6 +79,23 @@ def classes_dense(col_start, col_end, N: int, Br: int, Bc: int) -> np.ndarray:
     return out
 
 
+def classes_minmax_multi(col_start, col_end, N: int, Br: int, Bc: int) -> np.ndarray:
+    """Rows with K ranges ([K, N] arrays, each range valid 0 <= s <= e <= N-1).
+
+    Reading for the union: a tile is SKIP when every range alone would skip it,
+    FULL when some single range covers it for every row of the block (a
+    sufficient condition for the union to cover it), PARTIAL otherwise."""
+    s_all = np.asarray(col_start)
+    e_all = np.asarray(col_end)
+    per_k = [classes_minmax(s_all[k], e_all[k], N, Br, Bc) for k in range(s_all.shape[0])]
+    out = np.full(per_k[0].shape, SKIP, dtype=np.uint8)
+    for tab in per_k:
+        out = np.where((out == SKIP) & (tab != SKIP), PARTIAL, out)
+    for tab in per_k:
+        out = np.where(tab == FULL, FULL, out)
+    return out
+
+
 def unmasked_count(col_start, col_end, N: int) -> int:
     """Number of attended (query, key) pairs of one sequence, counted from the dense mask
     one row block at a time."""

@@ -94,6 +94,16 @@ def test_qkv_deterministic_bf16_normal():
     assert torch.equal(inputs.qkv_slice(5, "v", 0, 1, 256, 64), v[0, 1])
 
 
+def test_sinks_window_closed_form():
+    s, e = inputs.sinks_window_intervals(50, 8, 3)
+    assert s.shape == (2, 50)
+    for i in range(50):
+        assert (s[0, i], e[0, i]) == (0, min(2, i))
+        assert (s[1, i], e[1, i]) == (max(0, i - 7), i)
+    s, e = inputs.sinks_window_intervals(10, 4, 0)      # no sinks: an empty first range
+    assert np.all(e[0] < s[0])
+
+
 def test_random_intervals_valid():
     rng = np.random.default_rng(0)
     s, e = inputs.random_intervals(rng, 2, 333, empty_frac=0.2)

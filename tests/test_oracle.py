@@ -186,7 +186,60 @@ def pin_linearity(attn):
     np.testing.assert_allclose(O2, a * O1 + c, rtol=0, atol=1e-12)
 
 
+def pin_multi_overlap_is_single(attn):
+    """Two overlapping (or touching) ranges per row equal the single range that covers both."""
+    rng = np.random.default_rng(40)
+    B, H, N, d = 2, 2, 120, 16
+    q, k, v = _qkv(B, H, N, d, seed=40)
+    a = rng.integers(0, N, size=(B, N))
+    dd = np.minimum(N - 1, a + rng.integers(0, 60, size=(B, N)))
+    b_ = a + (rng.random((B, N)) * (dd - a + 1)).astype(np.int64)           # a <= b <= d
+    c_ = np.minimum(dd, np.maximum(b_ - 1, a + rng.integers(0, 40, size=(B, N))))   # b-1 <= c <= d
+    cs = np.stack([a, b_], axis=1).astype(np.int32)
+    ce = np.stack([c_, dd], axis=1).astype(np.int32)
+    O2, L2 = attn(q, k, v, cs, ce, SCALE(d))
+    O1, L1 = attn(q, k, v, a.astype(np.int32), dd.astype(np.int32), SCALE(d))
+    np.testing.assert_allclose(O2, O1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L2, L1, rtol=0, atol=1e-12)
+
+
+def pin_sinks_window_vs_sdpa(attn):
+    """Attention sinks plus a causal window equal torch's attention under a mask built
+    from tril/triu and the first columns."""
+    B, H, N, d, w, sinks = 1, 2, 130, 32, 20, 5
+    q, k, v = _qkv(B, H, N, d, seed=41)
+    cs, ce = inputs.sinks_window_intervals(N, w, sinks)
+    O, L = attn(q, k, v, cs[None], ce[None], SCALE(d))
+    ones = torch.ones(N, N, dtype=torch.bool)
+    causal = torch.tril(ones)
+    band = causal & torch.triu(ones, diagonal=-(w - 1))
+    sink = causal.clone()
+    sink[:, sinks:] = False
+    mask = (band | sink).numpy()
+    for h in range(H):
+        ref = _sdpa(q[0, h], k[0, h], v[0, h], SCALE(d), attn_mask=mask)
+        np.testing.assert_allclose(O[0, h], ref, rtol=0, atol=1e-12)
+
+
+def pin_multi_q_zero(attn):
+    """Q = 0 with disjoint ranges: O is the mean of v over the union, LSE = ln(|union|)."""
+    rng = np.random.default_rng(42)
+    B, H, N, d, K = 1, 2, 90, 8, 3
+    _, k, v = _qkv(B, H, N, d, seed=42)
+    q = np.zeros_like(k)
+    cs, ce = inputs.random_multi_intervals(rng, B, K, N, empty_frac=0.2, max_width=15)
+    O, L = attn(q, k, v, cs, ce, SCALE(d))
+    for i in range(N):
+        keys = sorted({j for kk in range(K) for j in range(max(cs[0, kk, i], 0), min(ce[0, kk, i], N - 1) + 1)})
+        if not keys:
+            assert np.all(O[0, :, i] == 0) and np.all(np.isneginf(L[0, :, i]))
+            continue
+        np.testing.assert_allclose(O[0, :, i], v[0][:, keys].astype(np.float64).mean(axis=1), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[0, :, i], math.log(len(keys)), rtol=0, atol=1e-13)
+
+
 ALL_PINS = [pin_bruteforce, pin_q_zero, pin_width_one, pin_causal_row0,
+            pin_multi_overlap_is_single, pin_sinks_window_vs_sdpa, pin_multi_q_zero,
             pin_full_and_causal_vs_sdpa, pin_sliding_vs_sdpa,
             pin_doc_packing_is_per_doc_causal, pin_prefix_lm, pin_lse_logsumexp,
             pin_linearity]

@@ -37,8 +37,11 @@ def _caught(pins, fn):
 
 
 ATTN_MUTANTS = {
-    "exclusive_end": ("(j[None, :] <= e[:, None])", "(j[None, :] < e[:, None])"),
-    "exclusive_start": ("(j[None, :] >= s[:, None])", "(j[None, :] > s[:, None])"),
+    "exclusive_end": ("(j[None, :] <= e[k][:, None])", "(j[None, :] < e[k][:, None])"),
+    "exclusive_start": ("(j[None, :] >= s[k][:, None])", "(j[None, :] > s[k][:, None])"),
+    "union_keeps_last_range": ("        M |= (j[None, :]", "        M = (j[None, :]"),
+    "union_as_intersection": ("    M = np.zeros((s.shape[1], N), dtype=bool)\n    for k in range(s.shape[0]):\n        M |= ",
+                              "    M = np.ones((s.shape[1], N), dtype=bool)\n    for k in range(s.shape[0]):\n        M &= "),
     "dropped_scale": ("S = scale64 * (qh @ kh.T)", "S = (qh @ kh.T)"),
     "scale_squared": ("S = scale64 * (qh @ kh.T)", "S = scale64 * scale64 * (qh @ kh.T)"),
     "lse_without_max": ("m[ok] + np.log(l[ok])", "np.log(l[ok])"),
@@ -75,3 +78,19 @@ def test_tile_mutant_is_caught(name):
     old, new = TILE_MUTANTS[name]
     mod = _mutant("tiles.py", old, new, {"dense_mask": oracle.dense_mask})
     assert _caught(test_oracle_tiles.ALL_PINS, mod.classes_minmax), f"mutant {name} survived every pin"
+
+
+MULTI_TILE_MUTANTS = {
+    "skip_if_any_range_skips": ("        out = np.where((out == SKIP) & (tab != SKIP), PARTIAL, out)\n    for tab in per_k:\n        out = np.where(tab == FULL, FULL, out)",
+                                "        out = np.where((out == SKIP) & (tab != SKIP), PARTIAL, out)\n    out = np.where(np.any([t == SKIP for t in per_k], axis=0), SKIP, out)\n    for tab in per_k:\n        out = np.where(tab == FULL, FULL, out)"),
+    "full_ignored": ("        out = np.where(tab == FULL, FULL, out)", "        out = out"),
+    "first_range_only": ("range(s_all.shape[0])]", "range(1)]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_TILE_MUTANTS))
+def test_multi_tile_mutant_is_caught(name):
+    import oracle
+    old, new = MULTI_TILE_MUTANTS[name]
+    mod = _mutant("tiles.py", old, new, {"dense_mask": oracle.dense_mask})
+    assert _caught(test_oracle_tiles.MULTI_PINS, mod.classes_minmax_multi), f"mutant {name} survived every pin"

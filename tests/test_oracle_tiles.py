@@ -88,6 +88,45 @@ def test_tile_pin(pin):
     pin(oracle.classes_minmax)
 
 
+def pin_multi_sinks_window_counts(classes_multi):
+    """Sinks (10) + window (1024), N = 32768, 128x128 tiles: the window's 2268 non-skip
+    tiles (504 partial) plus key block 0 as a partial tile for the 247 query blocks
+    t >= 9 whose window no longer reaches it: 2515 non-skip, 751 partial."""
+    N = 32768
+    s, e = inputs.sinks_window_intervals(N, 1024, 10)
+    c = _counts(classes_multi(s, e, N, 128, 128))
+    assert c[FULL] + c[PARTIAL] == 2515
+    assert c[PARTIAL] == 751
+
+
+def pin_multi_against_dense(classes_multi):
+    """Union rule vs dense count: FULL implies dense-full, SKIP implies dense-empty; a range
+    that covers a tile for every row makes it FULL; one range reproduces the single rule."""
+    rng = np.random.default_rng(9)
+    for N, Br, Bc in ((130, 16, 16), (257, 64, 32), (200, 33, 17)):
+        s, e = inputs.random_multi_intervals(rng, 1, 3, N, max_width=40)
+        a = classes_multi(s[0], e[0], N, Br, Bc)
+        d = oracle.classes_dense(s[0], e[0], N, Br, Bc)
+        assert np.all(d[a == FULL] == FULL)
+        assert np.all(d[a == SKIP] == SKIP)
+        assert np.array_equal(classes_multi(s[0][:1], e[0][:1], N, Br, Bc),
+                              oracle.classes_minmax(s[0][0], e[0][0], N, Br, Bc))
+    # a second range covering everything turns every tile FULL
+    N = 100
+    s0, e0 = inputs.causal_intervals(N)
+    s = np.stack([s0, np.zeros(N, np.int32)])
+    e = np.stack([e0, np.full(N, N - 1, np.int32)])
+    assert np.all(classes_multi(s, e, N, 32, 32) == FULL)
+
+
+MULTI_PINS = [pin_multi_sinks_window_counts, pin_multi_against_dense]
+
+
+@pytest.mark.parametrize("pin", MULTI_PINS, ids=lambda f: f.__name__)
+def test_multi_tile_pin(pin):
+    pin(oracle.classes_minmax_multi)
+
+
 def test_causal_skip_tends_to_half():
     N, T = 1 << 16, 64
     n = N // T
