@@ -100,6 +100,57 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v,
                        int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                        void* out, float* lse, hipStream_t stream);
 
+/*
+ * Rows with several key ranges.  The FlashMask article lists, as an
+ * extension, rows whose attended keys are several disjoint column ranges
+ * (§6.1 item 1), and as a use, attention sinks next to a sliding window
+ * (§5.2 item 4), which one range per row cannot express.  Here each query
+ * row holds n_ranges inclusive ranges, 1 <= n_ranges <= FM_MAX_RANGES, and
+ * attends their union (ranges may overlap, touch, or be empty).
+ *
+ * Layout: col_start, col_end are int32 [B][n_ranges][N] device: range k of
+ * row r of batch b is element (b*n_ranges + k)*N + r.  With n_ranges = 1
+ * this is the [B][N] layout of the single-range calls, and the results are
+ * bit-identical to them.
+ *
+ * Tile classes of a union (reading of §2.2 for several ranges): SKIP when
+ * every range alone skips the tile, FULL when one range alone makes it FULL
+ * (that range then covers every row of the tile, so the union does too),
+ * PARTIAL otherwise.
+ */
+#define FM_MAX_RANGES 4
+
+/*
+ * fm_attn_fwd_multi -- fm_attn_fwd for rows with n_ranges key ranges.
+ * Arguments, outputs, asynchrony and errors as fm_attn_fwd; additionally
+ * FM_ERR_INVALID_ARG when n_ranges is outside [1, FM_MAX_RANGES].  Any int32
+ * values are accepted; a range with no key of [0, N) adds nothing, and a row
+ * whose ranges all hold no key gets O = 0, LSE = -inf.
+ */
+FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v,
+                             const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                             void* out, float* lse, hipStream_t stream);
+
+/*
+ * fm_classify_tiles_multi -- fm_classify_tiles for one sequence whose rows
+ * hold n_ranges ranges: col_start, col_end are int32 [n_ranges][N] device
+ * (for batch b pass col_start + b*n_ranges*N).  Classes as stated above.
+ * Synchronous.  FM_ERR_BAD_INTERVAL when any range of any row breaks
+ * 0 <= s <= e <= N-1 (the table is still written).
+ */
+FM_API int fm_classify_tiles_multi(const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                                   int64_t N, int32_t Br, int32_t Bc, uint8_t* class_out);
+
+/*
+ * fm_tile_schedule_multi -- fm_tile_schedule for [B][n_ranges][N] intervals.
+ * work_out counts the key blocks of the union of the ranges' non-skip blocks
+ * (the non-SKIP tiles of the query block's row of the class table).
+ */
+FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                                  int64_t B, int64_t N, int64_t d,
+                                  int32_t* work_out, int32_t* order_out);
+
 /* The query and key block sizes the attention kernel uses for head dimension d
  * (the shape at which tiles are skipped).  FM_ERR_UNSUPPORTED for other d. */
 FM_API int fm_attn_tile_shape(int64_t d, int32_t* Br, int32_t* Bc);

@@ -27,6 +27,8 @@ int hip_fail(hipError_t e) {
         if (e_ != hipSuccess) return hip_fail(e_); \
     } while (0)
 
+static_assert(fm::kMaxRanges == FM_MAX_RANGES, "range limit of the kernels and of the ABI");
+
 constexpr int64_t kMaxN = int64_t(1) << 28;
 // The attention kernel addresses one (b, h) slice of K or V with 32-bit byte
 // offsets: N * d * 2 must stay below 2^31.
@@ -146,21 +148,24 @@ FM_API int fm_profile_read(double* total_ms, int64_t* launches) {
     return status;
 }
 
-FM_API int fm_classify_tiles(const int32_t* col_start, const int32_t* col_end, int64_t N, int32_t Br,
-                             int32_t Bc, uint8_t* class_out) {
+FM_API int fm_classify_tiles_multi(const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                                   int64_t N, int32_t Br, int32_t Bc, uint8_t* class_out) {
     if (col_start == nullptr || col_end == nullptr || class_out == nullptr) return FM_ERR_INVALID_ARG;
+    if (n_ranges < 1 || n_ranges > fm::kMaxRanges) return FM_ERR_INVALID_ARG;
     if (N < 1 || N > kMaxN || Br < 1 || Bc < 1 || Br > kMaxN || Bc > kMaxN) return FM_ERR_INVALID_ARG;
     if (!aligned(col_start, 4) || !aligned(col_end, 4)) return FM_ERR_INVALID_ARG;
     const int64_t n_q = (N + Br - 1) / Br;
     const int64_t n_kv = (N + Bc - 1) / Bc;
+    const size_t meta_bytes = (size_t)(n_q * n_ranges) * sizeof(fm::TileMeta);
     void* buf = nullptr;
-    FM_HIP(hipMalloc(&buf, (size_t)n_q * sizeof(fm::TileMeta) + 16));
+    FM_HIP(hipMalloc(&buf, meta_bytes + 16));
     auto* meta = static_cast<fm::TileMeta*>(buf);
-    auto* bad = reinterpret_cast<int32_t*>(static_cast<char*>(buf) + n_q * sizeof(fm::TileMeta));
+    auto* bad = reinterpret_cast<int32_t*>(static_cast<char*>(buf) + meta_bytes);
     int bad_host = 0;
     hipError_t e = hipMemsetAsync(bad, 0, sizeof(int32_t), 0);
-    if (e == hipSuccess) e = fm::launch_preprocess(col_start, col_end, 1, N, Br, Bc, meta, nullptr, bad, 0);
-    if (e == hipSuccess) e = fm::launch_class_table(meta, n_q, n_kv, class_out, 0);
+    if (e == hipSuccess)
+        e = fm::launch_preprocess(col_start, col_end, n_ranges, 1, N, Br, Bc, meta, nullptr, bad, 0);
+    if (e == hipSuccess) e = fm::launch_class_table(meta, n_ranges, n_q, n_kv, class_out, 0);
     if (e == hipSuccess) e = hipMemcpy(&bad_host, bad, sizeof(int32_t), hipMemcpyDeviceToHost);
     hipError_t ef = hipFree(buf);
     if (e != hipSuccess) return hip_fail(e);
@@ -168,24 +173,31 @@ FM_API int fm_classify_tiles(const int32_t* col_start, const int32_t* col_end, i
     return bad_host ? FM_ERR_BAD_INTERVAL : FM_OK;
 }
 
-FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
-                            int64_t d, int32_t* work_out, int32_t* order_out) {
+FM_API int fm_classify_tiles(const int32_t* col_start, const int32_t* col_end, int64_t N, int32_t Br,
+                             int32_t Bc, uint8_t* class_out) {
+    return fm_classify_tiles_multi(col_start, col_end, 1, N, Br, Bc, class_out);
+}
+
+FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                                  int64_t B, int64_t N, int64_t d, int32_t* work_out, int32_t* order_out) {
     if (col_start == nullptr || col_end == nullptr || work_out == nullptr || order_out == nullptr)
         return FM_ERR_INVALID_ARG;
+    if (n_ranges < 1 || n_ranges > fm::kMaxRanges) return FM_ERR_INVALID_ARG;
     if (B < 1 || N < 1 || N > kMaxN) return FM_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
     const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
     if (B * n_q >= (int64_t(1) << 31)) return FM_ERR_INVALID_ARG;
     void* buf = nullptr;
-    FM_HIP(hipMalloc(&buf, (size_t)(B * n_q) * sizeof(fm::TileMeta)));
+    FM_HIP(hipMalloc(&buf, (size_t)(B * n_q * n_ranges) * sizeof(fm::TileMeta)));
+    auto* meta = static_cast<fm::TileMeta*>(buf);
     // the same path fm_attn_fwd takes for this size
     hipError_t e;
     if (B * n_q <= fm::kPrepSmallMax) {
-        e = fm::launch_prep_small(col_start, col_end, B, N, fm::kBr, fm::kBc, static_cast<fm::TileMeta*>(buf),
-                                  work_out, order_out, 0);
+        e = fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work_out,
+                                  order_out, 0);
     } else {
-        e = fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc, static_cast<fm::TileMeta*>(buf),
-                                  work_out, nullptr, 0);
+        e = fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work_out,
+                                  nullptr, 0);
         if (e == hipSuccess) e = fm::launch_schedule(work_out, B * n_q, order_out, 0);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(0);
@@ -195,13 +207,19 @@ FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, in
     return FM_OK;
 }
 
-FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_t* col_start,
-                       const int32_t* col_end, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                       void* out, float* lse, hipStream_t stream) {
+FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
+                            int64_t d, int32_t* work_out, int32_t* order_out) {
+    return fm_tile_schedule_multi(col_start, col_end, 1, B, N, d, work_out, order_out);
+}
+
+FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v, const int32_t* col_start,
+                             const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
+                             int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
     // ---- host-side checks, before any HIP call
     if (q == nullptr || k == nullptr || v == nullptr || col_start == nullptr || col_end == nullptr ||
         out == nullptr || lse == nullptr)
         return FM_ERR_INVALID_ARG;
+    if (n_ranges < 1 || n_ranges > fm::kMaxRanges) return FM_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || N < 1 || N > kMaxAttnN) return FM_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
     if (!(scale > 0.f) || !isfinite(scale)) return FM_ERR_INVALID_ARG;
@@ -209,11 +227,12 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
         !aligned(lse, 4) || !aligned(col_start, 4) || !aligned(col_end, 4))
         return FM_ERR_INVALID_ARG;
     const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
-    if (B * H * n_q >= (int64_t(1) << 31) || B * N >= (int64_t(1) << 40)) return FM_ERR_INVALID_ARG;
+    if (B * H * n_q >= (int64_t(1) << 31) || B * n_ranges * N >= (int64_t(1) << 40))
+        return FM_ERR_INVALID_ARG;
 
-    // ---- workspace: meta[M] | work[M] | order[M]
+    // ---- workspace: meta[M][n_ranges] | work[M] | order[M]
     const int64_t M = B * n_q;
-    const size_t meta_bytes = ((size_t)M * sizeof(fm::TileMeta) + 255) & ~size_t(255);
+    const size_t meta_bytes = ((size_t)(M * n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
     const size_t int_bytes = ((size_t)M * sizeof(int32_t) + 255) & ~size_t(255);
     void* ws = nullptr;
     FM_HIP(get_workspace(stream, meta_bytes + 2 * int_bytes, &ws));
@@ -224,9 +243,11 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
     const bool natural = g_schedule_mode == 1;
     if (!natural && M <= fm::kPrepSmallMax) {
         // one launch: metadata and longest-first order together
-        FM_HIP(fm::launch_prep_small(col_start, col_end, B, N, fm::kBr, fm::kBc, meta, work, order, stream));
+        FM_HIP(fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work, order,
+                                     stream));
     } else {
-        FM_HIP(fm::launch_preprocess(col_start, col_end, B, N, fm::kBr, fm::kBc, meta, work, nullptr, stream));
+        FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work, nullptr,
+                                     stream));
         if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream));
     }
 
@@ -243,13 +264,19 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
             }
         }
     }
-    FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, meta, natural ? nullptr : order, B, H, N, d,
-                                scale, out, lse, stream, ev.first, ev.second));
+    FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, n_ranges, meta, natural ? nullptr : order, B, H,
+                                N, d, scale, out, lse, stream, ev.first, ev.second));
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
         g_timing.pending.push_back(ev);
     }
     return FM_OK;
+}
+
+FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_t* col_start,
+                       const int32_t* col_end, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       void* out, float* lse, hipStream_t stream) {
+    return fm_attn_fwd_multi(q, k, v, col_start, col_end, 1, B, H, N, d, scale, out, lse, stream);
 }
 
 }  // extern "C"

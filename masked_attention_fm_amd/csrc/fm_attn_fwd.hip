@@ -31,6 +31,13 @@
 //     wavefront tests its own 32 rows: it skips blocks none of its rows
 //     attends and applies the interval compare only when the block is not
 //     inside all of its rows' intervals.
+//   * Rows may hold up to kMaxRanges ranges (FlashMask article §6.1 item 1,
+//     several column ranges per row; §5.2 item 4, sinks plus a window).  The
+//     kernel is instantiated per range count NIV: the visited key blocks are
+//     the union of the ranges' non-skip blocks in increasing order, a block
+//     is skipped or full for a wavefront by the per-range tests above, and
+//     the compare keeps a key that lies in any of the row's ranges.  With
+//     NIV = 1 this is the single-range kernel.
 
 #include <hip/hip_ext.h>
 #include <math.h>
@@ -86,12 +93,13 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, bf16x2 ones, float acc) {
     return acc;
 }
 
-template <int D>
+template <int D, int NIV>
 struct alignas(16) Smem {
     alignas(16) uint16_t k[2][kBc][D + kKPad];    // K block, row-major
     alignas(16) uint16_t vt[2][D][kBc + kVPad];   // V block, transposed, keys permuted by vt_pos
-    int start[kBr];                               // clamped start of each query row (kEmptyStart: none)
-    int width[kBr];                               // end - start (0 for rows that attend nothing)
+    int start[NIV][kBr];                          // clamped start of each range of each query row
+                                                  // (kEmptyStart: the range holds no key)
+    int width[NIV][kBr];                          // end - start (0 for empty ranges)
 };
 static_assert(((128 + kKPad) * 2) % 16 == 0 && ((64 + kKPad) * 2) % 16 == 0, "K rows 16-byte aligned");
 static_assert(((kBc + kVPad) * 2) % 16 == 0, "V^T rows 16-byte aligned");
@@ -138,8 +146,8 @@ __device__ __forceinline__ void load_block(Staging<D>& st, __amdgpu_buffer_rsrc_
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D>& sm, int buf, int tid) {
+template <int D, int NIV>
+__device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D, NIV>& sm, int buf, int tid) {
 #pragma unroll
     for (int c = 0; c < Staging<D>::kChunksK; ++c) {
         const int chunk = tid + c * kThreads;
@@ -164,13 +172,15 @@ __device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D>& sm, i
     }
 }
 
-template <int D>
+// NIV: ranges per query row (the row attends their union).  col_start and
+// col_end are [B][NIV][N]; meta holds NIV records per query block.
+template <int D, int NIV>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
     const TileMeta* __restrict__ meta, const int32_t* __restrict__ order, int H, int N, int n_q,
     float c, int xcd_heads, uint16_t* __restrict__ O, float* __restrict__ LSE) {
-    __shared__ Smem<D> sm;
+    __shared__ Smem<D, NIV> sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -198,7 +208,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const int bt = order != nullptr ? order[q_item] : q_item;
     const int b = bt / n_q;
     const int t = bt - b * n_q;
-    const TileMeta tm = meta[bt];
+    TileMeta tm[NIV];
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) tm[k] = meta[(int64_t)bt * NIV + k];
 
     const int64_t bh = (int64_t)b * H + h;
     const uint16_t* Qbh = Q + bh * N * D;
@@ -209,19 +221,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     // Stage the block's intervals on chip, clamped to the key range [0, N).
     if (tid < kBr) {
         const int r = row0 + tid;
-        int s = kEmptyStart, w = 0;
-        if (r < N) {
-            const int s_raw = col_start[(int64_t)b * N + r];
-            const int e_raw = col_end[(int64_t)b * N + r];
-            const int sc = max(s_raw, 0);
-            const int ec = min(e_raw, N - 1);
-            if (sc <= ec) {
-                s = sc;
-                w = ec - sc;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            int s = kEmptyStart, w = 0;
+            if (r < N) {
+                const int64_t at = ((int64_t)b * NIV + k) * N + r;
+                const int sc = max(col_start[at], 0);
+                const int ec = min(col_end[at], N - 1);
+                if (sc <= ec) {
+                    s = sc;
+                    w = ec - sc;
+                }
             }
+            sm.start[k][tid] = s;
+            sm.width[k][tid] = w;
         }
-        sm.start[tid] = s;
-        sm.width[tid] = w;
     }
 
     // Q rows of this lane as MFMA B operands: Q[row][16 cs + 8 half .. +7].
@@ -244,31 +258,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     __syncthreads();
-    const int my_s = sm.start[wave * kRowsPerWave + r32];
-    const int my_w = sm.width[wave * kRowsPerWave + r32];
-    const bool my_any = my_s != kEmptyStart;
-    // Bounds of this wavefront's rows (the half-waves hold the same rows).
-    const int w_min_s = wave_min(my_any ? my_s : INT_MAX);
-    const int w_max_e = wave_max(my_any ? my_s + my_w : INT_MIN);
-    const int w_max_s = wave_max(my_any ? my_s : (qrow < N ? INT_MAX : INT_MIN));
-    const int w_min_e = wave_min(my_any ? my_s + my_w : (qrow < N ? INT_MIN : INT_MAX));
+    // Per range: this lane's row interval, and the bounds of the wavefront's
+    // rows (the half-waves hold the same rows).
+    int my_s[NIV], my_w[NIV];
+    int w_min_s[NIV], w_max_e[NIV], w_max_s[NIV], w_min_e[NIV];
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) {
+        my_s[k] = sm.start[k][wave * kRowsPerWave + r32];
+        my_w[k] = sm.width[k][wave * kRowsPerWave + r32];
+        const bool any = my_s[k] != kEmptyStart;
+        w_min_s[k] = wave_min(any ? my_s[k] : INT_MAX);
+        w_max_e[k] = wave_max(any ? my_s[k] + my_w[k] : INT_MIN);
+        w_max_s[k] = wave_max(any ? my_s[k] : (qrow < N ? INT_MAX : INT_MIN));
+        w_min_e[k] = wave_min(any ? my_s[k] + my_w[k] : (qrow < N ? INT_MIN : INT_MAX));
+    }
 
-    const int kv_first = tm.x;
-    const int kv_last = tm.y;
-    if (kv_first <= kv_last) {
+    // Key blocks in increasing order over the union of the ranges' non-skip
+    // blocks (one contiguous run for a single range).
+    int j = union_next<NIV>(tm, -1);
+    if (j != INT_MAX) {
         Staging<D> stage;
-        load_block<D>(stage, krs, vrs, kv_first * kBc, tid);
+        load_block<D>(stage, krs, vrs, j * kBc, tid);
         store_block<D>(stage, sm, 0, tid);
         __syncthreads();
 
-        for (int j = kv_first; j <= kv_last; ++j) {
-            const int buf = (j - kv_first) & 1;
-            const bool has_next = j < kv_last;
-            if (has_next) load_block<D>(stage, krs, vrs, (j + 1) * kBc, tid);
+        for (int buf = 0;; buf ^= 1) {
+            const int j_next = union_next<NIV>(tm, j);
+            const bool has_next = j_next != INT_MAX;
+            if (has_next) load_block<D>(stage, krs, vrs, j_next * kBc, tid);
 
             const int klo = j * kBc;
             const int khi = min(klo + kBc, N) - 1;
-            const bool wave_skip = khi < w_min_s || klo > w_max_e;
+            // The wavefront skips the block when each range of each of its
+            // rows misses it, and computes it without the compare when one
+            // range covers it for all of its rows.
+            bool wave_skip = true, wave_full = false;
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                wave_skip &= khi < w_min_s[k] || klo > w_max_e[k];
+                wave_full |= klo >= w_max_s[k] && khi <= w_min_e[k];
+            }
             if (!wave_skip) {
                 // ---- S^T = K Q^T: lane holds S[q = r32][key = 32 jb + 8 (v/4) + 4 half + v%4]
                 floatx16 st[kBc / 32];
@@ -286,15 +315,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
                 // ---- interval compare, only where some row of the wavefront
                 // does not attend the whole key block (boundary blocks).
-                const bool full = (klo + kBc <= N) && klo >= w_max_s && khi <= w_min_e;
+                const bool full = (klo + kBc <= N) && wave_full;
                 if (!full) {
-                    const int base = klo + 4 * half - my_s;
+                    int base[NIV];
+#pragma unroll
+                    for (int k = 0; k < NIV; ++k) base[k] = klo + 4 * half - my_s[k];
 #pragma unroll
                     for (int jb = 0; jb < kBc / 32; ++jb) {
 #pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const int off = jb * 32 + 8 * (v >> 2) + (v & 3);
-                            const bool ok = (uint32_t)(base + off) <= (uint32_t)my_w;
+                            bool ok = false;
+#pragma unroll
+                            for (int k = 0; k < NIV; ++k) ok |= (uint32_t)(base[k] + off) <= (uint32_t)my_w[k];
                             st[jb][v] = ok ? st[jb][v] : -INFINITY;
                         }
                     }
@@ -355,6 +388,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
             if (has_next) store_block<D>(stage, sm, buf ^ 1, tid);
             __syncthreads();
+            if (!has_next) break;
+            j = j_next;
         }
     }
 
@@ -381,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 }  // namespace
 
 hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
-                            const int32_t* col_end, const TileMeta* meta, const int32_t* order,
+                            const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const int64_t n_q = (N + kBr - 1) / kBr;
@@ -391,16 +426,19 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
     const auto* Kp = static_cast<const uint16_t*>(k);
     const auto* Vp = static_cast<const uint16_t*>(v);
     auto* Op = static_cast<uint16_t*>(out);
-    auto kernel = d == 128 ? attn_fwd_kernel<128> : attn_fwd_kernel<64>;
     // XCD-local head order needs whole heads per XCD and at least one XCD's
     // worth of resident workgroups (32 CUs x 2) per head.
     const int xcd_heads = (H % 8 == 0 && B * n_q >= 128) ? 1 : 0;
-    // With an event pair, the dispatch packet itself stamps the kernel's start
-    // and end, so the pair measures the kernel alone.
-    hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
-                          Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, xcd_heads, Op,
-                          lse);
-    return hipGetLastError();
+    return dispatch_ranges(n_iv, [&](auto niv) {
+        constexpr int NIV = decltype(niv)::value;
+        auto kernel = d == 128 ? attn_fwd_kernel<128, NIV> : attn_fwd_kernel<64, NIV>;
+        // With an event pair, the dispatch packet itself stamps the kernel's
+        // start and end, so the pair measures the kernel alone.
+        hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp,
+                              Kp, Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, xcd_heads,
+                              Op, lse);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace fm

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <climits>
+#include <type_traits>
 
 namespace fm {
 
@@ -18,22 +19,30 @@ namespace fm {
 constexpr int kBr = FM_QUERY_TILE;
 constexpr int kBc = FM_KEY_TILE;
 
-// Per query block (one sequence of one batch), computed from its rows' intervals:
+// Per query block and per key range of its rows (one sequence of one batch),
+// computed from the rows' intervals for that range:
 //   x = first non-skip key block, y = last non-skip key block (y < x: none),
 //   z = first FULL key block,     w = last FULL key block     (w < z: none).
-// Under the min/max rule the non-skip blocks and the full blocks each form one
-// contiguous range, so four integers describe the whole row of the class table.
+// Under the min/max rule the non-skip blocks and the full blocks of one range
+// each form one contiguous range of key blocks.  Rows may hold up to
+// kMaxRanges ranges (their union is attended); the records of query block
+// item are meta[item * n_iv + k], k < n_iv.
 using TileMeta = int4;
+constexpr int kMaxRanges = 4;
 
 // Interval preprocessor: one wavefront per (b, query block).
-//   meta[b*n_q + t], work[b*n_q + t] = non-skip key blocks (may be null),
-//   bad (may be null): set to 1 when a row breaks 0 <= s <= e <= N-1.
-hipError_t launch_preprocess(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
-                             int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* bad,
+//   col_start/col_end: [B][n_iv][N].
+//   meta[(b*n_q + t) * n_iv + k]; work[b*n_q + t] = non-skip key blocks of the
+//   union (may be null); bad (may be null): set to 1 when a row breaks
+//   0 <= s <= e <= N-1.
+hipError_t launch_preprocess(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
+                             int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* bad,
                              hipStream_t stream);
 
-// Expands meta of n_q query blocks into the uint8 class table [n_q][n_kv].
-hipError_t launch_class_table(const TileMeta* meta, int64_t n_q, int64_t n_kv, uint8_t* table,
+// Expands meta of n_q query blocks (n_iv ranges each) into the uint8 class
+// table [n_q][n_kv]: SKIP unless some range keeps the block, FULL when some
+// range covers it for every row, else PARTIAL.
+hipError_t launch_class_table(const TileMeta* meta, int n_iv, int64_t n_q, int64_t n_kv, uint8_t* table,
                               hipStream_t stream);
 
 // Longest-first order of M work items (ties by index).
@@ -42,14 +51,14 @@ hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipSt
 // Preprocessor and scheduler in one launch of one workgroup, for at most
 // kPrepSmallMax query blocks (B * n_q): same meta, work and order outputs.
 constexpr int kPrepSmallMax = 256;
-hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
-                             int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
+hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
+                             int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
                              hipStream_t stream);
 
 // Attention kernel.  order == nullptr runs query blocks in natural (b, t) order.
 // start/stop (may be null) are stamped at the kernel's own start and end.
 hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
-                            const int32_t* col_end, const TileMeta* meta, const int32_t* order,
+                            const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
@@ -130,6 +139,59 @@ __device__ __forceinline__ TileMeta query_block_meta(const int32_t* __restrict__
         m.w = -1;
     }
     return m;
+}
+
+// The key blocks a query block visits are the union of the non-skip ranges
+// [x, y] of its NIV records.  union_next gives the smallest block of that
+// union after block j (j = -1: the first block), or INT_MAX when none is left.
+// Every index is a compile-time constant after unrolling, so the records stay
+// in registers.
+template <int NIV>
+__device__ __forceinline__ int union_next(const TileMeta (&m)[NIV], int j) {
+    int best = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) {
+        const int c = max(j + 1, m[k].x);
+        if (c <= m[k].y) best = min(best, c);
+    }
+    return best;
+}
+
+// Number of key blocks in that union: runs of overlapping or adjacent ranges
+// are walked from left to right.
+template <int NIV>
+__device__ __forceinline__ int union_blocks(const TileMeta (&m)[NIV]) {
+    int total = 0;
+    int j = union_next<NIV>(m, -1);
+    while (j != INT_MAX) {
+        int e = j;                     // end of the run that starts at j
+        bool grew = true;
+        while (grew) {
+            grew = false;
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                if (m[k].x <= m[k].y && m[k].x <= e + 1 && m[k].y > e) {
+                    e = m[k].y;
+                    grew = true;
+                }
+            }
+        }
+        total += e - j + 1;
+        j = union_next<NIV>(m, e);
+    }
+    return total;
+}
+
+// Calls f(std::integral_constant<int, NIV>) for n_iv in 1..kMaxRanges.
+template <typename F>
+__host__ hipError_t dispatch_ranges(int n_iv, F&& f) {
+    switch (n_iv) {
+        case 1: return f(std::integral_constant<int, 1>{});
+        case 2: return f(std::integral_constant<int, 2>{});
+        case 3: return f(std::integral_constant<int, 3>{});
+        case 4: return f(std::integral_constant<int, 4>{});
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace fm

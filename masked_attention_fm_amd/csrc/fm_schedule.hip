@@ -47,6 +47,7 @@ constexpr int kPrepThreads = 1024;
 // Small problems: one workgroup computes every query block's metadata (one
 // wavefront per block, as the preprocessor does) and then ranks the blocks
 // from LDS, saving a launch.
+template <int NIV>
 __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int n_q, int n_kv,
     int Br, int Bc, int M, TileMeta* __restrict__ meta, int32_t* __restrict__ work,
@@ -56,12 +57,17 @@ __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
     for (int item = threadIdx.x >> 6; item < M; item += kPrepThreads / 64) {
         const int b = item / n_q;
         const int t = item - b * n_q;
-        int invalid = 0;
-        const TileMeta m = query_block_meta(col_start + (int64_t)b * N, col_end + (int64_t)b * N, t, N, Br,
-                                            Bc, n_kv, lane, &invalid);
+        TileMeta m[NIV];
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            const int64_t off = ((int64_t)b * NIV + k) * N;
+            int invalid = 0;
+            m[k] = query_block_meta(col_start + off, col_end + off, t, N, Br, Bc, n_kv, lane, &invalid);
+        }
         if (lane == 0) {
-            const int w = m.y >= m.x ? m.y - m.x + 1 : 0;
-            meta[item] = m;
+            const int w = union_blocks<NIV>(m);
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) meta[(int64_t)item * NIV + k] = m[k];
             work[item] = w;
             s_work[item] = w;
         }
@@ -80,16 +86,18 @@ __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
 
 }  // namespace
 
-hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t N,
-                             int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
+hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
+                             int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
                              hipStream_t stream) {
     const int64_t n_q = (N + Br - 1) / Br;
     const int64_t n_kv = (N + Bc - 1) / Bc;
     const int64_t M = B * n_q;
     if (M > kPrepSmallMax) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prep_small_kernel, dim3(1), dim3(kPrepThreads), 0, stream, col_start, col_end, (int)N,
-                       (int)n_q, (int)n_kv, Br, Bc, (int)M, meta, work, order);
-    return hipGetLastError();
+    return dispatch_ranges(n_iv, [&](auto niv) {
+        hipLaunchKernelGGL(prep_small_kernel<decltype(niv)::value>, dim3(1), dim3(kPrepThreads), 0, stream,
+                           col_start, col_end, (int)N, (int)n_q, (int)n_kv, Br, Bc, (int)M, meta, work, order);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream) {

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libf
 FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_BAD_INTERVAL, FM_ERR_HIP = range(5)
 FM_TILE_SKIP, FM_TILE_FULL, FM_TILE_PARTIAL = 0, 1, 2
 FM_OPT_SCHEDULE = 1
+FM_MAX_RANGES = 4
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -30,6 +31,10 @@ SIGNATURES = {
                                    _P, _P, _P]),
     "fm_attn_tile_shape": (ctypes.c_int, [_I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "fm_tile_schedule": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P]),
+    "fm_attn_fwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                         _P, _P, _P]),
+    "fm_classify_tiles_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P]),
+    "fm_tile_schedule_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P]),
     "fm_set_option": (ctypes.c_int, [ctypes.c_int, _I64]),
     "fm_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "fm_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
@@ -93,14 +98,16 @@ def fm_attn_tile_shape(d: int) -> Tuple[int, int]:
     return br.value, bc.value
 
 
-def fm_classify_tiles(col_start: torch.Tensor, col_end: torch.Tensor, Br: int, Bc: int,
-                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """uint8 [ceil(N/Br), ceil(N/Bc)] class table of one sequence (synchronous)."""
+def _intervals(col_start: torch.Tensor, col_end: torch.Tensor, shape: Tuple[int, ...], what: str):
     _dev_tensor(col_start, "col_start", torch.int32)
     _dev_tensor(col_end, "col_end", torch.int32)
-    if col_start.dim() != 1 or col_end.shape != col_start.shape:
-        raise ValueError("col_start / col_end must be 1-D of equal length")
-    N = col_start.shape[0]
+    if tuple(col_start.shape) != shape or tuple(col_end.shape) != shape:
+        raise ValueError(f"col_start / col_end must be {what}, got {tuple(col_start.shape)} "
+                         f"and {tuple(col_end.shape)}")
+
+
+def _classify(func: str, col_start, col_end, n_ranges: Optional[int], Br: int, Bc: int, out):
+    N = col_start.shape[-1]
     shape = (-(-N // Br), -(-N // Bc)) if Br > 0 and Bc > 0 else (0, 0)
     if out is None:
         out = torch.empty(shape, dtype=torch.uint8, device=col_start.device)
@@ -109,42 +116,72 @@ def fm_classify_tiles(col_start: torch.Tensor, col_end: torch.Tensor, Br: int, B
         if tuple(out.shape) != shape:
             raise ValueError(f"out must have shape {shape}")
     torch.cuda.current_stream(col_start.device).synchronize()
-    _check("fm_classify_tiles", lib().fm_classify_tiles(col_start.data_ptr(), col_end.data_ptr(), N,
-                                                         int(Br), int(Bc), out.data_ptr()))
+    L = lib()
+    if n_ranges is None:
+        status = L.fm_classify_tiles(col_start.data_ptr(), col_end.data_ptr(), N, int(Br), int(Bc),
+                                     out.data_ptr())
+    else:
+        status = L.fm_classify_tiles_multi(col_start.data_ptr(), col_end.data_ptr(), n_ranges, N, int(Br),
+                                           int(Bc), out.data_ptr())
+    _check(func, status)
     return out
 
 
-def fm_tile_schedule(col_start: torch.Tensor, col_end: torch.Tensor, d: int):
-    """(work, order) int32 [B * ceil(N/Br)] of the attention kernel's scheduler (synchronous)."""
-    _dev_tensor(col_start, "col_start", torch.int32)
-    _dev_tensor(col_end, "col_end", torch.int32)
-    if col_start.dim() != 2 or col_end.shape != col_start.shape:
-        raise ValueError("col_start / col_end must be [B, N]")
-    B, N = col_start.shape
+def fm_classify_tiles(col_start: torch.Tensor, col_end: torch.Tensor, Br: int, Bc: int,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """uint8 [ceil(N/Br), ceil(N/Bc)] class table of one sequence, intervals [N] (synchronous)."""
+    if col_start.dim() != 1:
+        raise ValueError("col_start / col_end must be 1-D of equal length")
+    _intervals(col_start, col_end, tuple(col_start.shape), "[N]")
+    return _classify("fm_classify_tiles", col_start, col_end, None, Br, Bc, out)
+
+
+def fm_classify_tiles_multi(col_start: torch.Tensor, col_end: torch.Tensor, Br: int, Bc: int,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Class table of one sequence whose rows hold K ranges, intervals [K, N] (synchronous)."""
+    if col_start.dim() != 2:
+        raise ValueError("col_start / col_end must be [K, N]")
+    _intervals(col_start, col_end, tuple(col_start.shape), "[K, N]")
+    return _classify("fm_classify_tiles_multi", col_start, col_end, col_start.shape[0], Br, Bc, out)
+
+
+def _schedule(func: str, col_start, col_end, n_ranges: Optional[int], d: int):
+    B, N = col_start.shape[0], col_start.shape[-1]
     br, _ = fm_attn_tile_shape(d)
     M = B * (-(-N // br))
     work = torch.empty(M, dtype=torch.int32, device=col_start.device)
     order = torch.empty(M, dtype=torch.int32, device=col_start.device)
     torch.cuda.current_stream(col_start.device).synchronize()
-    _check("fm_tile_schedule", lib().fm_tile_schedule(col_start.data_ptr(), col_end.data_ptr(), B, N,
-                                                       int(d), work.data_ptr(), order.data_ptr()))
+    L = lib()
+    if n_ranges is None:
+        status = L.fm_tile_schedule(col_start.data_ptr(), col_end.data_ptr(), B, N, int(d), work.data_ptr(),
+                                    order.data_ptr())
+    else:
+        status = L.fm_tile_schedule_multi(col_start.data_ptr(), col_end.data_ptr(), n_ranges, B, N, int(d),
+                                          work.data_ptr(), order.data_ptr())
+    _check(func, status)
     return work, order
 
 
-def fm_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: torch.Tensor,
-                col_end: torch.Tensor, scale: Optional[float] = None,
-                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Masked attention forward; returns (out bf16 [B,H,N,d], lse fp32 [B,H,N]).  Asynchronous."""
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        _dev_tensor(x, name, torch.bfloat16)
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    B, H, N, d = q.shape
-    _dev_tensor(col_start, "col_start", torch.int32)
-    _dev_tensor(col_end, "col_end", torch.int32)
-    if tuple(col_start.shape) != (B, N) or tuple(col_end.shape) != (B, N):
+def fm_tile_schedule(col_start: torch.Tensor, col_end: torch.Tensor, d: int):
+    """(work, order) int32 [B * ceil(N/Br)] of the attention kernel's scheduler, intervals [B, N]
+    (synchronous)."""
+    if col_start.dim() != 2:
         raise ValueError("col_start / col_end must be [B, N]")
+    _intervals(col_start, col_end, tuple(col_start.shape), "[B, N]")
+    return _schedule("fm_tile_schedule", col_start, col_end, None, d)
+
+
+def fm_tile_schedule_multi(col_start: torch.Tensor, col_end: torch.Tensor, d: int):
+    """fm_tile_schedule for intervals [B, K, N] (synchronous)."""
+    if col_start.dim() != 3:
+        raise ValueError("col_start / col_end must be [B, K, N]")
+    _intervals(col_start, col_end, tuple(col_start.shape), "[B, K, N]")
+    return _schedule("fm_tile_schedule_multi", col_start, col_end, col_start.shape[1], d)
+
+
+def _attn(func: str, q, k, v, col_start, col_end, n_ranges: Optional[int], scale, out, lse, stream):
+    B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     if out is None:
@@ -159,11 +196,49 @@ def fm_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: to
         _dev_tensor(lse, "lse", torch.float32)
         if tuple(lse.shape) != (B, H, N):
             raise ValueError("lse must be [B, H, N]")
-    status = lib().fm_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), col_start.data_ptr(),
-                               col_end.data_ptr(), B, H, N, d, float(scale), out.data_ptr(),
-                               lse.data_ptr(), _stream_handle(stream))
-    _check("fm_attn_fwd", status)
+    L = lib()
+    if n_ranges is None:
+        status = L.fm_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), col_start.data_ptr(),
+                               col_end.data_ptr(), B, H, N, d, float(scale), out.data_ptr(), lse.data_ptr(),
+                               _stream_handle(stream))
+    else:
+        status = L.fm_attn_fwd_multi(q.data_ptr(), k.data_ptr(), v.data_ptr(), col_start.data_ptr(),
+                                     col_end.data_ptr(), n_ranges, B, H, N, d, float(scale), out.data_ptr(),
+                                     lse.data_ptr(), _stream_handle(stream))
+    _check(func, status)
     return out, lse
+
+
+def _qkv(q, k, v):
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(x, name, torch.bfloat16)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    return q.shape
+
+
+def fm_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: torch.Tensor,
+                col_end: torch.Tensor, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Masked attention forward, intervals [B, N]; returns (out bf16 [B,H,N,d], lse fp32 [B,H,N]).
+    Asynchronous."""
+    B, H, N, d = _qkv(q, k, v)
+    _intervals(col_start, col_end, (B, N), "[B, N]")
+    return _attn("fm_attn_fwd", q, k, v, col_start, col_end, None, scale, out, lse, stream)
+
+
+def fm_attn_fwd_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: torch.Tensor,
+                      col_end: torch.Tensor, scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fm_attn_fwd for rows with K ranges, intervals [B, K, N]; each row attends their union."""
+    B, H, N, d = _qkv(q, k, v)
+    if col_start.dim() != 3:
+        raise ValueError("col_start / col_end must be [B, K, N]")
+    _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
+    return _attn("fm_attn_fwd_multi", q, k, v, col_start, col_end, col_start.shape[1], scale, out, lse,
+                 stream)
 
 
 def fm_set_option(option: int, value: int) -> None:

@@ -125,3 +125,48 @@ def test_binding_refuses_cpu_tensors(L):
     s = torch.zeros(1, 8, dtype=torch.int32)
     with pytest.raises(ValueError):
         fmb.fm_attn_fwd(x, x, x, s, s)
+
+
+def attn_multi(L, n_ranges, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cs=FAKE, ce=FAKE, B=1, H=1, N=128, d=128, scale=0.125,
+                out=FAKE, lse=FAKE)
+    args.update(kw)
+    return L.fm_attn_fwd_multi(args["q"], args["k"], args["v"], args["cs"], args["ce"], n_ranges, args["B"],
+                               args["H"], args["N"], args["d"], args["scale"], args["out"], args["lse"],
+                               None)
+
+
+@pytest.mark.parametrize("n_ranges,kw,status", [
+    (0, {}, fmb.FM_ERR_INVALID_ARG),
+    (-1, {}, fmb.FM_ERR_INVALID_ARG),
+    (fmb.FM_MAX_RANGES + 1, {}, fmb.FM_ERR_INVALID_ARG),
+    (2, dict(q=None), fmb.FM_ERR_INVALID_ARG),
+    (2, dict(ce=FAKE + 2), fmb.FM_ERR_INVALID_ARG),
+    (2, dict(d=80), fmb.FM_ERR_UNSUPPORTED),
+    (3, dict(scale=float("nan")), fmb.FM_ERR_INVALID_ARG),
+    (4, dict(N=(1 << 22) + 1), fmb.FM_ERR_INVALID_ARG),
+])
+def test_attn_fwd_multi_rejects_bad_arguments(L, n_ranges, kw, status):
+    assert attn_multi(L, n_ranges, **kw) == status
+
+
+def test_classify_and_schedule_multi_reject_bad_arguments(L):
+    assert L.fm_classify_tiles_multi(FAKE, FAKE, 0, 100, 16, 16, FAKE) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_classify_tiles_multi(FAKE, FAKE, 5, 100, 16, 16, FAKE) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_classify_tiles_multi(FAKE, FAKE, 2, 100, 0, 16, FAKE) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_classify_tiles_multi(FAKE, None, 2, 100, 16, 16, FAKE) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_tile_schedule_multi(FAKE, FAKE, 0, 1, 100, 128, FAKE, FAKE) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_tile_schedule_multi(FAKE, FAKE, 2, 1, 100, 96, FAKE, FAKE) == fmb.FM_ERR_UNSUPPORTED
+
+
+def test_header_range_limit_matches_binding():
+    text = open(HEADER, encoding="utf-8").read()
+    assert re.search(r"#define FM_MAX_RANGES (\d+)", text).group(1) == str(fmb.FM_MAX_RANGES)
+
+
+def test_binding_multi_checks_shapes(L):
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    s = torch.zeros(1, 8, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fmb.fm_attn_fwd_multi(x, x, x, s, s)
