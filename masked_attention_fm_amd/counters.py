@@ -19,12 +19,16 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-ATTN_SOURCE = os.path.join(PKG, "csrc", "fm_attn_fwd.hip")
+# The attention kernel and the header whose device helpers it inlines.
+ATTN_SOURCES = [os.path.join(PKG, "csrc", "fm_attn_fwd.hip"), os.path.join(PKG, "csrc", "fm_internal.h")]
 
 
 def attn_source_hash() -> str:
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _kind(name: str) -> str:

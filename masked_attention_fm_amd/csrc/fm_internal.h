@@ -91,20 +91,16 @@ __device__ __forceinline__ int wave_max(int v) {
 }
 
 
-// Tile metadata of query block t of one sequence, reduced by one wavefront
-// (all 64 lanes must call it).  Rows past N are neutral; a row with no key in
-// [0, N) adds nothing to the non-skip range but rules out FULL blocks.
-// `invalid` (per lane) is set when a row breaks 0 <= s <= e <= N-1.
-__device__ __forceinline__ TileMeta query_block_meta(const int32_t* __restrict__ s_row,
-                                                     const int32_t* __restrict__ e_row, int t, int N,
-                                                     int Br, int Bc, int n_kv, int lane, int* invalid) {
+// Bounds of a set of rows' intervals: the non-skip range needs the smallest
+// start and largest end of the rows that attend some key, the full range the
+// largest start and smallest end of all rows (a row with no key in [0, N)
+// rules out FULL blocks).  `bad` flags a row that breaks 0 <= s <= e <= N-1.
+struct RowBounds {
     int min_s = INT_MAX, max_e = INT_MIN;   // non-skip range
     int max_s = INT_MIN, min_e = INT_MAX;   // full range
     int bad = 0;
-    const int r_end = min(t * Br + Br, N);
-    for (int r = t * Br + lane; r < r_end; r += 64) {
-        const int s = s_row[r];
-        const int e = e_row[r];
+
+    __device__ __forceinline__ void add(int s, int e, int N) {
         bad |= (s < 0) | (e > N - 1) | (s > e);
         const int sc = max(s, 0);
         const int ec = min(e, N - 1);
@@ -118,27 +114,43 @@ __device__ __forceinline__ TileMeta query_block_meta(const int32_t* __restrict__
             min_e = INT_MIN;
         }
     }
-    min_s = wave_min(min_s);
-    max_e = wave_max(max_e);
-    max_s = wave_max(max_s);
-    min_e = wave_min(min_e);
-    *invalid = bad;
-    TileMeta m;
-    if (max_e < min_s) {          // no row attends any key
-        m.x = 0;
-        m.y = -1;
-    } else {
-        m.x = min_s / Bc;
-        m.y = max_e / Bc;
+
+    // The tile record of a query block from the bounds of all of its rows.
+    __device__ __forceinline__ TileMeta meta(int N, int Bc, int n_kv) const {
+        TileMeta m;
+        if (max_e < min_s) {          // no row attends any key
+            m.x = 0;
+            m.y = -1;
+        } else {
+            m.x = min_s / Bc;
+            m.y = max_e / Bc;
+        }
+        if (max_s <= min_e) {
+            m.z = (max_s + Bc - 1) / Bc;
+            m.w = (min_e == N - 1) ? n_kv - 1 : (min_e + 1) / Bc - 1;
+        } else {
+            m.z = 0;
+            m.w = -1;
+        }
+        return m;
     }
-    if (max_s <= min_e) {
-        m.z = (max_s + Bc - 1) / Bc;
-        m.w = (min_e == N - 1) ? n_kv - 1 : (min_e + 1) / Bc - 1;
-    } else {
-        m.z = 0;
-        m.w = -1;
-    }
-    return m;
+};
+
+// Tile metadata of query block t of one sequence, reduced by one wavefront
+// (all 64 lanes must call it).  Rows past N are neutral.  `invalid` (per
+// lane) is set when one of the lane's rows breaks 0 <= s <= e <= N-1.
+__device__ __forceinline__ TileMeta query_block_meta(const int32_t* __restrict__ s_row,
+                                                     const int32_t* __restrict__ e_row, int t, int N,
+                                                     int Br, int Bc, int n_kv, int lane, int* invalid) {
+    RowBounds rb;
+    const int r_end = min(t * Br + Br, N);
+    for (int r = t * Br + lane; r < r_end; r += 64) rb.add(s_row[r], e_row[r], N);
+    *invalid = rb.bad;
+    rb.min_s = wave_min(rb.min_s);
+    rb.max_e = wave_max(rb.max_e);
+    rb.max_s = wave_max(rb.max_s);
+    rb.min_e = wave_min(rb.min_e);
+    return rb.meta(N, Bc, n_kv);
 }
 
 // The key blocks a query block visits are the union of the non-skip ranges

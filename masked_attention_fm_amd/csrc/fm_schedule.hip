@@ -44,27 +44,41 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __res
 
 constexpr int kPrepThreads = 1024;
 
-// Small problems: one workgroup computes every query block's metadata (one
-// wavefront per block, as the preprocessor does) and then ranks the blocks
-// from LDS, saving a launch.
+// Small problems: one workgroup computes every query block's metadata and
+// then ranks the blocks from LDS, saving a launch.  Each query block gets a
+// group of G lanes (G = 1024 / M rounded down to a power of two, at most 64);
+// a lane reads every G-th row of the block with its loads unrolled, so that
+// they are all in flight at once, and the group reduces by lane exchange.
 template <int NIV>
 __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int n_q, int n_kv,
-    int Br, int Bc, int M, TileMeta* __restrict__ meta, int32_t* __restrict__ work,
+    int Br, int Bc, int M, int G, TileMeta* __restrict__ meta, int32_t* __restrict__ work,
     int32_t* __restrict__ order) {
     __shared__ int s_work[kPrepSmallMax];
-    const int lane = threadIdx.x & 63;
-    for (int item = threadIdx.x >> 6; item < M; item += kPrepThreads / 64) {
+    const int item = threadIdx.x / G;          // G divides 64: a group never straddles wavefronts
+    const int g = threadIdx.x % G;
+    if (item < M) {
         const int b = item / n_q;
         const int t = item - b * n_q;
+        const int r0 = t * Br;
+        const int r_end = min(r0 + Br, N);
         TileMeta m[NIV];
 #pragma unroll
         for (int k = 0; k < NIV; ++k) {
-            const int64_t off = ((int64_t)b * NIV + k) * N;
-            int invalid = 0;
-            m[k] = query_block_meta(col_start + off, col_end + off, t, N, Br, Bc, n_kv, lane, &invalid);
+            const int32_t* s_row = col_start + ((int64_t)b * NIV + k) * N;
+            const int32_t* e_row = col_end + ((int64_t)b * NIV + k) * N;
+            RowBounds rb;
+#pragma unroll 8
+            for (int r = r0 + g; r < r_end; r += G) rb.add(s_row[r], e_row[r], N);
+            for (int off = G >> 1; off > 0; off >>= 1) {
+                rb.min_s = min(rb.min_s, __shfl_xor(rb.min_s, off));
+                rb.max_e = max(rb.max_e, __shfl_xor(rb.max_e, off));
+                rb.max_s = max(rb.max_s, __shfl_xor(rb.max_s, off));
+                rb.min_e = min(rb.min_e, __shfl_xor(rb.min_e, off));
+            }
+            m[k] = rb.meta(N, Bc, n_kv);
         }
-        if (lane == 0) {
+        if (g == 0) {
             const int w = union_blocks<NIV>(m);
 #pragma unroll
             for (int k = 0; k < NIV; ++k) meta[(int64_t)item * NIV + k] = m[k];
@@ -93,9 +107,12 @@ hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, i
     const int64_t n_kv = (N + Bc - 1) / Bc;
     const int64_t M = B * n_q;
     if (M > kPrepSmallMax) return hipErrorInvalidValue;
+    int G = 64;                                 // lanes per query block: a power of two, G * M <= 1024
+    while (G * M > kPrepThreads) G >>= 1;
     return dispatch_ranges(n_iv, [&](auto niv) {
         hipLaunchKernelGGL(prep_small_kernel<decltype(niv)::value>, dim3(1), dim3(kPrepThreads), 0, stream,
-                           col_start, col_end, (int)N, (int)n_q, (int)n_kv, Br, Bc, (int)M, meta, work, order);
+                           col_start, col_end, (int)N, (int)n_q, (int)n_kv, Br, Bc, (int)M, G, meta, work,
+                           order);
         return hipGetLastError();
     });
 }

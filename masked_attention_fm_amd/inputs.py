@@ -14,6 +14,9 @@ section 4.1):
 * prefix-LM         rows i <  p attend [0, p-1]; rows i >= p attend [0, i]
 * document packing  row i of the document starting at ``offset`` attends
                     [offset, i]                          (section 3.3 example)
+* sinks + window    two ranges per row, united: the first ``sinks`` keys
+                    (causally) and a causal window of w keys (section 5.2
+                    item 4; several ranges per row: section 6.1 item 1)
 
 Random draws
 ------------
@@ -160,20 +163,29 @@ CONFIGS: Dict[str, Config] = {
     "C4": Config("C4", "prefix_lm", 2, 32, 16384, 128, "prefix_lm", 1003),
     "C5": Config("C5", "long_context_packed", 1, 8, 131072, 128, "doc_lognormal", 1004,
                  (("median", 4096), ("sigma", 1.0), ("lo", 128), ("hi", 32768))),
+    # Rows with two ranges: the article's sinks example (10 sink tokens, a
+    # window of 1024 keys) at the sliding-window workload's shape.
+    "S1": Config("S1", "sinks_plus_window", 1, 16, 32768, 128, "sinks_window", 1005,
+                 (("window", 1024), ("sinks", 10))),
 }
 
 
 @dataclasses.dataclass
 class MaskSpec:
-    col_start: np.ndarray           # int32 [B, N]
-    col_end: np.ndarray             # int32 [B, N]
+    col_start: np.ndarray           # int32 [B, N], or [B, K, N] for K ranges per row
+    col_end: np.ndarray             # same shape as col_start
     doc_lengths: Optional[List[List[int]]] = None   # per batch, for document masks
     prefix: Optional[List[int]] = None              # per batch, for prefix-LM
 
 
 def make_intervals(mask: str, B: int, N: int, seed: int, **params) -> MaskSpec:
-    """Build the [B, N] interval arrays of one mask family from a seed."""
+    """Build the [B, N] interval arrays of one mask family from a seed ([B, K, N]
+    for the families with K ranges per row)."""
     rng = np.random.default_rng(seed)
+    if mask == "sinks_window":
+        s, e = sinks_window_intervals(N, int(params["window"]), int(params["sinks"]))
+        return MaskSpec(np.ascontiguousarray(np.broadcast_to(s, (B,) + s.shape)),
+                        np.ascontiguousarray(np.broadcast_to(e, (B,) + e.shape)))
     cs = np.empty((B, N), np.int32)
     ce = np.empty((B, N), np.int32)
     docs: Optional[List[List[int]]] = None

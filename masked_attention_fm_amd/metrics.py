@@ -20,6 +20,35 @@ def attended_pairs(col_start: np.ndarray, col_end: np.ndarray, N: int) -> int:
     return int(np.maximum(e - s + 1, 0).sum())
 
 
+def attended_pairs_union(col_start: np.ndarray, col_end: np.ndarray, N: int) -> int:
+    """Attended (row, key) pairs for rows with K ranges, arrays [..., K, N]: a key
+    inside several ranges of a row counts once.  The ranges of each row are
+    taken in increasing start order and each adds the keys past the furthest
+    end seen so far."""
+    s = np.maximum(np.asarray(col_start, np.int64), 0)
+    e = np.minimum(np.asarray(col_end, np.int64), N - 1)
+    empty = s > e
+    s = np.where(empty, N, s)                       # empty ranges sort last and add nothing
+    e = np.where(empty, -1, e)
+    order = np.argsort(s, axis=-2, kind="stable")
+    s = np.take_along_axis(s, order, axis=-2)
+    e = np.take_along_axis(e, order, axis=-2)
+    reach = np.full(s.shape[:-2] + s.shape[-1:], -1, np.int64)
+    total = 0
+    for k in range(s.shape[-2]):
+        sk, ek = s[..., k, :], e[..., k, :]
+        total += int(np.maximum(ek - np.maximum(sk, reach + 1) + 1, 0).sum())
+        reach = np.maximum(reach, ek)
+    return total
+
+
+def spec_attended_pairs(col_start: np.ndarray, col_end: np.ndarray, N: int) -> int:
+    """attended_pairs for [B, N] intervals, attended_pairs_union for [B, K, N]."""
+    if np.ndim(col_start) == 3:
+        return attended_pairs_union(col_start, col_end, N)
+    return attended_pairs(col_start, col_end, N)
+
+
 def effective_flops(col_start: np.ndarray, col_end: np.ndarray, N: int, H: int, d: int) -> int:
     return 4 * d * H * attended_pairs(col_start, col_end, N)
 

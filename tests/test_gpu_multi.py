@@ -205,17 +205,21 @@ def test_multi_q_zero_is_union_mean():
         assert np.abs(L[0, :, i] - np.log(n)).max() <= LSE_TOL
 
 
-def test_sinks_window_long_sequence_sampled():
-    """Attention sinks plus a window at a long length (10 sink tokens, a window of
-    1024 keys), on sampled rows: the first rows, block edges, rows where the
-    window leaves the sinks, and random rows."""
-    B, H, N, d = 1, 4, 32768, 128
-    w, sinks = 1024, 10
-    s, e = sinks_window(B, N, w, sinks)
-    q, k, v = inputs.make_qkv(B, H, N, d, seed=31)
-    rng = np.random.default_rng(31)
-    picks = {0, 1, 9, 10, 11, 127, 128, 1023, 1024, 1033, 1034, 1035, 1100, N // 2, N - 1}
-    picks.update(int(x) for x in rng.integers(0, N, 200))
+def test_sinks_window_workload_sampled():
+    """The sinks-plus-window workload at full size, in the launch configuration the
+    benchmark times, on sampled rows: the first rows, block edges, the rows where
+    the window leaves the sinks, and random rows, for every head."""
+    cfg = inputs.CONFIGS["S1"]
+    spec = inputs.config_intervals(cfg)
+    w, sinks = cfg.param("window"), cfg.param("sinks")
+    q, k, v = inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    rng = np.random.default_rng(cfg.seed)
+    join = w + sinks
+    picks = {0, 1, sinks - 1, sinks, sinks + 1, 127, 128, w - 1, w, join - 2, join - 1, join, join + 1,
+             cfg.N // 2, cfg.N - 1}
+    picks.update(int(x) for x in rng.integers(0, cfg.N, 200))
     rows = np.array(sorted(picks))
-    log("sinks+window N=32768")
-    check_multi(q, k, v, s, e, inputs.default_scale(d), "sinks+window 32768", rows=rows)
+    log(f"workload {cfg.describe()}")
+    dO, dL = check_multi(q, k, v, spec.col_start, spec.col_end, inputs.default_scale(cfg.d),
+                         "S1 sinks+window", rows=rows)
+    log(f"S1: worst max|dO|={dO:.3e} max|dLSE|={dL:.3e} ({len(rows)} sampled rows, all {cfg.H} heads)")

@@ -27,6 +27,27 @@ def test_attended_pairs_general_intervals():
     assert metrics.attended_pairs(s, e, N) == oracle.unmasked_count(s, e, N)
 
 
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_attended_pairs_union_equals_dense_count(K):
+    rng = np.random.default_rng(40 + K)
+    N = 500
+    s, e = inputs.random_multi_intervals(rng, 2, K, N, empty_frac=0.2, max_width=120)
+    s[:, 0, :50] -= 80                              # some ranges reach outside [0, N)
+    e[:, -1, -50:] += 80
+    assert metrics.attended_pairs_union(s, e, N) == sum(oracle.unmasked_count(s[b], e[b], N) for b in range(2))
+
+
+def test_sinks_window_pairs_closed_form():
+    """10 sinks and a window of 1024: rows up to 1033 see [0, i]; later rows 10 + 1024 keys."""
+    cfg = inputs.CONFIGS["S1"]
+    spec = inputs.config_intervals(cfg)
+    n_join = cfg.param("window") + cfg.param("sinks")          # first row whose window leaves the sinks
+    expect = n_join * (n_join + 1) // 2 + (cfg.N - n_join) * n_join
+    assert metrics.spec_attended_pairs(spec.col_start, spec.col_end, cfg.N) == expect
+    assert metrics.spec_attended_pairs(spec.col_start[:, :, :3000], spec.col_end[:, :, :3000], 3000) == \
+        oracle.unmasked_count(spec.col_start[0, :, :3000], spec.col_end[0, :, :3000], 3000)
+
+
 def test_effective_flops_c1_closed_form():
     cfg = inputs.CONFIGS["C1"]
     spec = inputs.config_intervals(cfg)

@@ -72,7 +72,14 @@ def test_config_intervals_deterministic_and_valid():
         a = inputs.config_intervals(cfg)
         b = inputs.config_intervals(cfg)
         assert np.array_equal(a.col_start, b.col_start) and np.array_equal(a.col_end, b.col_end)
-        assert a.col_start.shape == (cfg.B, cfg.N) and a.col_start.dtype == np.int32
+        assert a.col_start.dtype == np.int32 and a.col_end.shape == a.col_start.shape
+        if cfg.mask == "sinks_window":
+            assert a.col_start.shape == (cfg.B, 2, cfg.N)
+            s, e = inputs.sinks_window_intervals(cfg.N, cfg.param("window"), cfg.param("sinks"))
+            assert all(np.array_equal(a.col_start[b], s) and np.array_equal(a.col_end[b], e)
+                       for b in range(cfg.B))
+            continue
+        assert a.col_start.shape == (cfg.B, cfg.N)
         assert np.all(0 <= a.col_start) and np.all(a.col_start <= a.col_end)
         assert np.all(a.col_end <= cfg.N - 1)
         if cfg.mask == "prefix_lm":
