@@ -47,14 +47,17 @@ constexpr int kPrepThreads = 1024;
 // Small problems: one workgroup computes every query block's metadata and
 // then ranks the blocks from LDS, saving a launch.  Each query block gets a
 // group of G lanes (G = 1024 / M rounded down to a power of two, at most 64);
-// a lane reads every G-th row of the block with its loads unrolled, so that
-// they are all in flight at once, and the group reduces by lane exchange.
+// a lane reads every G-th row (or 16-byte chunk of four rows) of the block
+// with its loads unrolled, so that they are all in flight at once, and the
+// group reduces by lane exchange.  The same groups then rank the items: each
+// lane counts over one slice of the work array.
 template <int NIV>
 __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int n_q, int n_kv,
-    int Br, int Bc, int M, int G, TileMeta* __restrict__ meta, int32_t* __restrict__ work,
+    int Br, int Bc, int M, int G, bool vec4, TileMeta* __restrict__ meta, int32_t* __restrict__ work,
     int32_t* __restrict__ order) {
-    __shared__ int s_work[kPrepSmallMax];
+    // work of each item, padded with INT_MIN up to G * SL <= M + 4 G <= 2 * kPrepSmallMax entries
+    __shared__ __attribute__((aligned(16))) int s_work[2 * kPrepSmallMax];
     const int item = threadIdx.x / G;          // G divides 64: a group never straddles wavefronts
     const int g = threadIdx.x % G;
     if (item < M) {
@@ -68,8 +71,23 @@ __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
             const int32_t* s_row = col_start + ((int64_t)b * NIV + k) * N;
             const int32_t* e_row = col_end + ((int64_t)b * NIV + k) * N;
             RowBounds rb;
+            if (vec4) {
+                // rows in 16-byte chunks of four (N and both bases are multiples of 4 rows)
+                const int4* s4 = reinterpret_cast<const int4*>(s_row);
+                const int4* e4 = reinterpret_cast<const int4*>(e_row);
 #pragma unroll 8
-            for (int r = r0 + g; r < r_end; r += G) rb.add(s_row[r], e_row[r], N);
+                for (int c = (r0 >> 2) + g; c < (r_end >> 2); c += G) {
+                    const int4 sv = s4[c];
+                    const int4 ev = e4[c];
+                    rb.add(sv.x, ev.x, N);
+                    rb.add(sv.y, ev.y, N);
+                    rb.add(sv.z, ev.z, N);
+                    rb.add(sv.w, ev.w, N);
+                }
+            } else {
+#pragma unroll 8
+                for (int r = r0 + g; r < r_end; r += G) rb.add(s_row[r], e_row[r], N);
+            }
             for (int off = G >> 1; off > 0; off >>= 1) {
                 rb.min_s = min(rb.min_s, __shfl_xor(rb.min_s, off));
                 rb.max_e = max(rb.max_e, __shfl_xor(rb.max_e, off));
@@ -86,15 +104,26 @@ __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
             s_work[item] = w;
         }
     }
+    // Rank: the G lanes of item x each count the items ranked ahead of x in
+    // one slice of SL entries of s_work (SL a multiple of 4, read 16 bytes at
+    // a time); entries past M hold INT_MIN and never count.
+    const int SL = (((M + G - 1) / G) + 3) & ~3;
+    for (int y = M + threadIdx.x; y < G * SL; y += kPrepThreads) s_work[y] = INT_MIN;
     __syncthreads();
-    for (int x = threadIdx.x; x < M; x += kPrepThreads) {
-        const int wx = s_work[x];
+    if (item < M) {
+        const int wx = s_work[item];
         int rank = 0;
-        for (int y = 0; y < M; ++y) {
-            const int wy = s_work[y];
-            rank += (wy > wx) | ((wy == wx) & (y < x));
+        const int4* w4 = reinterpret_cast<const int4*>(s_work + g * SL);
+        for (int c = 0; c < SL / 4; ++c) {
+            const int4 w = w4[c];
+            const int y = g * SL + 4 * c;
+            rank += (w.x > wx) | ((w.x == wx) & (y < item));
+            rank += (w.y > wx) | ((w.y == wx) & (y + 1 < item));
+            rank += (w.z > wx) | ((w.z == wx) & (y + 2 < item));
+            rank += (w.w > wx) | ((w.w == wx) & (y + 3 < item));
         }
-        order[rank] = x;
+        for (int off = G >> 1; off > 0; off >>= 1) rank += __shfl_xor(rank, off);
+        if (g == 0) order[rank] = item;
     }
 }
 
@@ -109,10 +138,13 @@ hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, i
     if (M > kPrepSmallMax) return hipErrorInvalidValue;
     int G = 64;                                 // lanes per query block: a power of two, G * M <= 1024
     while (G * M > kPrepThreads) G >>= 1;
+    // 128-bit interval loads when every query block starts on a 16-byte boundary
+    const bool vec4 = N % 4 == 0 && Br % 4 == 0 && (reinterpret_cast<uintptr_t>(col_start) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(col_end) & 15) == 0;
     return dispatch_ranges(n_iv, [&](auto niv) {
         hipLaunchKernelGGL(prep_small_kernel<decltype(niv)::value>, dim3(1), dim3(kPrepThreads), 0, stream,
-                           col_start, col_end, (int)N, (int)n_q, (int)n_kv, Br, Bc, (int)M, G, meta, work,
-                           order);
+                           col_start, col_end, (int)N, (int)n_q, (int)n_kv, Br, Bc, (int)M, G, vec4, meta,
+                           work, order);
         return hipGetLastError();
     });
 }
