@@ -20,16 +20,19 @@ Sources (web pages, cited by title and section):
   article): §2 item 2, softmax of scaled scores q_i.k_j/sqrt(d) with max
   subtraction.
 * "FlashMask: Efficient and Rich Mask Extension of FlashAttention"
-  (abstract): skipping masked work does not change accuracy.
+  (abstract): skipping masked work does not change accuracy; the method is
+  used in training, which needs the gradients (``attention_bwd``: the chain
+  rule through the forward definition).
 
 Every function here is pinned by CPU tests against values fixed by the
 pages or by mathematics (closed forms, invariants, brute force, library
 routines); none is "parity unpinned".
 """
 from .attention import attention, attention_weights, dense_mask, bf16_round
+from .backward import attention_bwd
 from .tiles import (SKIP, FULL, PARTIAL, classes_minmax, classes_minmax_multi, classes_dense,
                     unmasked_count)
 
-__all__ = ["attention", "attention_weights", "dense_mask", "bf16_round",
+__all__ = ["attention", "attention_weights", "attention_bwd", "dense_mask", "bf16_round",
            "SKIP", "FULL", "PARTIAL", "classes_minmax", "classes_minmax_multi", "classes_dense",
            "unmasked_count"]

@@ -10,6 +10,7 @@ import types
 import pytest
 
 import test_oracle
+import test_oracle_bwd
 import test_oracle_tiles
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
@@ -22,7 +23,8 @@ def _mutant(module_file, old, new, extra_globals=None):
     src = src.replace(old, new)
     mod = types.ModuleType("oracle_mutant")
     mod.__dict__.update(extra_globals or {})
-    code = compile(src.replace("from .attention import dense_mask", ""), module_file, "exec")
+    code = compile(src.replace("from .attention import dense_mask", "from oracle.attention import dense_mask"),
+                   module_file, "exec")
     exec(code, mod.__dict__)
     return mod
 
@@ -94,3 +96,26 @@ def test_multi_tile_mutant_is_caught(name):
     old, new = MULTI_TILE_MUTANTS[name]
     mod = _mutant("tiles.py", old, new, {"dense_mask": oracle.dense_mask})
     assert _caught(test_oracle_tiles.MULTI_PINS, mod.classes_minmax_multi), f"mutant {name} survived every pin"
+
+
+BWD_MUTANTS = {
+    "no_row_correction": ("dS = P * (dP - Dr[:, None])", "dS = P * dP"),
+    "row_correction_sign": ("dS = P * (dP - Dr[:, None])", "dS = P * (dP + Dr[:, None])"),
+    "row_correction_from_dP": ("Dr = (P * dP).sum(axis=1)", "Dr = dP.sum(axis=1)"),
+    "dq_without_scale": ("dQ[b, h][rr] = scale64 * (dS @ kh)", "dQ[b, h][rr] = (dS @ kh)"),
+    "dk_without_scale": ("dK[b, h][support] += scale64 * (dS.T @ qh)", "dK[b, h][support] += (dS.T @ qh)"),
+    "dq_with_v": ("dQ[b, h][rr] = scale64 * (dS @ kh)", "dQ[b, h][rr] = scale64 * (dS @ vh)"),
+    "dv_from_dS": ("dV[b, h][support] += P.T @ doh", "dV[b, h][support] += dS.T @ doh"),
+    "unnormalised_P": ("P[attended] = p[attended] / l[attended][:, None]", "P[attended] = p[attended]"),
+    "mask_ignored": ("S = np.where(Ms, S, -np.inf)", "S = S"),
+    "dP_with_k": ("dP = doh @ vh.T", "dP = doh @ kh.T"),
+    "dk_overwritten": ("dK[b, h][support] += scale64", "dK[b, h][support] = scale64"),
+    "dv_overwritten": ("dV[b, h][support] += P.T", "dV[b, h][support] = P.T"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    old, new = BWD_MUTANTS[name]
+    mod = _mutant("backward.py", old, new)
+    assert _caught(test_oracle_bwd.ALL_BWD_PINS, mod.attention_bwd), f"mutant {name} survived every pin"
