@@ -151,6 +151,44 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
                                   int64_t B, int64_t N, int64_t d,
                                   int32_t* work_out, int32_t* order_out);
 
+/*
+ * fm_attn_bwd -- gradients of fm_attn_fwd: given dO = dL/dO, the gradients
+ * dL/dQ, dL/dK, dL/dV.  The pages give the forward only and place the method
+ * in training (FlashMask abstract), which needs them; they follow from the
+ * forward's definition by the chain rule.  With P the masked softmax,
+ * recomputed from the forward's LSE (P_ij = exp(scale q_i.k_j - LSE_i) for
+ * attended keys, 0 otherwise), D_i = sum_c dO_ic O_ic and
+ * dS_ij = P_ij (dO_i . v_j - D_i):
+ *     dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K.
+ * Tiles skipped by the forward's rule are skipped here too (they have P = 0).
+ *
+ *   q, k, v, out, dout : bfloat16 [B][H][N][d] device, contiguous, 16-byte
+ *               aligned; out and lse are fm_attn_fwd's outputs for q, k, v
+ *               and the same intervals and scale.
+ *   lse       : float32 [B][H][N] device.
+ *   col_start, col_end, B, H, N, d, scale : as fm_attn_fwd.
+ *   dq, dk, dv : float32 [B][H][N][d] device, 16-byte aligned, fully written
+ *               (rows no query attends get dk = dv = 0; rows that attend
+ *               nothing get dq = 0).
+ *   stream    : HIP stream the work is queued on.
+ *
+ * Asynchronous on `stream`; deterministic (no atomics: every output element is
+ * written once).  Workspace, argument checks and errors as fm_attn_fwd, whose
+ * internal workspace per (device, stream) it shares (about 4 B per row and head
+ * plus 40 B per query block).  Inputs must not alias the outputs.
+ */
+FM_API int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       const float* lse, const int32_t* col_start, const int32_t* col_end,
+                       int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       float* dq, float* dk, float* dv, hipStream_t stream);
+
+/* fm_attn_bwd for rows with n_ranges ranges ([B][n_ranges][N] intervals, as
+ * fm_attn_fwd_multi). */
+FM_API int fm_attn_bwd_multi(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                             float* dq, float* dk, float* dv, hipStream_t stream);
+
 /* The query and key block sizes the attention kernel uses for head dimension d
  * (the shape at which tiles are skipped).  FM_ERR_UNSUPPORTED for other d. */
 FM_API int fm_attn_tile_shape(int64_t d, int32_t* Br, int32_t* Bc);

@@ -19,8 +19,8 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# The attention kernel and the header whose device helpers it inlines.
-ATTN_SOURCES = [os.path.join(PKG, "csrc", "fm_attn_fwd.hip"), os.path.join(PKG, "csrc", "fm_internal.h")]
+# The attention kernel and the headers whose device helpers it inlines.
+ATTN_SOURCES = [os.path.join(PKG, "csrc", name) for name in ("fm_attn_fwd.hip", "fm_internal.h", "fm_mfma.h")]
 
 
 def attn_source_hash() -> str:

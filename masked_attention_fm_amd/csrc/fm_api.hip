@@ -279,4 +279,76 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
     return fm_attn_fwd_multi(q, k, v, col_start, col_end, 1, B, H, N, d, scale, out, lse, stream);
 }
 
+FM_API int fm_attn_bwd_multi(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, float* dq, float* dk,
+                             float* dv, hipStream_t stream) {
+    // ---- host-side checks, before any HIP call
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+        col_start == nullptr || col_end == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+        return FM_ERR_INVALID_ARG;
+    if (n_ranges < 1 || n_ranges > fm::kMaxRanges) return FM_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || N > kMaxAttnN) return FM_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
+    if (!(scale > 0.f) || !isfinite(scale)) return FM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(col_start, 4) ||
+        !aligned(col_end, 4))
+        return FM_ERR_INVALID_ARG;
+    const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
+    const int64_t n_qc = (N + fm::kBwdRows - 1) / fm::kBwdRows;
+    const int64_t n_kb = (N + fm::kBwdKeys - 1) / fm::kBwdKeys;
+    if (B * H * n_qc >= (int64_t(1) << 31) || B * n_ranges * N >= (int64_t(1) << 40)) return FM_ERR_INVALID_ARG;
+
+    // ---- workspace: meta_q[Mq][n] | work_q | order_q | meta_c[Mc][n] | kvr[Mk] | work_k | order_k | D[B H N]
+    const int64_t Mq = B * n_q, Mc = B * n_qc, Mk = B * n_kb;
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t o_work_q = al((size_t)(Mq * n_ranges) * sizeof(fm::TileMeta));
+    const size_t o_order_q = o_work_q + al((size_t)Mq * 4);
+    const size_t o_meta_c = o_order_q + al((size_t)Mq * 4);
+    const size_t o_kvr = o_meta_c + al((size_t)(Mc * n_ranges) * sizeof(fm::TileMeta));
+    const size_t o_work_k = o_kvr + al((size_t)Mk * sizeof(int4));
+    const size_t o_order_k = o_work_k + al((size_t)Mk * 4);
+    const size_t o_dd = o_order_k + al((size_t)Mk * 4);
+    const size_t total = o_dd + al((size_t)(B * H * N) * sizeof(float));
+    void* ws = nullptr;
+    FM_HIP(get_workspace(stream, total, &ws));
+    char* w = static_cast<char*>(ws);
+    auto* meta_q = reinterpret_cast<fm::TileMeta*>(w);
+    auto* work_q = reinterpret_cast<int32_t*>(w + o_work_q);
+    auto* order_q = reinterpret_cast<int32_t*>(w + o_order_q);
+    auto* meta_c = reinterpret_cast<fm::TileMeta*>(w + o_meta_c);
+    auto* kvr = reinterpret_cast<int4*>(w + o_kvr);
+    auto* work_k = reinterpret_cast<int32_t*>(w + o_work_k);
+    auto* order_k = reinterpret_cast<int32_t*>(w + o_order_k);
+    auto* dd = reinterpret_cast<float*>(w + o_dd);
+
+    FM_HIP(fm::launch_bwd_rowdot(out, dout, B * H * N, d, dd, stream));
+    // dQ: the forward's query blocks, key blocks and longest-first order
+    if (Mq <= fm::kPrepSmallMax) {
+        FM_HIP(fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, order_q,
+                                     stream));
+    } else {
+        FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, nullptr,
+                                     stream));
+        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream));
+    }
+    // dK, dV: query chunks per key block, key blocks longest first
+    FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBwdRows, fm::kBwdKeys, meta_c, nullptr,
+                                 nullptr, stream));
+    FM_HIP(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream));
+    FM_HIP(fm::launch_schedule(work_k, Mk, order_k, stream));
+    FM_HIP(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, kvr, order_k, B, H, N,
+                               d, scale, dk, dv, stream));
+    FM_HIP(fm::launch_bwd_dq(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_q, order_q, B, H, N, d,
+                             scale, dq, stream));
+    return FM_OK;
+}
+
+FM_API int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       const float* lse, const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t H,
+                       int64_t N, int64_t d, float scale, float* dq, float* dk, float* dv, hipStream_t stream) {
+    return fm_attn_bwd_multi(q, k, v, out, dout, lse, col_start, col_end, 1, B, H, N, d, scale, dq, dk, dv, stream);
+}
+
 }  // extern "C"

@@ -1,0 +1,682 @@
+// Gradients of masked attention for gfx950 (MI355X): dQ, dK, dV from the
+// forward's LSE.
+//
+// The pages give the forward pass only; they use the method in training
+// (FlashMask abstract), which needs these gradients.  With P the masked
+// softmax recomputed from the saved LSE (P = exp(scale q.k - LSE), 0 outside
+// the row's ranges), D = rowsum(dO * O) and dS = P (dO V^T - D):
+//   dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K.
+// The tile skipping of the forward carries over unchanged (FlashMask article
+// §2.2, §4.1 items 2-3): a pair of blocks skipped there has P = 0 here and
+// contributes nothing, so it is never loaded; a FULL pair needs no compare.
+//
+// Two kernels, no atomics, deterministic:
+//   * bwd_dkdv_kernel: one workgroup per (b, h, block of kBwdKeys = 128 keys),
+//     4 wavefronts of 32 keys.  A wavefront keeps its K and V rows in registers
+//     as MFMA B operands and walks the query chunks (kBwdRows = 64 rows) whose
+//     non-skip ranges hold its key block: S = Q K^T and dP = dO V^T with Q and
+//     dO read from LDS; then dV^T += dO^T P and dK^T += Q^T dS with P and dS
+//     taken straight from the registers (the vt_pos key order) and Q^T, dO^T
+//     staged transposed in LDS.  A lane ends up holding one key's dK and dV row.
+//   * bwd_dq_kernel: one workgroup per (b, h, query block of kBr = 128 rows),
+//     the forward's structure: S^T = K Q^T and dP^T = V dO^T with Q and dO in
+//     registers, then dQ^T += K^T dS^T, walking the union of the non-skip key
+//     blocks.  A lane ends up holding one query's dQ row.
+// Both double-buffer their operands through LDS (one barrier per step) and
+// run one workgroup per CU (their LDS rings exceed half of the 160 KB).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "fm_internal.h"
+#include "fm_mfma.h"
+
+namespace fm {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPad = 8;                        // bf16 padding per LDS operand row (16 B)
+
+static_assert(kBwdKeys == 32 * kWaves, "one 32-key MFMA column block per wavefront");
+static_assert(kBr == 32 * kWaves, "one 32-row MFMA column block per wavefront");
+static_assert(kBwdRows % 16 == 0 && kBc % 16 == 0, "chunks are whole MFMA contraction steps");
+
+// ---------------------------------------------------------------- D = rowsum(dO * O)
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ O,
+                                                         const uint16_t* __restrict__ dO, int64_t rows,
+                                                         float* __restrict__ dd) {
+    constexpr int kLanes = D / 8;              // lanes per row, 8 columns each
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kLanes;
+    const int c8 = threadIdx.x % kLanes;
+    float acc = 0.f;
+    if (row < rows) {
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + row * D + c8 * 8);
+        const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + row * D + c8 * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+    }
+#pragma unroll
+    for (int off = kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && c8 == 0) dd[row] = acc;
+}
+
+// ---------------------------------------------------------------- query chunks per key block
+
+// One wavefront per (b, J): lanes scan the query chunks t = lane, lane + 64, ...
+template <int NIV>
+__global__ __launch_bounds__(256) void kv_ranges_kernel(const TileMeta* __restrict__ meta_c, int n_qc, int n_kb,
+                                                        int64_t items, int4* __restrict__ kvr,
+                                                        int32_t* __restrict__ work) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= items) return;                 // whole wavefront leaves together
+    const int64_t b = item / n_kb;
+    const int J = (int)(item - b * n_kb);
+    int lo = INT_MAX, hi = INT_MIN, count = 0;
+    for (int t = lane; t < n_qc; t += 64) {
+        bool live = false;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            const TileMeta m = meta_c[((int64_t)b * n_qc + t) * NIV + k];
+            live |= m.x <= J && J <= m.y;
+        }
+        if (live) {
+            lo = min(lo, t);
+            hi = max(hi, t);
+            ++count;
+        }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    count = wave_sum(count);
+    if (lane == 0) {
+        kvr[item] = make_int4(count > 0 ? lo : 0, count > 0 ? hi : -1, count, 0);
+        work[item] = count;
+    }
+}
+
+// Launch slot -> (head, work item): the forward's XCD-local head order.
+__device__ __forceinline__ void slot_to_item(int xcd_heads, int H, int& h, int& item) {
+    if (xcd_heads) {
+        const int s = blockIdx.x >> 3;
+        const int M = gridDim.x / H;
+        h = (blockIdx.x & 7) + 8 * (s / M);
+        item = s % M;
+    } else {
+        h = blockIdx.x % H;
+        item = blockIdx.x / H;
+    }
+}
+
+// Staged interval of one row of one range, clamped to [0, N): start, width.
+__device__ __forceinline__ int2 clamp_interval(int s_raw, int e_raw, int N) {
+    const int sc = max(s_raw, 0);
+    const int ec = min(e_raw, N - 1);
+    return sc <= ec ? make_int2(sc, ec - sc) : make_int2(kEmptyStart, 0);
+}
+
+// Bounds of one wavefront's rows for one range (rows past N are neutral; a
+// row with no key in the range rules out FULL): {min_s, max_e, max_s, min_e}.
+__device__ __forceinline__ int4 wave_row_bounds(int s, int w, bool in_seq) {
+    const bool any = s != kEmptyStart;
+    return make_int4(wave_min(any ? s : INT_MAX), wave_max(any ? s + w : INT_MIN),
+                     wave_max(any ? s : (in_seq ? INT_MAX : INT_MIN)),
+                     wave_min(any ? s + w : (in_seq ? INT_MIN : INT_MAX)));
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int D, int NIV>
+struct alignas(16) DkvSmem {
+    alignas(16) uint16_t q[2][kBwdRows][D + kPad];      // Q chunk, row-major
+    alignas(16) uint16_t qt[2][D][kBwdRows + kPad];     // Q chunk, transposed, rows in vt_pos order
+    alignas(16) uint16_t go[2][kBwdRows][D + kPad];     // dO chunk, row-major
+    alignas(16) uint16_t got[2][D][kBwdRows + kPad];    // dO chunk, transposed, rows in vt_pos order
+    alignas(16) float lse2[2][kBwdRows];                // LSE * log2 e (+inf past N)
+    alignas(16) float dd[2][kBwdRows];                  // D (0 past N)
+    alignas(16) int start[2][NIV][kBwdRows];
+    alignas(16) int width[2][NIV][kBwdRows];
+};
+
+template <int D, int NIV>
+struct DkvStage {
+    static constexpr int kItems = (kBwdRows / 4) * (D / 8);    // 4 rows x 8 columns per item
+    static_assert(kItems <= kThreads, "one item per thread at most");
+    u32x4 q[4];
+    u32x4 go[4];
+    float lse2, dd;
+    int s[NIV], w[NIV];
+};
+
+template <int D, int NIV>
+__device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, __amdgpu_buffer_rsrc_t qrs,
+                                         __amdgpu_buffer_rsrc_t grs, const float* __restrict__ lse_bh,
+                                         const float* __restrict__ dd_bh, const int32_t* __restrict__ cs_b,
+                                         const int32_t* __restrict__ ce_b, int row0, int N, int tid) {
+    if (DkvStage<D, NIV>::kItems == kThreads || tid < DkvStage<D, NIV>::kItems) {
+        const int r0 = 4 * (tid % (kBwdRows / 4));
+        const int n0 = 8 * (tid / (kBwdRows / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int off = ((row0 + r0 + r) * D + n0) * 2;
+            st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+            st.go[r] = __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0);
+        }
+    }
+    if (tid < kBwdRows) {
+        const int row = row0 + tid;
+        if (row < N) {
+            st.lse2 = lse_bh[row] * kLog2e;
+            st.dd = dd_bh[row];
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                const int2 iv = clamp_interval(cs_b[(int64_t)k * N + row], ce_b[(int64_t)k * N + row], N);
+                st.s[k] = iv.x;
+                st.w[k] = iv.y;
+            }
+        } else {
+            st.lse2 = INFINITY;                // P = 0 for rows past N
+            st.dd = 0.f;
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                st.s[k] = kEmptyStart;
+                st.w[k] = 0;
+            }
+        }
+    }
+}
+
+template <int D, int NIV>
+__device__ __forceinline__ void dkv_store(const DkvStage<D, NIV>& st, DkvSmem<D, NIV>& sm, int buf, int tid) {
+    if (DkvStage<D, NIV>::kItems == kThreads || tid < DkvStage<D, NIV>::kItems) {
+        const int r0 = 4 * (tid % (kBwdRows / 4));
+        const int n0 = 8 * (tid / (kBwdRows / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<u32x4*>(&sm.q[buf][r0 + r][n0]) = st.q[r];
+            *reinterpret_cast<u32x4*>(&sm.go[buf][r0 + r][n0]) = st.go[r];
+        }
+        store_transposed_4x8(st.q, &sm.qt[buf][0][0], kBwdRows + kPad, n0, vt_pos(r0));
+        store_transposed_4x8(st.go, &sm.got[buf][0][0], kBwdRows + kPad, n0, vt_pos(r0));
+    }
+    if (tid < kBwdRows) {
+        sm.lse2[buf][tid] = st.lse2;
+        sm.dd[buf][tid] = st.dd;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            sm.start[buf][k][tid] = st.s[k];
+            sm.width[buf][k][tid] = st.w[k];
+        }
+    }
+}
+
+template <int NIV>
+__device__ __forceinline__ bool chunk_live(const TileMeta* __restrict__ meta_c, int64_t base, int J) {
+    bool live = false;
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) {
+        const TileMeta m = meta_c[base * NIV + k];
+        live |= m.x <= J && J <= m.y;
+    }
+    return live;
+}
+
+template <int D, int NIV>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
+    const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
+    const TileMeta* __restrict__ meta_c, const int4* __restrict__ kvr, const int32_t* __restrict__ order, int H,
+    int N, int n_qc, int n_kb, float c, float scale, int xcd_heads, float* __restrict__ dK,
+    float* __restrict__ dV) {
+    __shared__ DkvSmem<D, NIV> sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+
+    int h, slot;
+    slot_to_item(xcd_heads, H, h, slot);
+    const int bj = order[slot];
+    const int b = bj / n_kb;
+    const int J = bj - b * n_kb;
+    const int4 range = kvr[bj];                 // {first chunk, last chunk, live chunks}
+
+    const int64_t bh = (int64_t)b * H + h;
+    const int key = J * kBwdKeys + wave * 32 + r32;     // this lane's key
+    const int kw0 = J * kBwdKeys + wave * 32;           // the wavefront's first key
+
+    // K and V rows of this lane's key as MFMA B operands: [key][16 cs + 8 half .. +7].
+    bf16x8 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+    for (int cs = 0; cs < D / 16; ++cs) {
+        if (key < N) {
+            kreg[cs] = *reinterpret_cast<const bf16x8*>(K + (bh * N + key) * D + cs * 16 + half * 8);
+            vreg[cs] = *reinterpret_cast<const bf16x8*>(V + (bh * N + key) * D + cs * 16 + half * 8);
+        } else {
+            kreg[cs] = bf16x8{};
+            vreg[cs] = bf16x8{};
+        }
+    }
+    floatx16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+        dkacc[nb] = floatx16{};
+        dvacc[nb] = floatx16{};
+    }
+
+    const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(Q + bh * N * D, N * D * 2);
+    const __amdgpu_buffer_rsrc_t grs = slice_rsrc(dO + bh * N * D, N * D * 2);
+    const float* lse_bh = LSE + bh * N;
+    const float* dd_bh = Dd + bh * N;
+    const int32_t* cs_b = col_start + (int64_t)b * NIV * N;
+    const int32_t* ce_b = col_end + (int64_t)b * NIV * N;
+    const int64_t meta_row = (int64_t)b * n_qc;
+
+    int t = range.z > 0 ? range.x : INT_MAX;
+    if (t != INT_MAX) {
+        DkvStage<D, NIV> stage;
+        dkv_load<D, NIV>(stage, qrs, grs, lse_bh, dd_bh, cs_b, ce_b, t * kBwdRows, N, tid);
+        dkv_store<D, NIV>(stage, sm, 0, tid);
+        __syncthreads();
+        for (int buf = 0;; buf ^= 1) {
+            int t_next = t + 1;
+            while (t_next <= range.y && !chunk_live<NIV>(meta_c, meta_row + t_next, J)) ++t_next;
+            const bool has_next = t_next <= range.y;
+            if (has_next)
+                dkv_load<D, NIV>(stage, qrs, grs, lse_bh, dd_bh, cs_b, ce_b, t_next * kBwdRows, N, tid);
+
+            // Does some row of the chunk attend the wavefront's keys, and does
+            // one range cover them for every row?  Lane l looks at row l.
+            const int row0 = t * kBwdRows;
+            const int klo = kw0;
+            const int khi = min(kw0 + 31, N - 1);
+            bool wave_skip = true, wave_full = false;
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                const int4 rb = wave_row_bounds(sm.start[buf][k][lane], sm.width[buf][k][lane], row0 + lane < N);
+                wave_skip &= khi < rb.x || klo > rb.y;
+                wave_full |= klo >= rb.z && khi <= rb.w;
+            }
+            wave_skip |= klo >= N;               // every key of the wavefront lies past N
+            if (!wave_skip) {
+                // ---- S = Q K^T, dP = dO V^T: lane holds [query 32 qb + 8 (v/4) + 4 half + v%4][key]
+                floatx16 s[kBwdRows / 32], dp[kBwdRows / 32];
+#pragma unroll
+                for (int qb = 0; qb < kBwdRows / 32; ++qb) {
+                    s[qb] = floatx16{};
+                    dp[qb] = floatx16{};
+                }
+#pragma unroll
+                for (int cs = 0; cs < D / 16; ++cs) {
+#pragma unroll
+                    for (int qb = 0; qb < kBwdRows / 32; ++qb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.q[buf][qb * 32 + r32][cs * 16 + half * 8]);
+                        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[cs], s[qb], 0, 0, 0);
+                        const bf16x8 g = *reinterpret_cast<const bf16x8*>(&sm.go[buf][qb * 32 + r32][cs * 16 + half * 8]);
+                        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, vreg[cs], dp[qb], 0, 0, 0);
+                    }
+                }
+                // ---- P = exp(scale s - LSE) inside the ranges, dS = P (dP - D)
+#pragma unroll
+                for (int qb = 0; qb < kBwdRows / 32; ++qb) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int qi = qb * 32 + 8 * g + 4 * half;     // four consecutive queries
+                        const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[buf][qi]);
+                        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[buf][qi]);
+                        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+                        bool ok[4] = {true, true, true, true};
+                        if (!wave_full) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) ok[q] = false;
+#pragma unroll
+                            for (int k = 0; k < NIV; ++k) {
+                                const int4 s4 = *reinterpret_cast<const int4*>(&sm.start[buf][k][qi]);
+                                const int4 w4 = *reinterpret_cast<const int4*>(&sm.width[buf][k][qi]);
+                                ok[0] |= (uint32_t)(key - s4.x) <= (uint32_t)w4.x;
+                                ok[1] |= (uint32_t)(key - s4.y) <= (uint32_t)w4.y;
+                                ok[2] |= (uint32_t)(key - s4.z) <= (uint32_t)w4.z;
+                                ok[3] |= (uint32_t)(key - s4.w) <= (uint32_t)w4.w;
+                            }
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int v = 4 * g + q;
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][v], c, -lv[q]));
+                            const float pm = ok[q] ? p : 0.f;
+                            s[qb][v] = pm;
+                            dp[qb][v] = pm * (dp[qb][v] - dv4[q]);
+                        }
+                    }
+                }
+                // ---- dV^T += dO^T P, dK^T += Q^T dS (contraction over the chunk's queries)
+#pragma unroll
+                for (int ks = 0; ks < kBwdRows / 16; ++ks) {
+                    bf16x8 pb, sb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pb[e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
+                        sb[e] = (__bf16)dp[ks >> 1][8 * (ks & 1) + e];
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < D / 32; ++nb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.got[buf][nb * 32 + r32][16 * ks + 8 * half]);
+                        dvacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, dvacc[nb], 0, 0, 0);
+                        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.qt[buf][nb * 32 + r32][16 * ks + 8 * half]);
+                        dkacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, dkacc[nb], 0, 0, 0);
+                    }
+                }
+            }
+            if (has_next) dkv_store<D, NIV>(stage, sm, buf ^ 1, tid);
+            __syncthreads();
+            if (!has_next) break;
+            t = t_next;
+        }
+    }
+
+    // ---- epilogue: lane holds dK, dV of its key at d = 32 nb + 8 g + 4 half + (0..3).
+    if (key < N) {
+        float* dk_row = dK + (bh * N + key) * D;
+        float* dv_row = dV + (bh * N + key) * D;
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = nb * 32 + 8 * g + 4 * half;
+                *reinterpret_cast<float4*>(dk_row + col) =
+                    make_float4(scale * dkacc[nb][4 * g], scale * dkacc[nb][4 * g + 1], scale * dkacc[nb][4 * g + 2],
+                                scale * dkacc[nb][4 * g + 3]);
+                *reinterpret_cast<float4*>(dv_row + col) =
+                    make_float4(dvacc[nb][4 * g], dvacc[nb][4 * g + 1], dvacc[nb][4 * g + 2], dvacc[nb][4 * g + 3]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D, int NIV>
+struct alignas(16) DqSmem {
+    alignas(16) uint16_t k[2][kBc][D + kPad];       // K block, row-major
+    alignas(16) uint16_t v[2][kBc][D + kPad];       // V block, row-major
+    alignas(16) uint16_t kt[2][D][kBc + kPad];      // K block, transposed, keys in vt_pos order
+    int start[NIV][kBr];
+    int width[NIV][kBr];
+};
+
+template <int D>
+struct DqStage {
+    static constexpr int kItems = (kBc / 4) * (D / 8);   // 4 keys x 8 columns per item
+    static_assert(kItems <= kThreads, "one item per thread at most");
+    u32x4 k[4];
+    u32x4 v[4];
+};
+
+template <int D>
+__device__ __forceinline__ void dq_load(DqStage<D>& st, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                        int kv0, int tid) {
+    if (DqStage<D>::kItems == kThreads || tid < DqStage<D>::kItems) {
+        const int j0 = 4 * (tid % (kBc / 4));
+        const int n0 = 8 * (tid / (kBc / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int off = ((kv0 + j0 + r) * D + n0) * 2;
+            st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+            st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+        }
+    }
+}
+
+template <int D, int NIV>
+__device__ __forceinline__ void dq_store(const DqStage<D>& st, DqSmem<D, NIV>& sm, int buf, int tid) {
+    if (DqStage<D>::kItems == kThreads || tid < DqStage<D>::kItems) {
+        const int j0 = 4 * (tid % (kBc / 4));
+        const int n0 = 8 * (tid / (kBc / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<u32x4*>(&sm.k[buf][j0 + r][n0]) = st.k[r];
+            *reinterpret_cast<u32x4*>(&sm.v[buf][j0 + r][n0]) = st.v[r];
+        }
+        store_transposed_4x8(st.k, &sm.kt[buf][0][0], kBc + kPad, n0, vt_pos(j0));
+    }
+}
+
+template <int D, int NIV>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
+    const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, const TileMeta* __restrict__ meta,
+    const int32_t* __restrict__ order, int H, int N, int n_q, float c, float scale, int xcd_heads,
+    float* __restrict__ dQ) {
+    __shared__ DqSmem<D, NIV> sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+
+    int h, slot;
+    slot_to_item(xcd_heads, H, h, slot);
+    const int bt = order != nullptr ? order[slot] : slot;
+    const int b = bt / n_q;
+    const int t = bt - b * n_q;
+    TileMeta tm[NIV];
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) tm[k] = meta[(int64_t)bt * NIV + k];
+
+    const int64_t bh = (int64_t)b * H + h;
+    const int row0 = t * kBr;
+    const int qrow = row0 + wave * 32 + r32;
+
+    if (tid < kBr) {
+        const int r = row0 + tid;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            int2 iv = make_int2(kEmptyStart, 0);
+            if (r < N) {
+                const int64_t at = ((int64_t)b * NIV + k) * N + r;
+                iv = clamp_interval(col_start[at], col_end[at], N);
+            }
+            sm.start[k][tid] = iv.x;
+            sm.width[k][tid] = iv.y;
+        }
+    }
+
+    // Q and dO rows of this lane's query as MFMA B operands.
+    bf16x8 qreg[D / 16], greg[D / 16];
+#pragma unroll
+    for (int cs = 0; cs < D / 16; ++cs) {
+        if (qrow < N) {
+            qreg[cs] = *reinterpret_cast<const bf16x8*>(Q + (bh * N + qrow) * D + cs * 16 + half * 8);
+            greg[cs] = *reinterpret_cast<const bf16x8*>(dO + (bh * N + qrow) * D + cs * 16 + half * 8);
+        } else {
+            qreg[cs] = bf16x8{};
+            greg[cs] = bf16x8{};
+        }
+    }
+    const float lse2 = qrow < N ? LSE[bh * N + qrow] * kLog2e : INFINITY;   // P = 0 past N
+    const float drow = qrow < N ? Dd[bh * N + qrow] : 0.f;
+
+    floatx16 dqacc[D / 32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) dqacc[nb] = floatx16{};
+
+    __syncthreads();
+    int my_s[NIV], my_w[NIV];
+    int4 wb[NIV];
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) {
+        my_s[k] = sm.start[k][wave * 32 + r32];
+        my_w[k] = sm.width[k][wave * 32 + r32];
+        wb[k] = wave_row_bounds(my_s[k], my_w[k], qrow < N);
+    }
+
+    const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + bh * N * D, N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + bh * N * D, N * D * 2);
+
+    int j = union_next<NIV>(tm, -1);
+    if (j != INT_MAX) {
+        DqStage<D> stage;
+        dq_load<D>(stage, krs, vrs, j * kBc, tid);
+        dq_store<D, NIV>(stage, sm, 0, tid);
+        __syncthreads();
+        for (int buf = 0;; buf ^= 1) {
+            const int j_next = union_next<NIV>(tm, j);
+            const bool has_next = j_next != INT_MAX;
+            if (has_next) dq_load<D>(stage, krs, vrs, j_next * kBc, tid);
+
+            const int klo = j * kBc;
+            const int khi = min(klo + kBc, N) - 1;
+            bool wave_skip = true, wave_full = false;
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                wave_skip &= khi < wb[k].x || klo > wb[k].y;
+                wave_full |= klo >= wb[k].z && khi <= wb[k].w;
+            }
+            wave_full &= klo + kBc <= N;         // keys past N are always masked
+            if (!wave_skip) {
+                // ---- S^T = K Q^T, dP^T = V dO^T: lane holds [key 32 jb + 8 (v/4) + 4 half + v%4][query]
+                floatx16 st[kBc / 32], dpt[kBc / 32];
+#pragma unroll
+                for (int jb = 0; jb < kBc / 32; ++jb) {
+                    st[jb] = floatx16{};
+                    dpt[jb] = floatx16{};
+                }
+#pragma unroll
+                for (int cs = 0; cs < D / 16; ++cs) {
+#pragma unroll
+                    for (int jb = 0; jb < kBc / 32; ++jb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][jb * 32 + r32][cs * 16 + half * 8]);
+                        st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
+                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&sm.v[buf][jb * 32 + r32][cs * 16 + half * 8]);
+                        dpt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, greg[cs], dpt[jb], 0, 0, 0);
+                    }
+                }
+                // ---- dS^T = P^T (dP^T - D) with P = exp(scale s - LSE) inside the ranges
+                int base[NIV];
+#pragma unroll
+                for (int k = 0; k < NIV; ++k) base[k] = klo + 4 * half - my_s[k];
+#pragma unroll
+                for (int jb = 0; jb < kBc / 32; ++jb) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        bool ok = true;
+                        if (!wave_full) {
+                            const int off = jb * 32 + 8 * (v >> 2) + (v & 3);
+                            ok = false;
+#pragma unroll
+                            for (int k = 0; k < NIV; ++k) ok |= (uint32_t)(base[k] + off) <= (uint32_t)my_w[k];
+                        }
+                        const float p = __builtin_amdgcn_exp2f(fmaf(st[jb][v], c, -lse2));
+                        const float pm = ok ? p : 0.f;
+                        dpt[jb][v] = pm * (dpt[jb][v] - drow);
+                    }
+                }
+                // ---- dQ^T += K^T dS^T
+#pragma unroll
+                for (int ks = 0; ks < kBc / 16; ++ks) {
+                    bf16x8 sb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sb[e] = (__bf16)dpt[ks >> 1][8 * (ks & 1) + e];
+#pragma unroll
+                    for (int nb = 0; nb < D / 32; ++nb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.kt[buf][nb * 32 + r32][16 * ks + 8 * half]);
+                        dqacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dqacc[nb], 0, 0, 0);
+                    }
+                }
+            }
+            if (has_next) dq_store<D, NIV>(stage, sm, buf ^ 1, tid);
+            __syncthreads();
+            if (!has_next) break;
+            j = j_next;
+        }
+    }
+
+    // ---- epilogue: lane holds dQ of its query at d = 32 nb + 8 g + 4 half + (0..3).
+    if (qrow < N) {
+        float* dq_row = dQ + (bh * N + qrow) * D;
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                *reinterpret_cast<float4*>(dq_row + nb * 32 + 8 * g + 4 * half) =
+                    make_float4(scale * dqacc[nb][4 * g], scale * dqacc[nb][4 * g + 1], scale * dqacc[nb][4 * g + 2],
+                                scale * dqacc[nb][4 * g + 3]);
+            }
+        }
+    }
+}
+
+int use_xcd_heads(int64_t H, int64_t items_per_head) { return (H % 8 == 0 && items_per_head >= 128) ? 1 : 0; }
+
+}  // namespace
+
+hipError_t launch_bwd_rowdot(const void* out, const void* dout, int64_t rows, int64_t d, float* dd,
+                             hipStream_t stream) {
+    const int64_t threads = rows * (d / 8);
+    const int64_t blocks = (threads + 255) / 256;
+    auto kernel = d == 128 ? bwd_rowdot_kernel<128> : bwd_rowdot_kernel<64>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(out),
+                       static_cast<const uint16_t*>(dout), rows, dd);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_ranges(const TileMeta* meta_c, int n_iv, int64_t B, int64_t N, int4* kvr, int32_t* work,
+                            hipStream_t stream) {
+    const int64_t n_qc = (N + kBwdRows - 1) / kBwdRows;
+    const int64_t n_kb = (N + kBwdKeys - 1) / kBwdKeys;
+    const int64_t items = B * n_kb;
+    const int64_t blocks = (items + 3) / 4;
+    return dispatch_ranges(n_iv, [&](auto niv) {
+        hipLaunchKernelGGL(kv_ranges_kernel<decltype(niv)::value>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           meta_c, (int)n_qc, (int)n_kb, items, kvr, work);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
+                           const TileMeta* meta_c, const int4* kvr, const int32_t* order, int64_t B, int64_t H,
+                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream) {
+    const int64_t n_qc = (N + kBwdRows - 1) / kBwdRows;
+    const int64_t n_kb = (N + kBwdKeys - 1) / kBwdKeys;
+    const int64_t grid = B * H * n_kb;
+    const int xcd = use_xcd_heads(H, B * n_kb);
+    const float c = scale * kLog2e;
+    return dispatch_ranges(n_iv, [&](auto niv) {
+        constexpr int NIV = decltype(niv)::value;
+        auto kernel = d == 128 ? bwd_dkdv_kernel<128, NIV> : bwd_dkdv_kernel<64, NIV>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), lse, dd, col_start,
+                           col_end, meta_c, kvr, order, (int)H, (int)N, (int)n_qc, (int)n_kb, c, scale, xcd, dk, dv);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                         const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
+                         const TileMeta* meta, const int32_t* order, int64_t B, int64_t H, int64_t N, int64_t d,
+                         float scale, float* dq, hipStream_t stream) {
+    const int64_t n_q = (N + kBr - 1) / kBr;
+    const int64_t grid = B * H * n_q;
+    const int xcd = use_xcd_heads(H, B * n_q);
+    const float c = scale * kLog2e;
+    return dispatch_ranges(n_iv, [&](auto niv) {
+        constexpr int NIV = decltype(niv)::value;
+        auto kernel = d == 128 ? bwd_dq_kernel<128, NIV> : bwd_dq_kernel<64, NIV>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), lse, dd, col_start,
+                           col_end, meta, order, (int)H, (int)N, (int)n_q, c, scale, xcd, dq);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace fm

@@ -43,46 +43,19 @@
 #include <math.h>
 
 #include "fm_internal.h"
+#include "fm_mfma.h"
 
 namespace fm {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = kBr / kWaves;     // 32
 constexpr int kKPad = 8;                       // bf16 padding per K row in LDS (16 B)
 constexpr int kVPad = 8;                       // bf16 padding per V^T row in LDS (16 B)
-constexpr int kEmptyStart = -(1 << 30);        // start of a row that attends nothing
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 static_assert(kRowsPerWave == 32, "one 32x32 MFMA column block per wavefront");
 static_assert(kBc % 32 == 0 && kBc % 16 == 0, "key block is a multiple of the MFMA shapes");
-
-// Position of key j (within a key block) in a V^T row of LDS.  The PV product
-// consumes, in contraction step ks and half-wave h, keys 16ks + 8a + 4h + q
-// (a = 0,1; q = 0..3) -- the keys that half-wave holds in its S^T registers.
-// Swapping bits 2 and 3 of j makes those eight keys contiguous.
-__device__ __forceinline__ int vt_pos(int j) {
-    return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-}
-
-// Combine a value with the one held by the other 32-lane half (lane l ^ 32).
-__device__ __forceinline__ float halves_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // acc + the sum of eight bf16 values, two per v_dot2 against (1, 1).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 p, bf16x2 ones, float acc) {
@@ -113,15 +86,6 @@ struct Staging {
     u32x4 k[kChunksK];
     u32x4 v[4];
 };
-
-// Buffer descriptor over one (b, h) slice of K or V: 32-bit byte offsets from
-// a scalar base, and the hardware returns zeros for any offset at or past
-// num_records, so rows past N need no clamp or branch.
-constexpr uint32_t kRawBufferFlags = 0x00020000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint16_t* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, kRawBufferFlags);
-}
 
 // Loads key block [kv0, kv0 + kBc) into registers.  Rows past N read as zero:
 // their scores are always masked (a block that reaches past N is never
@@ -158,17 +122,8 @@ __device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D, NIV>& 
     if (Staging<D>::kItemsV == kThreads || tid < Staging<D>::kItemsV) {
         const int j0 = 4 * (tid % (kBc / 4));
         const int n0 = 8 * (tid / (kBc / 4));
-        const int p = vt_pos(j0);
-        // 4 keys x 8 columns -> 8 columns x 4 keys (bf16 pairs regrouped).
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t a0 = st.v[0][w], a1 = st.v[1][w], a2 = st.v[2][w], a3 = st.v[3][w];
-            // v_perm_b32 byte selects: low halves (even column) / high halves (odd column)
-            const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-            const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-            *reinterpret_cast<u32x2*>(&sm.vt[buf][n0 + 2 * w][p]) = even;
-            *reinterpret_cast<u32x2*>(&sm.vt[buf][n0 + 2 * w + 1][p]) = odd;
-        }
+        // 4 keys x 8 columns -> 8 columns x 4 keys
+        store_transposed_4x8(st.v, &sm.vt[buf][0][0], kBc + kVPad, n0, vt_pos(j0));
     }
 }
 

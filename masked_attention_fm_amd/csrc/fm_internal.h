@@ -62,6 +62,33 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+// Backward pass (gradients of Q, K, V).  Shapes: the key-block kernel runs
+// kBwdKeys keys per workgroup against query chunks of kBwdRows rows; the
+// query-block kernel uses the forward's (kBr, kBc).
+constexpr int kBwdRows = 64;
+constexpr int kBwdKeys = 128;
+
+// D[bh][i] = sum_c dO[bh][i][c] * O[bh][i][c] (fp32) for B*H*N rows.
+hipError_t launch_bwd_rowdot(const void* out, const void* dout, int64_t rows, int64_t d, float* dd,
+                             hipStream_t stream);
+
+// For each (b, key block J of kBwdKeys keys): the first and last query chunk
+// (kBwdRows rows, records meta_c from launch_preprocess with that shape) whose
+// non-skip ranges hold J, and their count: kvr[b*n_kb + J] = {t_lo, t_hi, count, 0},
+// work[b*n_kb + J] = count.
+hipError_t launch_kv_ranges(const TileMeta* meta_c, int n_iv, int64_t B, int64_t N, int4* kvr, int32_t* work,
+                            hipStream_t stream);
+
+// The two gradient kernels (see fm_attn_bwd.hip).
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
+                           const TileMeta* meta_c, const int4* kvr, const int32_t* order, int64_t B, int64_t H,
+                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                         const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
+                         const TileMeta* meta, const int32_t* order, int64_t B, int64_t H, int64_t N, int64_t d,
+                         float scale, float* dq, hipStream_t stream);
+
 // ---------------------------------------------------------------- wavefront helpers
 
 // Butterfly exchange inside each 32-lane half with ds_swizzle (bit-mask mode:
@@ -79,6 +106,15 @@ __device__ __forceinline__ int wave_min(int v) {
     v = min(v, swizzle_xor<8>(v));
     v = min(v, swizzle_xor<16>(v));
     return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+    v += swizzle_xor<1>(v);
+    v += swizzle_xor<2>(v);
+    v += swizzle_xor<4>(v);
+    v += swizzle_xor<8>(v);
+    v += swizzle_xor<16>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 32);
 }
 
 __device__ __forceinline__ int wave_max(int v) {

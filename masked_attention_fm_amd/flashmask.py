@@ -34,6 +34,10 @@ SIGNATURES = {
     "fm_attn_fwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
                                          _P, _P, _P]),
     "fm_classify_tiles_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P]),
+    "fm_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                   _P, _P, _P, _P]),
+    "fm_attn_bwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64,
+                                         ctypes.c_float, _P, _P, _P, _P]),
     "fm_tile_schedule_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P]),
     "fm_set_option": (ctypes.c_int, [ctypes.c_int, _I64]),
     "fm_profile_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -239,6 +243,64 @@ def fm_attn_fwd_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_sta
     _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
     return _attn("fm_attn_fwd_multi", q, k, v, col_start, col_end, col_start.shape[1], scale, out, lse,
                  stream)
+
+
+def _bwd(func: str, q, k, v, out, dout, lse, col_start, col_end, n_ranges: Optional[int], scale,
+         dq, dk, dv, stream):
+    B, H, N, d = _qkv(q, k, v)
+    for name, x in (("out", out), ("dout", dout)):
+        _dev_tensor(x, name, torch.bfloat16)
+        if x.shape != q.shape:
+            raise ValueError(f"{name} must match q's shape")
+    _dev_tensor(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    grads = []
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if g is None:
+            g = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        else:
+            _dev_tensor(g, name, torch.float32)
+            if g.shape != q.shape:
+                raise ValueError(f"{name} must match q's shape")
+        grads.append(g)
+    dq, dk, dv = grads
+    L = lib()
+    ptrs = [x.data_ptr() for x in (q, k, v, out, dout, lse, col_start, col_end)]
+    if n_ranges is None:
+        status = L.fm_attn_bwd(*ptrs, B, H, N, d, float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               _stream_handle(stream))
+    else:
+        status = L.fm_attn_bwd_multi(*ptrs, n_ranges, B, H, N, d, float(scale), dq.data_ptr(), dk.data_ptr(),
+                                     dv.data_ptr(), _stream_handle(stream))
+    _check(func, status)
+    return dq, dk, dv
+
+
+def fm_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                lse: torch.Tensor, col_start: torch.Tensor, col_end: torch.Tensor, scale: Optional[float] = None,
+                dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                dv: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) float32 [B,H,N,d] of fm_attn_fwd for upstream dout; intervals [B, N].
+    Asynchronous."""
+    B, H, N, d = _qkv(q, k, v)
+    _intervals(col_start, col_end, (B, N), "[B, N]")
+    return _bwd("fm_attn_bwd", q, k, v, out, dout, lse, col_start, col_end, None, scale, dq, dk, dv, stream)
+
+
+def fm_attn_bwd_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                      lse: torch.Tensor, col_start: torch.Tensor, col_end: torch.Tensor,
+                      scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+                      dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None, stream=None):
+    """fm_attn_bwd for intervals [B, K, N]."""
+    B, H, N, d = _qkv(q, k, v)
+    if col_start.dim() != 3:
+        raise ValueError("col_start / col_end must be [B, K, N]")
+    _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
+    return _bwd("fm_attn_bwd_multi", q, k, v, out, dout, lse, col_start, col_end, col_start.shape[1], scale,
+                dq, dk, dv, stream)
 
 
 def fm_set_option(option: int, value: int) -> None:

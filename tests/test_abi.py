@@ -170,3 +170,38 @@ def test_binding_multi_checks_shapes(L):
     s = torch.zeros(1, 8, dtype=torch.int32)
     with pytest.raises(ValueError):
         fmb.fm_attn_fwd_multi(x, x, x, s, s)
+
+
+def bwd(L, n_ranges=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, do=FAKE, lse=FAKE, cs=FAKE, ce=FAKE, B=1, H=1, N=128, d=128,
+             scale=0.125, dq=FAKE, dk=FAKE, dv=FAKE)
+    a.update(kw)
+    head = [a["q"], a["k"], a["v"], a["out"], a["do"], a["lse"], a["cs"], a["ce"]]
+    tail = [a["B"], a["H"], a["N"], a["d"], a["scale"], a["dq"], a["dk"], a["dv"], None]
+    if n_ranges is None:
+        return L.fm_attn_bwd(*head, *tail)
+    return L.fm_attn_bwd_multi(*head, n_ranges, *tail)
+
+
+@pytest.mark.parametrize("n_ranges", [None, 2])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(out=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(do=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(lse=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(dk=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(dv=FAKE + 4), fmb.FM_ERR_INVALID_ARG),
+    (dict(do=FAKE + 2), fmb.FM_ERR_INVALID_ARG),
+    (dict(N=0), fmb.FM_ERR_INVALID_ARG),
+    (dict(N=(1 << 22) + 1), fmb.FM_ERR_INVALID_ARG),
+    (dict(d=32), fmb.FM_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fmb.FM_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fmb.FM_ERR_INVALID_ARG),
+])
+def test_attn_bwd_rejects_bad_arguments(L, n_ranges, kw, status):
+    assert bwd(L, n_ranges, **kw) == status
+
+
+def test_attn_bwd_multi_rejects_bad_range_count(L):
+    assert bwd(L, 0) == fmb.FM_ERR_INVALID_ARG
+    assert bwd(L, fmb.FM_MAX_RANGES + 1) == fmb.FM_ERR_INVALID_ARG

@@ -1,0 +1,147 @@
+"""GPU parity of the backward pass (dQ, dK, dV through the C ABI) against the
+float64 oracle's gradients, on the forward's own outputs (O, LSE)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from masked_attention_fm_amd import flashmask as fm
+from masked_attention_fm_amd import inputs
+
+from test_gpu_parity import DEV, log, small_intervals, to_dev
+from test_gpu_multi import multi_intervals
+
+pytestmark = pytest.mark.gpu
+
+# max |G - G_ref| <= GRAD_TOL * max(1, max |G_ref|) for each of dQ, dK, dV
+GRAD_TOL = 2e-2
+
+
+def dout_for(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def run_bwd(q, k, v, do, s, e, scale, multi):
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    sd, ed = to_dev(s, e)
+    fwd = fm.fm_attn_fwd_multi if multi else fm.fm_attn_fwd
+    out, lse = fwd(qd, kd, vd, sd, ed, scale)
+    grads = [torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV) for _ in range(3)]
+    bwd = fm.fm_attn_bwd_multi if multi else fm.fm_attn_bwd
+    bwd(qd, kd, vd, out, dod, lse, sd, ed, scale, dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    return [g.cpu().numpy().astype(np.float64) for g in grads]
+
+
+def compare_grads(got, ref, what):
+    worst = 0.0
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.isfinite(g).all(), f"{what}: non-finite {name}"
+        err = float(np.abs(g - r).max()) if r.size else 0.0
+        scale = max(1.0, float(np.abs(r).max()) if r.size else 0.0)
+        log(f"{what}: {name} max|err|={err:.3e} max|ref|={scale:.3g} rel={err / scale:.3e}")
+        assert err <= GRAD_TOL * scale, f"{what}: {name} error {err} > {GRAD_TOL} * {scale}"
+        worst = max(worst, err / scale)
+    return worst
+
+
+def check_bwd(q, k, v, s, e, scale, what, multi=False, seed=0):
+    do = dout_for(q.shape, seed)
+    got = run_bwd(q, k, v, do, s, e, scale, multi)
+    ref = oracle.attention_bwd(*(x.float().numpy() for x in (q, k, v, do)), s, e, scale)
+    return compare_grads(got, ref, what)
+
+
+BWD_CASES = [
+    # (B, H, N, d, mask)
+    (1, 1, 1, 64, "causal"),
+    (1, 2, 64, 64, "causal"),
+    (1, 2, 130, 128, "random"),
+    (2, 2, 333, 128, "random"),
+    (1, 2, 1000, 128, "docs"),
+    (2, 1, 777, 64, "sliding"),
+    (2, 1, 1500, 128, "prefix"),
+    (1, 2, 515, 128, "random_empty"),
+    (1, 1, 300, 128, "out_of_range"),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_small(case):
+    B, H, N, d, mask = case
+    rng = np.random.default_rng(N * 11 + d)
+    s, e = small_intervals(mask, B, N, rng)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=N + 2 * d)
+    log(f"bwd small {case}")
+    check_bwd(q, k, v, s, e, inputs.default_scale(d), f"bwd {case}", seed=N)
+
+
+BWD_MULTI_CASES = [
+    (1, 2, 1000, 128, 2, "sinks"),
+    (2, 1, 700, 64, 3, "random"),
+    (1, 2, 900, 128, 4, "random_empty"),
+]
+
+
+@pytest.mark.parametrize("case", BWD_MULTI_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_multi_small(case):
+    B, H, N, d, K, kind = case
+    rng = np.random.default_rng(N * 5 + K)
+    s, e = multi_intervals(kind, B, K, N, rng)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=N + K + 7)
+    log(f"bwd multi {case}")
+    check_bwd(q, k, v, s, e, inputs.default_scale(d), f"bwd multi {case}", multi=True, seed=N + K)
+
+
+def test_bwd_q_zero_gives_zero_dk():
+    """Q = 0: dK = scale dS^T Q is exactly 0."""
+    B, H, N, d = 1, 2, 600, 128
+    rng = np.random.default_rng(17)
+    s, e = inputs.random_intervals(rng, B, N, empty_frac=0.1, max_width=200)
+    _, k, v = inputs.make_qkv(B, H, N, d, seed=17)
+    q = torch.zeros_like(k)
+    do = dout_for(q.shape, 17)
+    dq, dk, dv = run_bwd(q, k, v, do, s, e, inputs.default_scale(d), False)
+    assert np.all(dk == 0.0)
+
+
+def test_bwd_deterministic():
+    B, H, N, d = 1, 2, 2000, 128
+    spec = inputs.make_intervals("doc_uniform", B, N, 3, lo=100, hi=900)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=3)
+    do = dout_for(q.shape, 3)
+    a = run_bwd(q, k, v, do, spec.col_start, spec.col_end, inputs.default_scale(d), False)
+    b = run_bwd(q, k, v, do, spec.col_start, spec.col_end, inputs.default_scale(d), False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_doc_packed_workload_heads():
+    """The doc-packed workload (N = 8192, d = 128) at full size, four heads, all rows."""
+    cfg = inputs.CONFIGS["C2"]
+    spec = inputs.config_intervals(cfg)
+    H = 4
+    q, k, v = (x[:, :H].contiguous() for x in inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed))
+    log("bwd C2 four heads")
+    worst = check_bwd(q, k, v, spec.col_start, spec.col_end, inputs.default_scale(cfg.d), "bwd C2", seed=cfg.seed)
+    log(f"bwd C2: worst relative error {worst:.3e}")
+
+
+def test_bwd_dv_within_rounding_bound_of_each_weight():
+    """dV = P^T dO with every weight rounded to bfloat16 (relative error <= u = 2^-8)
+    and exact bf16 dO: each element obeys |dV - dV_ref| <= 2u sum_i P_ij |dO_ic| (+ fp32
+    accumulation), with P from the oracle."""
+    B, H, N, d = 1, 2, 300, 128
+    rng = np.random.default_rng(23)
+    s, e = inputs.random_intervals(rng, B, N, empty_frac=0.1, max_width=120)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=23)
+    do = dout_for(q.shape, 23)
+    _, _, dv = run_bwd(q, k, v, do, s, e, inputs.default_scale(d), False)
+    qf, kf, vf, dof = (x.float().numpy().astype(np.float64) for x in (q, k, v, do))
+    P = oracle.attention_weights(qf, kf, s, e, inputs.default_scale(d))        # [B, H, N, N]
+    ref = np.einsum("bhij,bhic->bhjc", P, dof)
+    bound = 2 * 2.0 ** -8 * np.einsum("bhij,bhic->bhjc", P, np.abs(dof)) + 1e-5
+    excess = np.abs(dv - ref) - bound
+    log(f"dV elementwise: max (err - bound) = {excess.max():.3e}, max err/bound = {(np.abs(dv - ref) / bound).max():.3f}")
+    assert excess.max() <= 0.0
