@@ -1,14 +1,15 @@
 """Benchmark of the FlashMask forward path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2] [--no-per-config]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-backward]
 
 A step is one fm_attn_fwd call (interval preprocessor + scheduler + attention
 kernel) over one batch of the workload, inputs resident in HBM.  Prints ONE
 JSON line: effective TFLOP/s counting 4*d FLOPs per attended (query, key)
 pair, the attention kernel's roofline figures (its own duration measured with
 HIP events the library records on its stream), the other workloads' figures
-under "per_config", and the CPU oracle timed on a bounded sample.
+under "per_config", the backward pass (fm_attn_bwd, 10*d FLOPs per attended
+pair) under "backward", and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ def parse():
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass figures")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -143,6 +145,46 @@ def time_config(cfg, steps, warmup, with_kernel_timer=True):
     return res
 
 
+def time_backward(cfg, steps, warmup):
+    """fm_attn_bwd steps on the workload (inputs resident: q, k, v, the forward's out and
+    lse, and a bf16 N(0,1) upstream gradient).  Algorithmic work: 10 d FLOPs per attended
+    pair (five products of 2 d: the recomputed scores, dV, dP, dK, dQ)."""
+    import torch
+    from masked_attention_fm_amd import flashmask as fm
+    from masked_attention_fm_amd import inputs, metrics
+
+    dev = torch.device("cuda:0")
+    spec = inputs.config_intervals(cfg)
+    q, k, v = (x.to(dev) for x in inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed))
+    cs = torch.from_numpy(spec.col_start).to(dev)
+    ce = torch.from_numpy(spec.col_end).to(dev)
+    scale = inputs.default_scale(cfg.d)
+    multi = spec.col_start.ndim == 3
+    fwd = fm.fm_attn_fwd_multi if multi else fm.fm_attn_fwd
+    bwd = fm.fm_attn_bwd_multi if multi else fm.fm_attn_bwd
+    out, lse = fwd(q, k, v, cs, ce, scale)
+    g = torch.Generator(device=dev).manual_seed(cfg.seed)
+    dout = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        bwd(q, k, v, out, dout, lse, cs, ce, scale, dq=dq, dk=dk, dv=dv, stream=stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        bwd(q, k, v, out, dout, lse, cs, ce, scale, dq=dq, dk=dk, dv=dv, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    U = metrics.spec_attended_pairs(spec.col_start, spec.col_end, cfg.N) * cfg.H
+    flops = 10 * cfg.d * U
+    del q, k, v, out, lse, dout, dq, dk, dv
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "effective_flops": flops, "effective_tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def load_counters(key):
     """Hardware-counter record of the attention kernel on this workload, if it was taken
     from the current kernel source (profiles/attn_fwd_<key>_counters.json)."""
@@ -230,6 +272,16 @@ def main():
                                                  "skip_ratio", "partial_ratio", "tile_executed_tflops")
                                if k in r}
 
+    backward = {}
+    if not args.no_backward:
+        for key, c in inputs.CONFIGS.items():
+            if key != cfg.key and args.no_per_config:
+                continue
+            steps = 100 if c.N <= 1024 else max(5, min(args.steps, 20))
+            r = time_backward(c, steps, min(args.warmup, 3))
+            log(f"{key} backward: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
+            backward[key] = r
+
     if args.copy_mib:
         n = args.copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
@@ -285,6 +337,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 
