@@ -1,7 +1,7 @@
 """Benchmark of the FlashMask forward path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2] [--no-per-config]
-                    [--no-cpu-baseline] [--no-backward]
+                    [--no-cpu-baseline] [--no-backward] [--no-fp8]
 
 A step is one fm_attn_fwd call (interval preprocessor + scheduler + attention
 kernel) over one batch of the workload, inputs resident in HBM.  Prints ONE
@@ -9,7 +9,8 @@ JSON line: effective TFLOP/s counting 4*d FLOPs per attended (query, key)
 pair, the attention kernel's roofline figures (its own duration measured with
 HIP events the library records on its stream), the other workloads' figures
 under "per_config", the backward pass (fm_attn_bwd, 10*d FLOPs per attended
-pair) under "backward", and the CPU oracle timed on a bounded sample.
+pair) under "backward", the FP8-input forward (fm_attn_fwd_fp8) under
+"fp8_forward", and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -35,6 +36,7 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass figures")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-input forward figures")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -185,6 +187,40 @@ def time_backward(cfg, steps, warmup):
     return {"ms_per_step": ms, "effective_flops": flops, "effective_tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def time_fp8(cfg, steps, warmup):
+    """fm_attn_fwd_fp8 steps on the workload's draws quantized per tensor to e4m3 (inputs
+    resident); same 4 d FLOPs per attended pair as the bf16 forward."""
+    import torch
+    from masked_attention_fm_amd import flashmask as fm
+    from masked_attention_fm_amd import inputs, metrics
+
+    dev = torch.device("cuda:0")
+    spec = inputs.config_intervals(cfg)
+    (q8, qs), (k8, ks), (v8, vs) = inputs.make_qkv_fp8(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    q8, k8, v8 = (x.to(dev) for x in (q8, k8, v8))
+    cs = torch.from_numpy(spec.col_start).to(dev)
+    ce = torch.from_numpy(spec.col_end).to(dev)
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
+    scale = inputs.default_scale(cfg.d)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    flops = 4 * cfg.d * metrics.spec_attended_pairs(spec.col_start, spec.col_end, cfg.N) * cfg.H
+    del q8, k8, v8, out, lse
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "effective_flops": flops, "effective_tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def load_counters(key):
     """Hardware-counter record of the attention kernel on this workload, if it was taken
     from the current kernel source (profiles/attn_fwd_<key>_counters.json)."""
@@ -282,6 +318,16 @@ def main():
             log(f"{key} backward: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
             backward[key] = r
 
+    fp8 = {}
+    if not args.no_fp8:
+        for key, c in inputs.CONFIGS.items():
+            if key != cfg.key and args.no_per_config:
+                continue
+            steps = 200 if c.N <= 1024 else max(5, min(args.steps, 20))
+            r = time_fp8(c, steps, min(args.warmup, 5))
+            log(f"{key} fp8: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
+            fp8[key] = r
+
     if args.copy_mib:
         n = args.copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
@@ -338,6 +384,7 @@ def main():
         "cpu_baseline": cpu,
         "per_config": per_config,
         "backward": backward,
+        "fp8_forward": fp8,
     }
     print(json.dumps(line), flush=True)
 

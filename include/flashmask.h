@@ -133,6 +133,29 @@ FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v,
                              void* out, float* lse, hipStream_t stream);
 
 /*
+ * fm_attn_fwd_fp8 -- the forward pass on FP8 inputs.  The FlashMask article
+ * names an FP8 mode of its H100 path (§4.2) without saying which products run
+ * in FP8.  Reading used here: Q, K and V are stored as OCP FP8 e4m3 (the
+ * "e4m3fn" encoding: bias 7, no infinities, 0x7F/0xFF NaN) with one
+ * dequantization scale per tensor (the real value of a code x is
+ * scale * e4m3(x)); the score product Q K^T runs on the FP8 matrix units with
+ * fp32 accumulation; V is widened exactly to bf16 and the weights and the
+ * P V product stay bf16, as in fm_attn_fwd.  The result is therefore
+ * fm_attn_fwd's result for the dequantized inputs, to the same accuracy.
+ *
+ *   q8, k8, v8 : uint8 (e4m3) [B][H][N][d] device, contiguous, 16-byte aligned.
+ *   q_scale, k_scale, v_scale : dequantization scales, finite and > 0.
+ *   col_start, col_end, n_ranges : as fm_attn_fwd_multi ([B][n_ranges][N]).
+ *   B, H, N, d, scale, out, lse, stream : as fm_attn_fwd (out is bfloat16).
+ * Errors as fm_attn_fwd_multi; FM_ERR_INVALID_ARG for a bad scale.
+ */
+FM_API int fm_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                           float q_scale, float k_scale, float v_scale,
+                           const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                           int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                           void* out, float* lse, hipStream_t stream);
+
+/*
  * fm_classify_tiles_multi -- fm_classify_tiles for one sequence whose rows
  * hold n_ranges ranges: col_start, col_end are int32 [n_ranges][N] device
  * (for batch b pass col_start + b*n_ranges*N).  Classes as stated above.

@@ -212,9 +212,15 @@ FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, in
     return fm_tile_schedule_multi(col_start, col_end, 1, B, N, d, work_out, order_out);
 }
 
-FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v, const int32_t* col_start,
-                             const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
-                             int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass for bf16 inputs (fp8_scales == nullptr) or e4m3 inputs with
+// their three dequantization scales.
+int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* col_start, const int32_t* col_end,
+                  int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
+                  hipStream_t stream, const float* fp8_scales) {
     // ---- host-side checks, before any HIP call
     if (q == nullptr || k == nullptr || v == nullptr || col_start == nullptr || col_end == nullptr ||
         out == nullptr || lse == nullptr)
@@ -265,12 +271,32 @@ FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v, const 
         }
     }
     FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, n_ranges, meta, natural ? nullptr : order, B, H,
-                                N, d, scale, out, lse, stream, ev.first, ev.second));
+                                N, d, scale, out, lse, stream, ev.first, ev.second, fp8_scales));
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
         g_timing.pending.push_back(ev);
     }
     return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v, const int32_t* col_start,
+                             const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
+                             int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
+    return attn_fwd_impl(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, nullptr);
+}
+
+FM_API int fm_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_scale, float k_scale,
+                           float v_scale, const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                           int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
+                           hipStream_t stream) {
+    const float scales[3] = {q_scale, k_scale, v_scale};
+    for (float x : scales)
+        if (!(x > 0.f) || !isfinite(x)) return FM_ERR_INVALID_ARG;
+    return attn_fwd_impl(q8, k8, v8, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, scales);
 }
 
 FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_t* col_start,

@@ -127,15 +127,122 @@ __device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D, NIV>& 
     }
 }
 
-// NIV: ranges per query row (the row attends their union).  col_start and
-// col_end are [B][NIV][N]; meta holds NIV records per query block.
+// ---------------------------------------------------------------- FP8 inputs
+//
+// Q, K and V stored as OCP e4m3 (one byte) with per-tensor dequantization
+// scales.  The score product runs on v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit block scales: a 32 x 32 x 64 product whose A and B operands hold 32
+// bytes per lane, and whose A row / B column is the lane mod 32 and whose
+// contraction index depends only on (lane / 32, byte) in the same way for A
+// and B (checked by an in-bounds probe), so any consistent order of the head
+// dimension is correct: lane half h of a 64-wide step holds columns
+// 64 cs + 32 h + (0..31).  V is widened to bf16 while it is staged (exact: the
+// three mantissa bits of e4m3 fit in bf16), so the PV product, the weights
+// and the output keep the bf16 path's arithmetic.
+constexpr int kK8Pad = 16;                     // bytes of padding per fp8 K row in LDS
+constexpr int kUnitScales = 0x7F7F7F7F;        // E8M0 block scale 2^0 in every byte
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
 template <int D, int NIV>
+struct alignas(16) Smem8 {
+    alignas(16) uint8_t k8[2][kBc][D + kK8Pad];   // K block, row-major, e4m3
+    alignas(16) uint16_t vt[2][D][kBc + kVPad];   // V block widened to bf16, transposed, vt_pos order
+    int start[NIV][kBr];
+    int width[NIV][kBr];
+};
+static_assert((128 + kK8Pad) % 16 == 0 && (64 + kK8Pad) % 16 == 0, "fp8 K rows 16-byte aligned");
+
+template <int D>
+struct Staging8 {
+    static constexpr int kChunksK = kBc * D / 16 / kThreads;  // 16-byte K chunks per thread
+    static constexpr int kItemsV = (kBc / 4) * (D / 8);       // 4 keys x 8 columns per item
+    static_assert(kChunksK >= 1 && kChunksK * kThreads * 16 == kBc * D, "K block splits evenly");
+    static_assert(kItemsV <= kThreads, "one V item per thread at most");
+    u32x4 k[kChunksK];
+    u32x2 v[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_block8(Staging8<D>& st, __amdgpu_buffer_rsrc_t krs,
+                                            __amdgpu_buffer_rsrc_t vrs, int kv0, int tid) {
+    const int base = kv0 * D;
+#pragma unroll
+    for (int c = 0; c < Staging8<D>::kChunksK; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int row = chunk / (D / 16);
+        const int col16 = chunk % (D / 16);
+        st.k[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + row * D + col16 * 16, 0, 0);
+    }
+    if (Staging8<D>::kItemsV == kThreads || tid < Staging8<D>::kItemsV) {
+        const int j0 = 4 * (tid % (kBc / 4));
+        const int n0 = 8 * (tid / (kBc / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            st.v[r] = __builtin_amdgcn_raw_buffer_load_b64(vrs, base + (j0 + r) * D + n0, 0, 0);
+    }
+}
+
+// Two e4m3 bytes of `w` (the low or the high half) as a packed bf16 pair.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    const bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int D, int NIV>
+__device__ __forceinline__ void store_block8(const Staging8<D>& st, Smem8<D, NIV>& sm, int buf, int tid) {
+#pragma unroll
+    for (int c = 0; c < Staging8<D>::kChunksK; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int row = chunk / (D / 16);
+        const int col16 = chunk % (D / 16);
+        *reinterpret_cast<u32x4*>(&sm.k8[buf][row][col16 * 16]) = st.k[c];
+    }
+    if (Staging8<D>::kItemsV == kThreads || tid < Staging8<D>::kItemsV) {
+        const int j0 = 4 * (tid % (kBc / 4));
+        const int n0 = 8 * (tid / (kBc / 4));
+        u32x4 rows[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            rows[r] = u32x4{e4m3x2_to_bf16x2<false>(st.v[r][0]), e4m3x2_to_bf16x2<true>(st.v[r][0]),
+                            e4m3x2_to_bf16x2<false>(st.v[r][1]), e4m3x2_to_bf16x2<true>(st.v[r][1])};
+        store_transposed_4x8(rows, &sm.vt[buf][0][0], kBc + kVPad, n0, vt_pos(j0));
+    }
+}
+
+// Types of one instantiation: bf16 inputs, or e4m3 inputs (F8).
+template <int D, int NIV, bool F8>
+struct FwdTypes {
+    using In = uint16_t;
+    using Shared = Smem<D, NIV>;
+    using Stage = Staging<D>;
+    using QReg = bf16x8;
+    static constexpr int kQRegs = D / 16;
+};
+template <int D, int NIV>
+struct FwdTypes<D, NIV, true> {
+    using In = uint8_t;
+    using Shared = Smem8<D, NIV>;
+    using Stage = Staging8<D>;
+    using QReg = v8i;
+    static constexpr int kQRegs = D / 64;
+};
+
+// NIV: ranges per query row (the row attends their union).  col_start and
+// col_end are [B][NIV][N]; meta holds NIV records per query block.  F8: Q, K,
+// V are e4m3 (c then includes their dequantization scales, and v_scale
+// multiplies the output).
+template <int D, int NIV, bool F8>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
-    const TileMeta* __restrict__ meta, const int32_t* __restrict__ order, int H, int N, int n_q,
-    float c, int xcd_heads, uint16_t* __restrict__ O, float* __restrict__ LSE) {
-    __shared__ Smem<D, NIV> sm;
+    const typename FwdTypes<D, NIV, F8>::In* __restrict__ Q, const typename FwdTypes<D, NIV, F8>::In* __restrict__ K,
+    const typename FwdTypes<D, NIV, F8>::In* __restrict__ V, const int32_t* __restrict__ col_start,
+    const int32_t* __restrict__ col_end, const TileMeta* __restrict__ meta, const int32_t* __restrict__ order,
+    int H, int N, int n_q, float c, float v_scale, int xcd_heads, uint16_t* __restrict__ O,
+    float* __restrict__ LSE) {
+    using T = FwdTypes<D, NIV, F8>;
+    constexpr int kElt = (int)sizeof(typename T::In);   // bytes per Q/K/V element
+    __shared__ typename T::Shared sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -168,9 +275,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     for (int k = 0; k < NIV; ++k) tm[k] = meta[(int64_t)bt * NIV + k];
 
     const int64_t bh = (int64_t)b * H + h;
-    const uint16_t* Qbh = Q + bh * N * D;
-    const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + bh * N * D, N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + bh * N * D, N * D * 2);
+    const typename T::In* Qbh = Q + bh * N * D;
+    const __amdgpu_buffer_rsrc_t krs =
+        slice_rsrc(reinterpret_cast<const uint16_t*>(K + bh * N * D), N * D * kElt);
+    const __amdgpu_buffer_rsrc_t vrs =
+        slice_rsrc(reinterpret_cast<const uint16_t*>(V + bh * N * D), N * D * kElt);
     const int row0 = t * kBr;
 
     // Stage the block's intervals on chip, clamped to the key range [0, N).
@@ -193,15 +302,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         }
     }
 
-    // Q rows of this lane as MFMA B operands: Q[row][16 cs + 8 half .. +7].
+    // Q rows of this lane as MFMA B operands: Q[row][16 cs + 8 half .. +7]
+    // (F8: Q[row][64 cs + 32 half .. +31]).
     const int qrow = row0 + wave * kRowsPerWave + r32;
-    bf16x8 qreg[D / 16];
+    typename T::QReg qreg[T::kQRegs];
 #pragma unroll
-    for (int cs = 0; cs < D / 16; ++cs) {
-        if (qrow < N)
-            qreg[cs] = *reinterpret_cast<const bf16x8*>(Qbh + (int64_t)qrow * D + cs * 16 + half * 8);
-        else
-            qreg[cs] = bf16x8{};
+    for (int cs = 0; cs < T::kQRegs; ++cs) {
+        if constexpr (F8) {
+            if (qrow < N) {
+                const uint8_t* src = Qbh + (int64_t)qrow * D + cs * 64 + half * 32;
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
+                qreg[cs] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+                qreg[cs] = v8i{};
+            }
+        } else {
+            if (qrow < N)
+                qreg[cs] = *reinterpret_cast<const bf16x8*>(Qbh + (int64_t)qrow * D + cs * 16 + half * 8);
+            else
+                qreg[cs] = bf16x8{};
+        }
     }
 
     floatx16 oacc[D / 32];
@@ -232,15 +353,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     // blocks (one contiguous run for a single range).
     int j = union_next<NIV>(tm, -1);
     if (j != INT_MAX) {
-        Staging<D> stage;
-        load_block<D>(stage, krs, vrs, j * kBc, tid);
-        store_block<D>(stage, sm, 0, tid);
+        typename T::Stage stage;
+        if constexpr (F8) {
+            load_block8<D>(stage, krs, vrs, j * kBc, tid);
+            store_block8<D>(stage, sm, 0, tid);
+        } else {
+            load_block<D>(stage, krs, vrs, j * kBc, tid);
+            store_block<D>(stage, sm, 0, tid);
+        }
         __syncthreads();
 
         for (int buf = 0;; buf ^= 1) {
             const int j_next = union_next<NIV>(tm, j);
             const bool has_next = j_next != INT_MAX;
-            if (has_next) load_block<D>(stage, krs, vrs, j_next * kBc, tid);
+            if (has_next) {
+                if constexpr (F8)
+                    load_block8<D>(stage, krs, vrs, j_next * kBc, tid);
+                else
+                    load_block<D>(stage, krs, vrs, j_next * kBc, tid);
+            }
 
             const int klo = j * kBc;
             const int khi = min(klo + kBc, N) - 1;
@@ -258,13 +389,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 floatx16 st[kBc / 32];
 #pragma unroll
                 for (int jb = 0; jb < kBc / 32; ++jb) st[jb] = floatx16{};
+                if constexpr (F8) {
 #pragma unroll
-                for (int cs = 0; cs < D / 16; ++cs) {
+                    for (int cs = 0; cs < D / 64; ++cs) {
 #pragma unroll
-                    for (int jb = 0; jb < kBc / 32; ++jb) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            &sm.k[buf][jb * 32 + r32][cs * 16 + half * 8]);
-                        st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
+                        for (int jb = 0; jb < kBc / 32; ++jb) {
+                            const uint8_t* src = &sm.k8[buf][jb * 32 + r32][cs * 64 + half * 32];
+                            const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
+                            const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
+                            const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                            st[jb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qreg[cs], st[jb], 0, 0, 0,
+                                                                                     kUnitScales, 0, kUnitScales);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int cs = 0; cs < D / 16; ++cs) {
+#pragma unroll
+                        for (int jb = 0; jb < kBc / 32; ++jb) {
+                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                                &sm.k[buf][jb * 32 + r32][cs * 16 + half * 8]);
+                            st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
+                        }
                     }
                 }
 
@@ -341,7 +487,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 l16_run += rs16;
             }
 
-            if (has_next) store_block<D>(stage, sm, buf ^ 1, tid);
+            if (has_next) {
+                if constexpr (F8)
+                    store_block8<D>(stage, sm, buf ^ 1, tid);
+                else
+                    store_block<D>(stage, sm, buf ^ 1, tid);
+            }
             __syncthreads();
             if (!has_next) break;
             j = j_next;
@@ -352,7 +503,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const float l = halves_sum(l_run);
     const float l16 = halves_sum(l16_run);
     if (qrow < N) {
-        const float inv = l16 > 0.f ? 1.f / l16 : 0.f;
+        float inv = l16 > 0.f ? 1.f / l16 : 0.f;
+        if constexpr (F8) inv *= v_scale;
         uint16_t* orow = O + bh * N * D + (int64_t)qrow * D;
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
@@ -373,25 +525,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
-                            float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                            float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                            const float* fp8_scales) {
     const int64_t n_q = (N + kBr - 1) / kBr;
     const int64_t grid = B * H * n_q;
-    const float c = scale * kLog2e;
-    const auto* Qp = static_cast<const uint16_t*>(q);
-    const auto* Kp = static_cast<const uint16_t*>(k);
-    const auto* Vp = static_cast<const uint16_t*>(v);
+    const bool f8 = fp8_scales != nullptr;
+    const float c = (f8 ? scale * fp8_scales[0] * fp8_scales[1] : scale) * kLog2e;
+    const float v_scale = f8 ? fp8_scales[2] : 1.f;
     auto* Op = static_cast<uint16_t*>(out);
     // XCD-local head order needs whole heads per XCD and at least one XCD's
     // worth of resident workgroups (32 CUs x 2) per head.
     const int xcd_heads = (H % 8 == 0 && B * n_q >= 128) ? 1 : 0;
     return dispatch_ranges(n_iv, [&](auto niv) {
         constexpr int NIV = decltype(niv)::value;
-        auto kernel = d == 128 ? attn_fwd_kernel<128, NIV> : attn_fwd_kernel<64, NIV>;
         // With an event pair, the dispatch packet itself stamps the kernel's
         // start and end, so the pair measures the kernel alone.
-        hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp,
-                              Kp, Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, xcd_heads,
-                              Op, lse);
+        if (f8) {
+            const auto* Qp = static_cast<const uint8_t*>(q);
+            const auto* Kp = static_cast<const uint8_t*>(k);
+            const auto* Vp = static_cast<const uint8_t*>(v);
+            auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, true> : attn_fwd_kernel<64, NIV, true>;
+            hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
+                                  Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
+                                  xcd_heads, Op, lse);
+        } else {
+            const auto* Qp = static_cast<const uint16_t*>(q);
+            const auto* Kp = static_cast<const uint16_t*>(k);
+            const auto* Vp = static_cast<const uint16_t*>(v);
+            auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, false> : attn_fwd_kernel<64, NIV, false>;
+            hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
+                                  Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
+                                  xcd_heads, Op, lse);
+        }
         return hipGetLastError();
     });
 }

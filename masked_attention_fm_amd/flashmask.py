@@ -34,6 +34,8 @@ SIGNATURES = {
     "fm_attn_fwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
                                          _P, _P, _P]),
     "fm_classify_tiles_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P]),
+    "fm_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P, _I32,
+                                       _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P]),
     "fm_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                    _P, _P, _P, _P]),
     "fm_attn_bwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64,
@@ -243,6 +245,51 @@ def fm_attn_fwd_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_sta
     _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
     return _attn("fm_attn_fwd_multi", q, k, v, col_start, col_end, col_start.shape[1], scale, out, lse,
                  stream)
+
+
+def fm_attn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float, k_scale: float,
+                    v_scale: float, col_start: torch.Tensor, col_end: torch.Tensor, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward pass on e4m3 inputs (uint8 or torch.float8_e4m3fn tensors [B,H,N,d]) with per-tensor
+    dequantization scales; intervals [B, N] or [B, K, N].  Returns (out bf16, lse fp32).  Asynchronous."""
+    codes = []
+    for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if isinstance(x, torch.Tensor) and x.dtype == torch.float8_e4m3fn:
+            x = x.view(torch.uint8)
+        _dev_tensor(x, name, torch.uint8)
+        codes.append(x)
+    q8, k8, v8 = codes
+    if q8.dim() != 4 or k8.shape != q8.shape or v8.shape != q8.shape:
+        raise ValueError("q8, k8, v8 must share one [B, H, N, d] shape")
+    B, H, N, d = q8.shape
+    if col_start.dim() == 2:
+        _intervals(col_start, col_end, (B, N), "[B, N]")
+        n_ranges = 1
+    else:
+        if col_start.dim() != 3:
+            raise ValueError("col_start / col_end must be [B, N] or [B, K, N]")
+        _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
+        n_ranges = col_start.shape[1]
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    else:
+        _dev_tensor(out, "out", torch.bfloat16)
+        if out.shape != q8.shape:
+            raise ValueError("out must match q8's shape")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    else:
+        _dev_tensor(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be [B, H, N]")
+    status = lib().fm_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), float(q_scale), float(k_scale),
+                                   float(v_scale), col_start.data_ptr(), col_end.data_ptr(), n_ranges, B, H, N, d,
+                                   float(scale), out.data_ptr(), lse.data_ptr(), _stream_handle(stream))
+    _check("fm_attn_fwd_fp8", status)
+    return out, lse
 
 
 def _bwd(func: str, q, k, v, out, dout, lse, col_start, col_end, n_ranges: Optional[int], scale,

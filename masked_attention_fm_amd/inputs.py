@@ -262,6 +262,37 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int,
     return out[0], out[1], out[2]
 
 
+E4M3_MAX = 448.0        # largest finite OCP e4m3 ("e4m3fn") value
+
+
+def quantize_e4m3(x: torch.Tensor) -> Tuple[torch.Tensor, float]:
+    """Per-tensor FP8 quantization: (uint8 e4m3fn codes, scale) with scale = amax / 448 as a
+    float32 value and codes = RNE(x / scale), so that scale * e4m3(code) approximates x."""
+    xf = x.float()
+    amax = float(xf.abs().max())
+    scale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    y = (xf / scale).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
+
+
+def dequantize_e4m3(codes: torch.Tensor, scale: float) -> np.ndarray:
+    """float64 values scale * e4m3(code) (the decode is exact)."""
+    return codes.view(torch.float8_e4m3fn).float().numpy().astype(np.float64) * float(np.float32(scale))
+
+
+def make_qkv_fp8(B: int, H: int, N: int, d: int, seed: int, threads: Optional[int] = None):
+    """The make_qkv draws (before their bf16 rounding), quantized per tensor to e4m3:
+    ((q8, q_scale), (k8, k_scale), (v8, v_scale)) with uint8 codes [B, H, N, d]."""
+    out = [torch.empty(B, H, N, d, dtype=torch.float32) for _ in range(3)]
+    names = ("q", "k", "v")
+    for t in range(3):
+        for b in range(B):
+            for h in range(H):
+                g = torch.Generator().manual_seed(_slice_seed(seed, _TENSOR_INDEX[names[t]], b, h))
+                out[t][b, h] = torch.randn(N, d, generator=g, dtype=torch.float32)
+    return tuple(quantize_e4m3(x) for x in out)
+
+
 def default_scale(d: int) -> float:
     """1/sqrt(d) rounded to float32 (the value a caller passes as a C float)."""
     return float(np.float32(1.0 / np.sqrt(np.float32(d))))

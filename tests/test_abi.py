@@ -205,3 +205,26 @@ def test_attn_bwd_rejects_bad_arguments(L, n_ranges, kw, status):
 def test_attn_bwd_multi_rejects_bad_range_count(L):
     assert bwd(L, 0) == fmb.FM_ERR_INVALID_ARG
     assert bwd(L, fmb.FM_MAX_RANGES + 1) == fmb.FM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("scales,status", [
+    ((0.0, 1.0, 1.0), fmb.FM_ERR_INVALID_ARG),
+    ((1.0, -1.0, 1.0), fmb.FM_ERR_INVALID_ARG),
+    ((1.0, 1.0, float("nan")), fmb.FM_ERR_INVALID_ARG),
+    ((1.0, float("inf"), 1.0), fmb.FM_ERR_INVALID_ARG),
+])
+def test_attn_fwd_fp8_rejects_bad_scales(L, scales, status):
+    assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, *scales, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
+                             None) == status
+
+
+def test_attn_fwd_fp8_rejects_bad_arguments(L):
+    ok = (1.0, 1.0, 1.0)
+    assert L.fm_attn_fwd_fp8(None, FAKE, FAKE, *ok, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
+                             None) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, *ok, FAKE, FAKE, 0, 1, 1, 128, 128, 0.125, FAKE, FAKE,
+                             None) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, *ok, FAKE, FAKE, 1, 1, 1, 128, 96, 0.125, FAKE, FAKE,
+                             None) == fmb.FM_ERR_UNSUPPORTED
+    assert L.fm_attn_fwd_fp8(FAKE + 8, FAKE, FAKE, *ok, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
+                             None) == fmb.FM_ERR_INVALID_ARG

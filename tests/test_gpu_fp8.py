@@ -1,0 +1,122 @@
+"""GPU parity of the FP8-input forward pass (fm_attn_fwd_fp8): the oracle on the
+dequantized e4m3 inputs.  The score product is exact for FP8 inputs up to the FP8
+units' accumulation, and V widens exactly to bf16, so the bf16 path's error model
+applies: small cases are held to its elementwise bound (output and weight rounding),
+the full-size doc-packed workload to the 1e-2 / 1e-3 bars."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from masked_attention_fm_amd import flashmask as fm
+from masked_attention_fm_amd import inputs
+
+from test_gpu_parity import DEV, compare, log, small_intervals, to_dev
+from test_gpu_multi import multi_intervals
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp8(qkv8, s, e, scale):
+    (q8, qs), (k8, ks), (v8, vs) = qkv8
+    qd, kd, vd = to_dev(q8, k8, v8)
+    out = torch.full(q8.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(q8.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fm.fm_attn_fwd_fp8(qd, kd, vd, qs, ks, vs, *to_dev(s, e), scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_fp8(qkv8, s, e, scale, what, rows=None):
+    O, L = run_fp8(qkv8, s, e, scale)
+    deq = [inputs.dequantize_e4m3(c, sc) for c, sc in qkv8]
+    O_ref, L_ref = oracle.attention(*deq, s, e, scale, rows=rows)
+    if rows is not None:
+        O, L = O[:, :, rows], L[:, :, rows]
+    return compare(O, L, O_ref, L_ref, what)
+
+
+def bf16_half_ulp(x):
+    """Half the bf16 spacing at |x| (bf16 keeps 8 significant bits)."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def check_fp8_model(qkv8, s, e, scale, what):
+    """Elementwise bound of the bf16 output path on the dequantized inputs: rounding O to
+    bf16 (half an ulp) plus rounding each weight to bf16 before the PV product (relative
+    2^-8, so |dO_i| <= 2^-8 sum_j P_ij |v_j - O_i|), plus 1e-4 for the fp32 arithmetic and
+    the FP8 score accumulation; LSE within 1e-3."""
+    O, L = run_fp8(qkv8, s, e, scale)
+    q, k, v = (inputs.dequantize_e4m3(c, sc) for c, sc in qkv8)
+    O_ref, L_ref = oracle.attention(q, k, v, s, e, scale)
+    P = oracle.attention_weights(q, k, s, e, scale)                  # [B, H, N, N]
+    spread = np.einsum("bhij,bhijc->bhic", P, np.abs(v[:, :, None, :, :] - O_ref[:, :, :, None, :]))
+    bound = bf16_half_ulp(O_ref) + 2.0 ** -8 * spread + 1e-4
+    err = np.abs(O - O_ref)
+    empty = np.isneginf(L_ref)
+    assert np.array_equal(np.isneginf(L), empty), f"{what}: -inf LSE pattern differs"
+    dL = float(np.abs(L[~empty] - L_ref[~empty]).max()) if (~empty).any() else 0.0
+    log(f"{what}: max|dO|={err.max():.3e} max err/bound={(err / bound).max():.3f} max|dLSE|={dL:.3e}")
+    assert np.all(err <= bound), f"{what}: {(err > bound).sum()} elements beyond the rounding bound"
+    assert dL <= 1e-3
+
+
+FP8_CASES = [
+    (1, 1, 1, 64, "causal"),
+    (1, 2, 64, 64, "causal"),
+    (1, 2, 130, 128, "random"),
+    (2, 2, 333, 128, "random"),
+    (1, 2, 1000, 128, "docs"),
+    (2, 2, 777, 64, "sliding"),
+    (2, 1, 1500, 128, "prefix"),
+    (1, 2, 515, 128, "random_empty"),
+    (1, 1, 300, 128, "out_of_range"),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fp8_small(case):
+    B, H, N, d, mask = case
+    rng = np.random.default_rng(N * 13 + d)
+    s, e = small_intervals(mask, B, N, rng)
+    qkv8 = inputs.make_qkv_fp8(B, H, N, d, seed=N + 3 * d)
+    log(f"fp8 small {case}")
+    check_fp8_model(qkv8, s, e, inputs.default_scale(d), f"fp8 {case}")
+
+
+def test_fp8_multi_range():
+    B, H, N, d, K = 2, 2, 900, 128, 3
+    rng = np.random.default_rng(33)
+    s, e = multi_intervals("random_empty", B, K, N, rng)
+    qkv8 = inputs.make_qkv_fp8(B, H, N, d, seed=33)
+    check_fp8_model(qkv8, s, e, inputs.default_scale(d), "fp8 multi")
+
+
+def test_fp8_doc_packed_workload():
+    """The doc-packed workload (B=1, H=16, N=8192, d=128) from FP8 inputs, all rows."""
+    cfg = inputs.CONFIGS["C2"]
+    spec = inputs.config_intervals(cfg)
+    qkv8 = inputs.make_qkv_fp8(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    log("fp8 C2")
+    dO, dL = check_fp8(qkv8, spec.col_start, spec.col_end, inputs.default_scale(cfg.d), "fp8 C2")
+    log(f"fp8 C2: max|dO|={dO:.3e} max|dLSE|={dL:.3e}")
+
+
+def test_fp8_zero_q_is_mean_of_v():
+    """Q = 0: O_r is the mean of the dequantized v over the row's keys, LSE_r = ln(#keys)."""
+    B, H, N, d = 1, 2, 500, 128
+    rng = np.random.default_rng(41)
+    s, e = inputs.random_intervals(rng, B, N, empty_frac=0.05, max_width=250)
+    qkv8 = list(inputs.make_qkv_fp8(B, H, N, d, seed=41))
+    qkv8[0] = (torch.zeros_like(qkv8[0][0]), qkv8[0][1])
+    O, L = run_fp8(qkv8, s, e, inputs.default_scale(d))
+    v = inputs.dequantize_e4m3(*qkv8[2])
+    for i in range(N):
+        if s[0, i] > e[0, i]:
+            assert np.all(O[0, :, i] == 0) and np.all(np.isneginf(L[0, :, i]))
+            continue
+        mean = v[0][:, s[0, i]:e[0, i] + 1].mean(axis=1)
+        assert np.abs(O[0, :, i] - mean).max() <= 1e-2
+        assert np.abs(L[0, :, i] - np.log(e[0, i] - s[0, i] + 1)).max() <= 1e-3

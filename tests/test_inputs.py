@@ -117,3 +117,24 @@ def test_random_intervals_valid():
     nonempty = s <= e
     assert np.all(s >= 0) and np.all(e <= 332)
     assert 0.1 < 1 - nonempty.mean() < 0.3
+
+
+def test_e4m3_decode_known_codes():
+    """OCP e4m3fn: bias 7, 3 mantissa bits, largest finite 448, no infinities."""
+    codes = torch.tensor([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x7E, 0x80, 0xB8, 0x7F], dtype=torch.uint8)
+    vals = inputs.dequantize_e4m3(codes, 1.0)
+    expect = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 448.0, -0.0, -1.0]
+    assert vals[:9].tolist() == expect
+    assert np.isnan(vals[9])
+
+
+def test_quantize_e4m3_round_trip():
+    x = torch.randn(4096, generator=torch.Generator().manual_seed(1))
+    codes, scale = inputs.quantize_e4m3(x)
+    assert codes.dtype == torch.uint8 and scale > 0
+    back = inputs.dequantize_e4m3(codes, scale)
+    assert np.abs(back).max() <= 448.0 * scale * (1 + 1e-7)
+    # relative error of a round-to-nearest 4-significant-bit code, away from the subnormals
+    big = np.abs(x.numpy()) > 2.0 ** -6 * scale
+    rel = np.abs(back[big] - x.numpy()[big]) / np.abs(x.numpy()[big])
+    assert rel.max() <= 2.0 ** -4 + 1e-6
