@@ -133,6 +133,21 @@ FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v,
                              void* out, float* lse, hipStream_t stream);
 
 /*
+ * fm_attn_fwd_per_head -- fm_attn_fwd_multi with one interval set per head
+ * (the FlashMask article's §3.4 and §6.1 item 3: masks that differ across
+ * heads and layers, e.g. a different window per head; layers simply pass
+ * their own intervals).  col_start, col_end are int32 [B][H][n_ranges][N]
+ * device: range k of row r of head h of batch b is element
+ * ((b*H + h)*n_ranges + k)*N + r.  With every head's set equal, the results
+ * are bit-identical to fm_attn_fwd_multi's.  Other arguments, asynchrony and
+ * errors as fm_attn_fwd_multi.
+ */
+FM_API int fm_attn_fwd_per_head(const void* q, const void* k, const void* v,
+                                const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                                int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                void* out, float* lse, hipStream_t stream);
+
+/*
  * fm_attn_fwd_fp8 -- the forward pass on FP8 inputs.  The FlashMask article
  * names an FP8 mode of its H100 path (§4.2) without saying which products run
  * in FP8.  Reading used here: Q, K and V are stored as OCP FP8 e4m3 (the

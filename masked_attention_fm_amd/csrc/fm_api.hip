@@ -220,7 +220,7 @@ namespace {
 // their three dequantization scales.
 int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* col_start, const int32_t* col_end,
                   int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
-                  hipStream_t stream, const float* fp8_scales) {
+                  hipStream_t stream, const float* fp8_scales, bool per_head = false) {
     // ---- host-side checks, before any HIP call
     if (q == nullptr || k == nullptr || v == nullptr || col_start == nullptr || col_end == nullptr ||
         out == nullptr || lse == nullptr)
@@ -233,11 +233,12 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* co
         !aligned(lse, 4) || !aligned(col_start, 4) || !aligned(col_end, 4))
         return FM_ERR_INVALID_ARG;
     const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
-    if (B * H * n_q >= (int64_t(1) << 31) || B * n_ranges * N >= (int64_t(1) << 40))
+    const int64_t n_sets = per_head ? H : 1;   // interval sets per batch element
+    if (B * H * n_q >= (int64_t(1) << 31) || B * n_sets * n_ranges * N >= (int64_t(1) << 40))
         return FM_ERR_INVALID_ARG;
 
-    // ---- workspace: meta[M][n_ranges] | work[M] | order[M]
-    const int64_t M = B * n_q;
+    // ---- workspace: meta[M][n_ranges] | work[M] | order[M], M = n_sets * B * n_q
+    const int64_t M = n_sets * B * n_q;
     const size_t meta_bytes = ((size_t)(M * n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
     const size_t int_bytes = ((size_t)M * sizeof(int32_t) + 255) & ~size_t(255);
     void* ws = nullptr;
@@ -250,11 +251,11 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* co
     if (!natural && M <= fm::kPrepSmallMax) {
         // one launch: metadata and longest-first order together
         FM_HIP(fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work, order,
-                                     stream));
+                                     stream, (int)n_sets));
     } else {
         FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work, nullptr,
-                                     stream));
-        if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream));
+                                     stream, (int)n_sets));
+        if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream, B * n_q));
     }
 
     std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
@@ -271,7 +272,7 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* co
         }
     }
     FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, n_ranges, meta, natural ? nullptr : order, B, H,
-                                N, d, scale, out, lse, stream, ev.first, ev.second, fp8_scales));
+                                N, d, scale, out, lse, stream, ev.first, ev.second, fp8_scales, (int)n_sets));
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
         g_timing.pending.push_back(ev);
@@ -287,6 +288,12 @@ FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v, const 
                              const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
                              int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
     return attn_fwd_impl(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, nullptr);
+}
+
+FM_API int fm_attn_fwd_per_head(const void* q, const void* k, const void* v, const int32_t* col_start,
+                                const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
+                                int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
+    return attn_fwd_impl(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, nullptr, true);
 }
 
 FM_API int fm_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_scale, float k_scale,

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const typename FwdTypes<D, NIV, F8>::In* __restrict__ Q, const typename FwdTypes<D, NIV, F8>::In* __restrict__ K,
     const typename FwdTypes<D, NIV, F8>::In* __restrict__ V, const int32_t* __restrict__ col_start,
     const int32_t* __restrict__ col_end, const TileMeta* __restrict__ meta, const int32_t* __restrict__ order,
-    int H, int N, int n_q, float c, float v_scale, int xcd_heads, uint16_t* __restrict__ O,
+    int H, int N, int n_q, float c, float v_scale, int xcd_heads, int per_head, uint16_t* __restrict__ O,
     float* __restrict__ LSE) {
     using T = FwdTypes<D, NIV, F8>;
     constexpr int kElt = (int)sizeof(typename T::In);   // bytes per Q/K/V element
@@ -267,9 +267,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         h = blockIdx.x % H;
         q_item = blockIdx.x / H;
     }
-    const int bt = order != nullptr ? order[q_item] : q_item;
-    const int b = bt / n_q;
-    const int t = bt - b * n_q;
+    // With one interval set per head, head h reads set h: its items are the
+    // segment [h L, h L + L) of the preprocessor's records and of the order.
+    const int L = gridDim.x / H;                 // query blocks per head (B n_q)
+    const int set = per_head ? h : 0;
+    const int n_sets = per_head ? H : 1;
+    const int bt = order != nullptr ? order[set * L + q_item] : set * L + q_item;
+    const int local = bt - set * L;
+    const int b = local / n_q;
+    const int t = local - b * n_q;
     TileMeta tm[NIV];
 #pragma unroll
     for (int k = 0; k < NIV; ++k) tm[k] = meta[(int64_t)bt * NIV + k];
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         for (int k = 0; k < NIV; ++k) {
             int s = kEmptyStart, w = 0;
             if (r < N) {
-                const int64_t at = ((int64_t)b * NIV + k) * N + r;
+                const int64_t at = (((int64_t)b * n_sets + set) * NIV + k) * N + r;
                 const int sc = max(col_start[at], 0);
                 const int ec = min(col_end[at], N - 1);
                 if (sc <= ec) {
@@ -526,7 +532,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                            const float* fp8_scales) {
+                            const float* fp8_scales, int n_sets) {
     const int64_t n_q = (N + kBr - 1) / kBr;
     const int64_t grid = B * H * n_q;
     const bool f8 = fp8_scales != nullptr;
@@ -547,7 +553,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
             auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, true> : attn_fwd_kernel<64, NIV, true>;
             hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
-                                  xcd_heads, Op, lse);
+                                  xcd_heads, n_sets > 1 ? 1 : 0, Op, lse);
         } else {
             const auto* Qp = static_cast<const uint16_t*>(q);
             const auto* Kp = static_cast<const uint16_t*>(k);
@@ -555,7 +561,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
             auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, false> : attn_fwd_kernel<64, NIV, false>;
             hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
-                                  xcd_heads, Op, lse);
+                                  xcd_heads, n_sets > 1 ? 1 : 0, Op, lse);
         }
         return hipGetLastError();
     });

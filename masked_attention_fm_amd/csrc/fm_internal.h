@@ -30,14 +30,17 @@ constexpr int kBc = FM_KEY_TILE;
 using TileMeta = int4;
 constexpr int kMaxRanges = 4;
 
-// Interval preprocessor: one wavefront per (b, query block).
-//   col_start/col_end: [B][n_iv][N].
-//   meta[(b*n_q + t) * n_iv + k]; work[b*n_q + t] = non-skip key blocks of the
-//   union (may be null); bad (may be null): set to 1 when a row breaks
-//   0 <= s <= e <= N-1.
+// Work items.  Each batch element holds n_sets interval sets (1: all heads
+// share one set; H: one set per head), col_start/col_end [B][n_sets][n_iv][N].
+// Query block t of set g of batch element b is item (g*B + b)*n_q + t, so the
+// items of one set form a contiguous segment of B*n_q.
+//
+// Interval preprocessor: one wavefront per item.
+//   meta[item * n_iv + k]; work[item] = non-skip key blocks of the union (may
+//   be null); bad (may be null): set to 1 when a row breaks 0 <= s <= e <= N-1.
 hipError_t launch_preprocess(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
                              int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* bad,
-                             hipStream_t stream);
+                             hipStream_t stream, int n_sets = 1);
 
 // Expands meta of n_q query blocks (n_iv ranges each) into the uint8 class
 // table [n_q][n_kv]: SKIP unless some range keeps the block, FULL when some
@@ -45,15 +48,16 @@ hipError_t launch_preprocess(const int32_t* col_start, const int32_t* col_end, i
 hipError_t launch_class_table(const TileMeta* meta, int n_iv, int64_t n_q, int64_t n_kv, uint8_t* table,
                               hipStream_t stream);
 
-// Longest-first order of M work items (ties by index).
-hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream);
+// Longest-first order (ties by index) within each segment of L consecutive
+// items (L = M: one segment): order[seg*L + rank] = item.
+hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L = 0);
 
 // Preprocessor and scheduler in one launch of one workgroup, for at most
 // kPrepSmallMax query blocks (B * n_q): same meta, work and order outputs.
 constexpr int kPrepSmallMax = 256;
 hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
                              int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
-                             hipStream_t stream);
+                             hipStream_t stream, int n_sets = 1);
 
 // Attention kernel.  order == nullptr runs query blocks in natural (b, t) order.
 // start/stop (may be null) are stamped at the kernel's own start and end.
@@ -63,7 +67,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                            const float* fp8_scales = nullptr);
+                            const float* fp8_scales = nullptr, int n_sets = 1);
 
 // Backward pass (gradients of Q, K, V).  Shapes: the key-block kernel runs
 // kBwdKeys keys per workgroup against query chunks of kBwdRows rows; the

@@ -27,18 +27,20 @@ constexpr int kWavesPerBlock = 4;
 template <int NIV>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void preprocess_kernel(
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int n_q,
-    int n_kv, int Br, int Bc, int64_t items, TileMeta* __restrict__ meta,
+    int n_kv, int Br, int Bc, int64_t items, int64_t seg, int n_sets, TileMeta* __restrict__ meta,
     int32_t* __restrict__ work, int32_t* __restrict__ bad) {
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     if (item >= items) return;  // whole wavefront leaves together
-    const int64_t b = item / n_q;
-    const int t = (int)(item - b * n_q);
+    const int64_t g = item / seg;              // interval set
+    const int64_t rem = item - g * seg;
+    const int64_t b = rem / n_q;
+    const int t = (int)(rem - b * n_q);
     TileMeta m[NIV];
     int invalid = 0;
 #pragma unroll
     for (int k = 0; k < NIV; ++k) {
-        const int64_t off = (b * NIV + k) * N;
+        const int64_t off = ((b * n_sets + g) * NIV + k) * N;
         int inv = 0;
         m[k] = query_block_meta(col_start + off, col_end + off, t, N, Br, Bc, n_kv, lane, &inv);
         invalid |= inv;
@@ -79,15 +81,16 @@ __global__ __launch_bounds__(256) void class_table_kernel(const TileMeta* __rest
 
 hipError_t launch_preprocess(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
                              int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* bad,
-                             hipStream_t stream) {
+                             hipStream_t stream, int n_sets) {
     const int64_t n_q = (N + Br - 1) / Br;
     const int64_t n_kv = (N + Bc - 1) / Bc;
-    const int64_t items = B * n_q;
+    const int64_t seg = B * n_q;
+    const int64_t items = n_sets * seg;
     const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     return dispatch_ranges(n_iv, [&](auto niv) {
         hipLaunchKernelGGL(preprocess_kernel<decltype(niv)::value>, dim3((unsigned)blocks),
                            dim3(64 * kWavesPerBlock), 0, stream, col_start, col_end, (int)N, (int)n_q,
-                           (int)n_kv, Br, Bc, items, meta, work, bad);
+                           (int)n_kv, Br, Bc, items, seg, n_sets, meta, work, bad);
         return hipGetLastError();
     });
 }

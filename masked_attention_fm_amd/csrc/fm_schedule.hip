@@ -22,24 +22,34 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __restrict__ work, int M,
+// Items are ranked within their segment of L; a workgroup walks the union of
+// its threads' segments (uniform bounds for the barriers) and each thread
+// counts only its own segment.
+__global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __restrict__ work, int M, int L,
                                                             int32_t* __restrict__ order) {
     __shared__ int s_work[kThreads];
     const int x = blockIdx.x * kThreads + threadIdx.x;
     const int wx = x < M ? work[x] : INT_MIN;
+    const int x_first = blockIdx.x * kThreads;
+    const int x_last = min(M, x_first + kThreads) - 1;
+    const int y_begin = (x_first / L) * L;
+    const int y_end = min(M, (x_last / L + 1) * L);
+    const int my_lo = (x / L) * L;
+    const int my_hi = my_lo + L;
     int rank = 0;
-    for (int base = 0; base < M; base += kThreads) {
+    for (int base = y_begin; base < y_end; base += kThreads) {
         const int y = base + threadIdx.x;
-        s_work[threadIdx.x] = y < M ? work[y] : INT_MIN;
+        s_work[threadIdx.x] = y < y_end ? work[y] : INT_MIN;
         __syncthreads();
-        const int lim = min(kThreads, M - base);
+        const int lim = min(kThreads, y_end - base);
         for (int i = 0; i < lim; ++i) {
             const int wy = s_work[i];
-            rank += (wy > wx) | ((wy == wx) & (base + i < x));
+            const int yy = base + i;
+            rank += (yy >= my_lo) & (yy < my_hi) & ((wy > wx) | ((wy == wx) & (yy < x)));
         }
         __syncthreads();
     }
-    if (x < M) order[rank] = x;
+    if (x < M) order[my_lo + rank] = x;
 }
 
 constexpr int kPrepThreads = 1024;
@@ -54,22 +64,24 @@ constexpr int kPrepThreads = 1024;
 template <int NIV>
 __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int n_q, int n_kv,
-    int Br, int Bc, int M, int G, bool vec4, TileMeta* __restrict__ meta, int32_t* __restrict__ work,
-    int32_t* __restrict__ order) {
+    int Br, int Bc, int M, int G, bool vec4, int n_sets, int L, TileMeta* __restrict__ meta,
+    int32_t* __restrict__ work, int32_t* __restrict__ order) {
     // work of each item, padded with INT_MIN up to G * SL <= M + 4 G <= 2 * kPrepSmallMax entries
     __shared__ __attribute__((aligned(16))) int s_work[2 * kPrepSmallMax];
     const int item = threadIdx.x / G;          // G divides 64: a group never straddles wavefronts
     const int g = threadIdx.x % G;
     if (item < M) {
-        const int b = item / n_q;
-        const int t = item - b * n_q;
+        const int set = item / L;               // interval set (item = (set * B + b) * n_q + t)
+        const int rem = item - set * L;
+        const int b = rem / n_q;
+        const int t = rem - b * n_q;
         const int r0 = t * Br;
         const int r_end = min(r0 + Br, N);
         TileMeta m[NIV];
 #pragma unroll
         for (int k = 0; k < NIV; ++k) {
-            const int32_t* s_row = col_start + ((int64_t)b * NIV + k) * N;
-            const int32_t* e_row = col_end + ((int64_t)b * NIV + k) * N;
+            const int32_t* s_row = col_start + (((int64_t)b * n_sets + set) * NIV + k) * N;
+            const int32_t* e_row = col_end + (((int64_t)b * n_sets + set) * NIV + k) * N;
             RowBounds rb;
             if (vec4) {
                 // rows in 16-byte chunks of four (N and both bases are multiples of 4 rows)
@@ -112,18 +124,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
     __syncthreads();
     if (item < M) {
         const int wx = s_work[item];
+        const int lo = (item / L) * L;          // the item's segment [lo, lo + L)
+        const int hi = lo + L;
         int rank = 0;
         const int4* w4 = reinterpret_cast<const int4*>(s_work + g * SL);
         for (int c = 0; c < SL / 4; ++c) {
             const int4 w = w4[c];
             const int y = g * SL + 4 * c;
-            rank += (w.x > wx) | ((w.x == wx) & (y < item));
-            rank += (w.y > wx) | ((w.y == wx) & (y + 1 < item));
-            rank += (w.z > wx) | ((w.z == wx) & (y + 2 < item));
-            rank += (w.w > wx) | ((w.w == wx) & (y + 3 < item));
+            const int wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                rank += (y + q >= lo) & (y + q < hi) & ((wv[q] > wx) | ((wv[q] == wx) & (y + q < item)));
         }
         for (int off = G >> 1; off > 0; off >>= 1) rank += __shfl_xor(rank, off);
-        if (g == 0) order[rank] = item;
+        if (g == 0) order[lo + rank] = item;
     }
 }
 
@@ -131,10 +145,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
 
 hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
                              int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
-                             hipStream_t stream) {
+                             hipStream_t stream, int n_sets) {
     const int64_t n_q = (N + Br - 1) / Br;
     const int64_t n_kv = (N + Bc - 1) / Bc;
-    const int64_t M = B * n_q;
+    const int64_t L = B * n_q;                  // one segment per interval set
+    const int64_t M = n_sets * L;
     if (M > kPrepSmallMax) return hipErrorInvalidValue;
     int G = 64;                                 // lanes per query block: a power of two, G * M <= 1024
     while (G * M > kPrepThreads) G >>= 1;
@@ -143,16 +158,17 @@ hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, i
                       (reinterpret_cast<uintptr_t>(col_end) & 15) == 0;
     return dispatch_ranges(n_iv, [&](auto niv) {
         hipLaunchKernelGGL(prep_small_kernel<decltype(niv)::value>, dim3(1), dim3(kPrepThreads), 0, stream,
-                           col_start, col_end, (int)N, (int)n_q, (int)n_kv, Br, Bc, (int)M, G, vec4, meta,
-                           work, order);
+                           col_start, col_end, (int)N, (int)n_q, (int)n_kv, Br, Bc, (int)M, G, vec4, n_sets,
+                           (int)L, meta, work, order);
         return hipGetLastError();
     });
 }
 
-hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream) {
+hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L) {
+    if (L <= 0) L = M;
     const int64_t blocks = (M + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, work,
-                       (int)M, order);
+                       (int)M, (int)L, order);
     return hipGetLastError();
 }
 

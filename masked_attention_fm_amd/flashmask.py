@@ -34,6 +34,8 @@ SIGNATURES = {
     "fm_attn_fwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
                                          _P, _P, _P]),
     "fm_classify_tiles_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P]),
+    "fm_attn_fwd_per_head": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                            _P, _P, _P]),
     "fm_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P, _I32,
                                        _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P]),
     "fm_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
@@ -245,6 +247,40 @@ def fm_attn_fwd_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_sta
     _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
     return _attn("fm_attn_fwd_multi", q, k, v, col_start, col_end, col_start.shape[1], scale, out, lse,
                  stream)
+
+
+def fm_attn_fwd_per_head(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: torch.Tensor,
+                         col_end: torch.Tensor, scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fm_attn_fwd with one interval set per head: intervals [B, H, N] or [B, H, K, N]."""
+    B, H, N, d = _qkv(q, k, v)
+    if col_start.dim() == 3:
+        col_start, col_end = col_start.unsqueeze(2), col_end.unsqueeze(2)
+    if col_start.dim() != 4:
+        raise ValueError("col_start / col_end must be [B, H, N] or [B, H, K, N]")
+    _intervals(col_start, col_end, (B, H, col_start.shape[2], N), "[B, H, K, N]")
+    if not (col_start.is_contiguous() and col_end.is_contiguous()):
+        raise ValueError("col_start / col_end must be contiguous")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor(out, "out", torch.bfloat16)
+        if out.shape != q.shape:
+            raise ValueError("out must match q's shape")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _dev_tensor(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be [B, H, N]")
+    status = lib().fm_attn_fwd_per_head(q.data_ptr(), k.data_ptr(), v.data_ptr(), col_start.data_ptr(),
+                                        col_end.data_ptr(), col_start.shape[2], B, H, N, d, float(scale),
+                                        out.data_ptr(), lse.data_ptr(), _stream_handle(stream))
+    _check("fm_attn_fwd_per_head", status)
+    return out, lse
 
 
 def fm_attn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float, k_scale: float,

@@ -228,3 +228,11 @@ def test_attn_fwd_fp8_rejects_bad_arguments(L):
                              None) == fmb.FM_ERR_UNSUPPORTED
     assert L.fm_attn_fwd_fp8(FAKE + 8, FAKE, FAKE, *ok, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
                              None) == fmb.FM_ERR_INVALID_ARG
+
+
+def test_attn_fwd_per_head_rejects_bad_arguments(L):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert L.fm_attn_fwd_per_head(*args, 0, 1, 2, 128, 128, 0.125, FAKE, FAKE, None) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_attn_fwd_per_head(*args, 1, 1, 2, 128, 96, 0.125, FAKE, FAKE, None) == fmb.FM_ERR_UNSUPPORTED
+    assert L.fm_attn_fwd_per_head(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 2, 128, 128, 0.125, FAKE, FAKE,
+                                  None) == fmb.FM_ERR_INVALID_ARG
