@@ -133,10 +133,12 @@ FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v,
                              void* out, float* lse, hipStream_t stream);
 
 /*
- * fm_attn_fwd_per_head -- fm_attn_fwd_multi with one interval set per head
- * (the FlashMask article's §3.4 and §6.1 item 3: masks that differ across
- * heads and layers, e.g. a different window per head; layers simply pass
- * their own intervals).  col_start, col_end are int32 [B][H][n_ranges][N]
+ * fm_attn_fwd_per_head -- fm_attn_fwd_multi with one interval set per head.
+ * The FlashMask article varies the mask across layers (§3.4 item 1, a window
+ * size per layer; §6.1 item 3, a mask kind per layer), which needs no
+ * interface: each layer's call passes its own intervals.  This call carries
+ * the same idea inside one layer, across heads (e.g. a different window per
+ * head).  col_start, col_end are int32 [B][H][n_ranges][N]
  * device: range k of row r of head h of batch b is element
  * ((b*H + h)*n_ranges + k)*N + r.  With every head's set equal, the results
  * are bit-identical to fm_attn_fwd_multi's.  Other arguments, asynchrony and
