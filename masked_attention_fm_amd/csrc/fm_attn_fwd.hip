@@ -418,6 +418,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                             st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
                         }
                     }
+                    // Keep the LDS operand reads kAhead ahead of the MFMA that
+                    // consumes them (the default schedule reads two ahead and
+                    // waits on LDS latency before most MFMAs).  Groups: kAhead
+                    // reads, then alternately one MFMA and one read, then the
+                    // last kAhead MFMAs.
+                    constexpr int kMfmas = (D / 16) * (kBc / 32);
+                    constexpr int kAhead = kMfmas >= 12 ? 6 : kMfmas / 2;
+                    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);     // DS reads
+#pragma unroll
+                    for (int i = 0; i < kMfmas - kAhead; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
                 }
 
                 // ---- interval compare, only where some row of the wavefront
