@@ -369,3 +369,20 @@ def test_kernel_timer_counts_launches():
     finally:
         fm.fm_profile_enable(False)
     assert n == 3 and ms > 0
+
+
+def test_maximum_sequence_length():
+    """N = 2^22, the largest length the C ABI accepts (32-bit byte offsets within one
+    (b, h) slice): a 256-key window plus a few document-style rows; sampled rows,
+    including the last ones, against the oracle."""
+    B, H, N, d = 1, 1, 1 << 22, 64
+    s, e = inputs.sliding_window_intervals(N, 256)
+    s = s.copy()
+    s[N - 5:] = N - 5                      # a short final segment
+    s, e = s[None], e[None]
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=77)
+    rng = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, N // 2, N - 6, N - 5, N - 2, N - 1],
+                                     rng.integers(0, N, 200)]))
+    log("maximum length N=2^22")
+    check_case(q, k, v, s, e, inputs.default_scale(d), "N=2^22", rows=rows)
