@@ -87,8 +87,8 @@ FM_API int fm_classify_tiles(const int32_t* col_start, const int32_t* col_end, i
  *   lse       : float32  [B][H][N] device, natural log.
  *   stream    : HIP stream the work is queued on (0 = null stream).
  *
- * Asynchronous on `stream`: returns once the three kernels (interval
- * preprocessor, scheduler, attention) are queued.  Inputs must not alias the
+ * Asynchronous on `stream`: returns once its kernels (interval preprocessing
+ * and work ordering, then attention) are queued.  Inputs must not alias the
  * outputs.  The library keeps a small internal workspace per (device, stream),
  * grown in stream order; the call never synchronizes the device.
  * Errors: argument checks happen on the host before any HIP call

@@ -23,11 +23,28 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCES = [os.path.join(PKG, "csrc", name) for name in ("fm_attn_fwd.hip", "fm_internal.h", "fm_mfma.h")]
 
 
-def attn_source_hash() -> str:
+def code_text(text: str) -> str:
+    """Source text without // comments, blank lines and indentation: two sources with the
+    same code and different comments give the same text."""
+    lines = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].strip()
+        if code:
+            lines.append(" ".join(code.split()))
+    return "\n".join(lines)
+
+
+def attn_source_hash(sources=None) -> str:
+    """sha256 (first 16 hex) over the code of the attention kernel's sources (comments
+    and whitespace ignored).  `sources`: texts to hash instead of the files."""
     h = hashlib.sha256()
-    for path in ATTN_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    if sources is None:
+        sources = []
+        for path in ATTN_SOURCES:
+            with open(path, encoding="utf-8") as f:
+                sources.append(f.read())
+    for text in sources:
+        h.update(code_text(text).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

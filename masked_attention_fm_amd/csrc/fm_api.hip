@@ -42,10 +42,12 @@ int g_schedule_mode = 0;   // 0 longest first, 1 natural order
 
 // ---------------------------------------------------------------- workspace
 //
-// fm_attn_fwd needs per query block: 16 B of tile metadata, its work count
-// and its place in the launch order.  One buffer per (device, stream) is
-// kept and grown in stream order, so back-to-back calls on a stream reuse it
-// and calls on different streams never share it.
+// The forward calls need, per query block, 16 B of tile metadata per range,
+// a work count and a place in the launch order; the backward adds the same
+// for its query chunks and key blocks and one float per row and head.  One
+// buffer per (device, stream) is kept and grown in stream order, so
+// back-to-back calls on a stream reuse it and calls on different streams
+// never share it.  It lives until the process ends.
 
 struct Workspace {
     void* ptr = nullptr;

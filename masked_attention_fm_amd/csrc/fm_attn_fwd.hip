@@ -38,6 +38,11 @@
 //     is skipped or full for a wavefront by the per-range tests above, and
 //     the compare keeps a key that lies in any of the row's ranges.  With
 //     NIV = 1 this is the single-range kernel.
+//   * A second instantiation (F8) takes e4m3 Q, K, V: the score product runs
+//     on the FP8 matrix instruction and V is widened to bf16 as it is staged
+//     (see the FP8 section below).
+//   * With one interval set per head, head h reads set h; the work items of
+//     each set are a contiguous, separately ranked segment of the order.
 
 #include <hip/hip_ext.h>
 #include <math.h>

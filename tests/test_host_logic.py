@@ -80,3 +80,11 @@ def test_counter_summary_calibrates_with_the_copy(tmp_path):
     assert rec["hbm_write_bytes_per_launch"] == pytest.approx(1024 * 300)
     assert rec["mfma_busy_per_cu_busy"] == pytest.approx(0.5)
     assert rec["attn_source_sha256_16"] == counters.attn_source_hash()
+
+
+def test_code_hash_ignores_comments_and_whitespace():
+    a = "int f(int x) {  // doubles\n    return 2 * x;\n}\n"
+    b = "// f: twice x\nint f(int x) {\n\n  return 2 * x;   // twice\n}\n"
+    c = "int f(int x) {\n    return 3 * x;\n}\n"
+    assert counters.attn_source_hash([a]) == counters.attn_source_hash([b])
+    assert counters.attn_source_hash([a]) != counters.attn_source_hash([c])
