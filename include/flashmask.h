@@ -229,6 +229,13 @@ FM_API int fm_attn_bwd_multi(const void* q, const void* k, const void* v, const 
                              int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                              float* dq, float* dk, float* dv, hipStream_t stream);
 
+/* fm_attn_bwd for one interval set per head ([B][H][n_ranges][N] intervals, as
+ * fm_attn_fwd_per_head, whose out and lse it takes). */
+FM_API int fm_attn_bwd_per_head(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, const int32_t* col_start, const int32_t* col_end,
+                                int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                float* dq, float* dk, float* dv, hipStream_t stream);
+
 /* The query and key block sizes the attention kernel uses for head dimension d
  * (the shape at which tiles are skipped).  FM_ERR_UNSUPPORTED for other d. */
 FM_API int fm_attn_tile_shape(int64_t d, int32_t* Br, int32_t* Bc);

@@ -314,10 +314,14 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
     return fm_attn_fwd_multi(q, k, v, col_start, col_end, 1, B, H, N, d, scale, out, lse, stream);
 }
 
-FM_API int fm_attn_bwd_multi(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                             const float* lse, const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
-                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, float* dq, float* dk,
-                             float* dv, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward pass; per_head: one interval set per head ([B][H][n_ranges][N]).
+int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  const int32_t* col_start, const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
+                  int64_t d, float scale, float* dq, float* dk, float* dv, hipStream_t stream, bool per_head) {
     // ---- host-side checks, before any HIP call
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
         col_start == nullptr || col_end == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
@@ -333,10 +337,12 @@ FM_API int fm_attn_bwd_multi(const void* q, const void* k, const void* v, const 
     const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
     const int64_t n_qc = (N + fm::kBwdRows - 1) / fm::kBwdRows;
     const int64_t n_kb = (N + fm::kBwdKeys - 1) / fm::kBwdKeys;
-    if (B * H * n_qc >= (int64_t(1) << 31) || B * n_ranges * N >= (int64_t(1) << 40)) return FM_ERR_INVALID_ARG;
+    const int64_t n_sets = per_head ? H : 1;   // interval sets per batch element
+    if (B * H * n_qc >= (int64_t(1) << 31) || B * n_sets * n_ranges * N >= (int64_t(1) << 40))
+        return FM_ERR_INVALID_ARG;
 
     // ---- workspace: meta_q[Mq][n] | work_q | order_q | meta_c[Mc][n] | kvr[Mk] | work_k | order_k | D[B H N]
-    const int64_t Mq = B * n_q, Mc = B * n_qc, Mk = B * n_kb;
+    const int64_t Mq = n_sets * B * n_q, Mc = n_sets * B * n_qc, Mk = n_sets * B * n_kb;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t o_work_q = al((size_t)(Mq * n_ranges) * sizeof(fm::TileMeta));
     const size_t o_order_q = o_work_q + al((size_t)Mq * 4);
@@ -362,23 +368,44 @@ FM_API int fm_attn_bwd_multi(const void* q, const void* k, const void* v, const 
     // dQ: the forward's query blocks, key blocks and longest-first order
     if (Mq <= fm::kPrepSmallMax) {
         FM_HIP(fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, order_q,
-                                     stream));
+                                     stream, (int)n_sets));
     } else {
         FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, nullptr,
-                                     stream));
-        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream));
+                                     stream, (int)n_sets));
+        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q));
     }
-    // dK, dV: query chunks per key block, key blocks longest first
+    // dK, dV: query chunks per key block, key blocks longest first (within each set)
     FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBwdRows, fm::kBwdKeys, meta_c, nullptr,
-                                 nullptr, stream));
-    FM_HIP(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream));
-    FM_HIP(fm::launch_schedule(work_k, Mk, order_k, stream));
+                                 nullptr, stream, (int)n_sets));
+    FM_HIP(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream, (int)n_sets));
+    FM_HIP(fm::launch_schedule(work_k, Mk, order_k, stream, B * n_kb));
     FM_HIP(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, kvr, order_k, B, H, N,
-                               d, scale, dk, dv, stream));
+                               d, scale, dk, dv, stream, (int)n_sets));
     FM_HIP(fm::launch_bwd_dq(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_q, order_q, B, H, N, d,
-                             scale, dq, stream));
+                             scale, dq, stream, (int)n_sets));
     return FM_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+FM_API int fm_attn_bwd_multi(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, float* dq, float* dk,
+                             float* dv, hipStream_t stream) {
+    return attn_bwd_impl(q, k, v, out, dout, lse, col_start, col_end, n_ranges, B, H, N, d, scale, dq, dk, dv, stream,
+                         false);
+}
+
+FM_API int fm_attn_bwd_per_head(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, const int32_t* col_start, const int32_t* col_end,
+                                int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                float* dq, float* dk, float* dv, hipStream_t stream) {
+    return attn_bwd_impl(q, k, v, out, dout, lse, col_start, col_end, n_ranges, B, H, N, d, scale, dq, dk, dv, stream,
+                         true);
+}
+
 
 FM_API int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                        const float* lse, const int32_t* col_start, const int32_t* col_end, int64_t B, int64_t H,

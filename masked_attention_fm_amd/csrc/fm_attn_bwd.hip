@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
 
 // ---------------------------------------------------------------- query chunks per key block
 
-// One wavefront per (b, J): lanes scan the query chunks t = lane, lane + 64, ...
+// One wavefront per key-block item (set*B + b)*n_kb + J: lanes scan the query
+// chunks t = lane, lane + 64, ... of the same set and batch element, whose
+// records are rows (set*B + b)*n_qc + t.
 template <int NIV>
 __global__ __launch_bounds__(256) void kv_ranges_kernel(const TileMeta* __restrict__ meta_c, int n_qc, int n_kb,
                                                         int64_t items, int4* __restrict__ kvr,
@@ -73,14 +75,14 @@ __global__ __launch_bounds__(256) void kv_ranges_kernel(const TileMeta* __restri
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= items) return;                 // whole wavefront leaves together
-    const int64_t b = item / n_kb;
-    const int J = (int)(item - b * n_kb);
+    const int64_t sb = item / n_kb;            // set * B + b
+    const int J = (int)(item - sb * n_kb);
     int lo = INT_MAX, hi = INT_MIN, count = 0;
     for (int t = lane; t < n_qc; t += 64) {
         bool live = false;
 #pragma unroll
         for (int k = 0; k < NIV; ++k) {
-            const TileMeta m = meta_c[((int64_t)b * n_qc + t) * NIV + k];
+            const TileMeta m = meta_c[(sb * n_qc + t) * NIV + k];
             live |= m.x <= J && J <= m.y;
         }
         if (live) {
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
     const TileMeta* __restrict__ meta_c, const int4* __restrict__ kvr, const int32_t* __restrict__ order, int H,
-    int N, int n_qc, int n_kb, float c, float scale, int xcd_heads, float* __restrict__ dK,
+    int N, int n_qc, int n_kb, float c, float scale, int xcd_heads, int per_head, float* __restrict__ dK,
     float* __restrict__ dV) {
     __shared__ DkvSmem<D, NIV> sm;
     const int tid = threadIdx.x;
@@ -241,9 +243,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
     int h, slot;
     slot_to_item(xcd_heads, H, h, slot);
-    const int bj = order[slot];
-    const int b = bj / n_kb;
-    const int J = bj - b * n_kb;
+    // With one interval set per head, head h reads set h: its key-block items
+    // are the segment [h L, h L + L) of the records and of the order.
+    const int L = gridDim.x / H;                 // key blocks per head (B n_kb)
+    const int set = per_head ? h : 0;
+    const int n_sets = per_head ? H : 1;
+    const int bj = order[set * L + slot];
+    const int local = bj - set * L;
+    const int b = local / n_kb;
+    const int J = local - b * n_kb;
     const int4 range = kvr[bj];                 // {first chunk, last chunk, live chunks}
 
     const int64_t bh = (int64_t)b * H + h;
@@ -273,9 +281,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const __amdgpu_buffer_rsrc_t grs = slice_rsrc(dO + bh * N * D, N * D * 2);
     const float* lse_bh = LSE + bh * N;
     const float* dd_bh = Dd + bh * N;
-    const int32_t* cs_b = col_start + (int64_t)b * NIV * N;
-    const int32_t* ce_b = col_end + (int64_t)b * NIV * N;
-    const int64_t meta_row = (int64_t)b * n_qc;
+    const int32_t* cs_b = col_start + ((int64_t)b * n_sets + set) * NIV * N;
+    const int32_t* ce_b = col_end + ((int64_t)b * n_sets + set) * NIV * N;
+    const int64_t meta_row = ((int64_t)set * (L / n_kb) + b) * n_qc;
 
     int t = range.z > 0 ? range.x : INT_MAX;
     if (t != INT_MAX) {
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, const TileMeta* __restrict__ meta,
-    const int32_t* __restrict__ order, int H, int N, int n_q, float c, float scale, int xcd_heads,
+    const int32_t* __restrict__ order, int H, int N, int n_q, float c, float scale, int xcd_heads, int per_head,
     float* __restrict__ dQ) {
     __shared__ DqSmem<D, NIV> sm;
     const int tid = threadIdx.x;
@@ -463,9 +471,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 
     int h, slot;
     slot_to_item(xcd_heads, H, h, slot);
-    const int bt = order != nullptr ? order[slot] : slot;
-    const int b = bt / n_q;
-    const int t = bt - b * n_q;
+    const int L = gridDim.x / H;                 // query blocks per head (B n_q)
+    const int set = per_head ? h : 0;
+    const int n_sets = per_head ? H : 1;
+    const int bt = order != nullptr ? order[set * L + slot] : set * L + slot;
+    const int local = bt - set * L;
+    const int b = local / n_q;
+    const int t = local - b * n_q;
     TileMeta tm[NIV];
 #pragma unroll
     for (int k = 0; k < NIV; ++k) tm[k] = meta[(int64_t)bt * NIV + k];
@@ -480,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         for (int k = 0; k < NIV; ++k) {
             int2 iv = make_int2(kEmptyStart, 0);
             if (r < N) {
-                const int64_t at = ((int64_t)b * NIV + k) * N + r;
+                const int64_t at = (((int64_t)b * n_sets + set) * NIV + k) * N + r;
                 iv = clamp_interval(col_start[at], col_end[at], N);
             }
             sm.start[k][tid] = iv.x;
@@ -628,10 +640,10 @@ hipError_t launch_bwd_rowdot(const void* out, const void* dout, int64_t rows, in
 }
 
 hipError_t launch_kv_ranges(const TileMeta* meta_c, int n_iv, int64_t B, int64_t N, int4* kvr, int32_t* work,
-                            hipStream_t stream) {
+                            hipStream_t stream, int n_sets) {
     const int64_t n_qc = (N + kBwdRows - 1) / kBwdRows;
     const int64_t n_kb = (N + kBwdKeys - 1) / kBwdKeys;
-    const int64_t items = B * n_kb;
+    const int64_t items = n_sets * B * n_kb;
     const int64_t blocks = (items + 3) / 4;
     return dispatch_ranges(n_iv, [&](auto niv) {
         hipLaunchKernelGGL(kv_ranges_kernel<decltype(niv)::value>, dim3((unsigned)blocks), dim3(256), 0, stream,
@@ -643,7 +655,8 @@ hipError_t launch_kv_ranges(const TileMeta* meta_c, int n_iv, int64_t B, int64_t
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
                            const TileMeta* meta_c, const int4* kvr, const int32_t* order, int64_t B, int64_t H,
-                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream) {
+                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream,
+                           int n_sets) {
     const int64_t n_qc = (N + kBwdRows - 1) / kBwdRows;
     const int64_t n_kb = (N + kBwdKeys - 1) / kBwdKeys;
     const int64_t grid = B * H * n_kb;
@@ -655,7 +668,8 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                            static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), lse, dd, col_start,
-                           col_end, meta_c, kvr, order, (int)H, (int)N, (int)n_qc, (int)n_kb, c, scale, xcd, dk, dv);
+                           col_end, meta_c, kvr, order, (int)H, (int)N, (int)n_qc, (int)n_kb, c, scale, xcd,
+                           n_sets > 1 ? 1 : 0, dk, dv);
         return hipGetLastError();
     });
 }
@@ -663,7 +677,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
                          const TileMeta* meta, const int32_t* order, int64_t B, int64_t H, int64_t N, int64_t d,
-                         float scale, float* dq, hipStream_t stream) {
+                         float scale, float* dq, hipStream_t stream, int n_sets) {
     const int64_t n_q = (N + kBr - 1) / kBr;
     const int64_t grid = B * H * n_q;
     const int xcd = use_xcd_heads(H, B * n_q);
@@ -674,7 +688,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                            static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), lse, dd, col_start,
-                           col_end, meta, order, (int)H, (int)N, (int)n_q, c, scale, xcd, dq);
+                           col_end, meta, order, (int)H, (int)N, (int)n_q, c, scale, xcd, n_sets > 1 ? 1 : 0, dq);
         return hipGetLastError();
     });
 }

@@ -79,22 +79,23 @@ constexpr int kBwdKeys = 128;
 hipError_t launch_bwd_rowdot(const void* out, const void* dout, int64_t rows, int64_t d, float* dd,
                              hipStream_t stream);
 
-// For each (b, key block J of kBwdKeys keys): the first and last query chunk
-// (kBwdRows rows, records meta_c from launch_preprocess with that shape) whose
-// non-skip ranges hold J, and their count: kvr[b*n_kb + J] = {t_lo, t_hi, count, 0},
-// work[b*n_kb + J] = count.
+// For each key-block item (set*B + b)*n_kb + J (blocks of kBwdKeys keys): the
+// first and last query chunk (kBwdRows rows, records meta_c from
+// launch_preprocess with that shape and the same n_sets) whose non-skip ranges
+// hold J, and their count: kvr[item] = {t_lo, t_hi, count, 0}, work[item] = count.
 hipError_t launch_kv_ranges(const TileMeta* meta_c, int n_iv, int64_t B, int64_t N, int4* kvr, int32_t* work,
-                            hipStream_t stream);
+                            hipStream_t stream, int n_sets = 1);
 
 // The two gradient kernels (see fm_attn_bwd.hip).
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
                            const TileMeta* meta_c, const int4* kvr, const int32_t* order, int64_t B, int64_t H,
-                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream);
+                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream,
+                           int n_sets = 1);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
                          const TileMeta* meta, const int32_t* order, int64_t B, int64_t H, int64_t N, int64_t d,
-                         float scale, float* dq, hipStream_t stream);
+                         float scale, float* dq, hipStream_t stream, int n_sets = 1);
 
 // ---------------------------------------------------------------- wavefront helpers
 

@@ -40,6 +40,8 @@ SIGNATURES = {
                                        _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P]),
     "fm_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                    _P, _P, _P, _P]),
+    "fm_attn_bwd_per_head": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64,
+                                            ctypes.c_float, _P, _P, _P, _P]),
     "fm_attn_bwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64,
                                          ctypes.c_float, _P, _P, _P, _P]),
     "fm_tile_schedule_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P]),
@@ -352,12 +354,13 @@ def _bwd(func: str, q, k, v, out, dout, lse, col_start, col_end, n_ranges: Optio
     dq, dk, dv = grads
     L = lib()
     ptrs = [x.data_ptr() for x in (q, k, v, out, dout, lse, col_start, col_end)]
+    tail = (B, H, N, d, float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream_handle(stream))
     if n_ranges is None:
-        status = L.fm_attn_bwd(*ptrs, B, H, N, d, float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                               _stream_handle(stream))
+        status = L.fm_attn_bwd(*ptrs, *tail)
+    elif func == "fm_attn_bwd_per_head":
+        status = L.fm_attn_bwd_per_head(*ptrs, n_ranges, *tail)
     else:
-        status = L.fm_attn_bwd_multi(*ptrs, n_ranges, B, H, N, d, float(scale), dq.data_ptr(), dk.data_ptr(),
-                                     dv.data_ptr(), _stream_handle(stream))
+        status = L.fm_attn_bwd_multi(*ptrs, n_ranges, *tail)
     _check(func, status)
     return dq, dk, dv
 
@@ -383,6 +386,21 @@ def fm_attn_bwd_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: to
         raise ValueError("col_start / col_end must be [B, K, N]")
     _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
     return _bwd("fm_attn_bwd_multi", q, k, v, out, dout, lse, col_start, col_end, col_start.shape[1], scale,
+                dq, dk, dv, stream)
+
+
+def fm_attn_bwd_per_head(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                         dout: torch.Tensor, lse: torch.Tensor, col_start: torch.Tensor, col_end: torch.Tensor,
+                         scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+                         dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None, stream=None):
+    """fm_attn_bwd for one interval set per head: intervals [B, H, N] or [B, H, K, N]."""
+    B, H, N, d = _qkv(q, k, v)
+    if col_start.dim() == 3:
+        col_start, col_end = col_start.unsqueeze(2).contiguous(), col_end.unsqueeze(2).contiguous()
+    if col_start.dim() != 4:
+        raise ValueError("col_start / col_end must be [B, H, N] or [B, H, K, N]")
+    _intervals(col_start, col_end, (B, H, col_start.shape[2], N), "[B, H, K, N]")
+    return _bwd("fm_attn_bwd_per_head", q, k, v, out, dout, lse, col_start, col_end, col_start.shape[2], scale,
                 dq, dk, dv, stream)
 
 

@@ -236,3 +236,12 @@ def test_attn_fwd_per_head_rejects_bad_arguments(L):
     assert L.fm_attn_fwd_per_head(*args, 1, 1, 2, 128, 96, 0.125, FAKE, FAKE, None) == fmb.FM_ERR_UNSUPPORTED
     assert L.fm_attn_fwd_per_head(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 2, 128, 128, 0.125, FAKE, FAKE,
                                   None) == fmb.FM_ERR_INVALID_ARG
+
+
+def test_attn_bwd_per_head_rejects_bad_arguments(L):
+    head = [FAKE] * 8
+    tail = [1, 2, 128, 128, 0.125, FAKE, FAKE, FAKE, None]
+    assert L.fm_attn_bwd_per_head(*head, 0, *tail) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_attn_bwd_per_head(None, *head[1:], 1, *tail) == fmb.FM_ERR_INVALID_ARG
+    bad_d = [1, 2, 128, 80, 0.125, FAKE, FAKE, FAKE, None]
+    assert L.fm_attn_bwd_per_head(*head, 1, *bad_d) == fmb.FM_ERR_UNSUPPORTED

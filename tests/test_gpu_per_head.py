@@ -8,6 +8,7 @@ import oracle
 from masked_attention_fm_amd import flashmask as fm
 from masked_attention_fm_amd import inputs
 
+from test_gpu_bwd import GRAD_TOL, compare_grads, dout_for
 from test_gpu_parity import DEV, compare, log, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -85,3 +86,40 @@ def test_per_head_equal_sets_match_shared(H, N):
     o2, l2 = fm.fm_attn_fwd_per_head(q, k, v, sh, eh)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 3, 600, 128), (2, 8, 4096, 64)])
+def test_per_head_backward(B, H, N, d):
+    """Gradients with a different window per head against the oracle head by head;
+    (2, 8, 4096) takes the preprocessor + ranked-segment paths."""
+    s, e = window_per_head(B, H, N, [32, 300, 1, 1000, 64, 2048, 7, 4096])
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=N + 5)
+    do = dout_for(q.shape, N)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    sd, ed = to_dev(s, e)
+    out, lse = fm.fm_attn_fwd_per_head(qd, kd, vd, sd, ed)
+    dq, dk, dv = fm.fm_attn_bwd_per_head(qd, kd, vd, out, dod, lse, sd, ed)
+    torch.cuda.synchronize()
+    got = [g.cpu().numpy().astype(np.float64) for g in (dq, dk, dv)]
+    qf, kf, vf, dof = (x.float().numpy() for x in (q, k, v, do))
+    log(f"per-head backward B={B} H={H} N={N} d={d}")
+    for h in range(H):
+        ref = oracle.attention_bwd(qf[:, h:h + 1], kf[:, h:h + 1], vf[:, h:h + 1], dof[:, h:h + 1], s[:, h], e[:, h],
+                                   inputs.default_scale(d))
+        compare_grads([g[:, h:h + 1] for g in got], ref, f"per-head bwd h={h}")
+
+
+def test_per_head_backward_equal_sets_match_shared():
+    B, H, N, d = 1, 4, 1500, 128
+    spec = inputs.make_intervals("doc_uniform", B, N, 11, lo=100, hi=700)
+    q, k, v = to_dev(*inputs.make_qkv(B, H, N, d, seed=11))
+    do = to_dev(dout_for((B, H, N, d), 11))[0]
+    sd, ed = to_dev(spec.col_start, spec.col_end)
+    out, lse = fm.fm_attn_fwd(q, k, v, sd, ed)
+    g1 = fm.fm_attn_bwd(q, k, v, out, do, lse, sd, ed)
+    sh = sd[:, None, None].expand(B, H, 1, N).contiguous()
+    eh = ed[:, None, None].expand(B, H, 1, N).contiguous()
+    g2 = fm.fm_attn_bwd_per_head(q, k, v, out, do, lse, sh, eh)
+    torch.cuda.synchronize()
+    for a, b_ in zip(g1, g2):
+        assert torch.equal(a, b_)
