@@ -10,7 +10,8 @@ pair, the attention kernel's roofline figures (its own duration measured with
 HIP events the library records on its stream), the other workloads' figures
 under "per_config", the backward pass (fm_attn_bwd, 10*d FLOPs per attended
 pair) under "backward", the FP8-input forward (fm_attn_fwd_fp8) under
-"fp8_forward", and the CPU oracle timed on a bounded sample.
+"fp8_forward" (bf16 weights) and "fp8_all_forward" (e4m3 weights), and the CPU
+oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -187,9 +188,9 @@ def time_backward(cfg, steps, warmup):
     return {"ms_per_step": ms, "effective_flops": flops, "effective_tflops": flops / (ms * 1e-3) / 1e12}
 
 
-def time_fp8(cfg, steps, warmup):
-    """fm_attn_fwd_fp8 steps on the workload's draws quantized per tensor to e4m3 (inputs
-    resident); same 4 d FLOPs per attended pair as the bf16 forward."""
+def time_fp8(cfg, steps, warmup, mode):
+    """fm_attn_fwd_fp8 steps in the given mode on the workload's draws quantized per tensor
+    to e4m3 (inputs resident); same 4 d FLOPs per attended pair as the bf16 forward."""
     import torch
     from masked_attention_fm_amd import flashmask as fm
     from masked_attention_fm_amd import inputs, metrics
@@ -205,13 +206,13 @@ def time_fp8(cfg, steps, warmup):
     scale = inputs.default_scale(cfg.d)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream)
+        fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream, mode=mode)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(steps):
-        fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream)
+        fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream, mode=mode)
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
@@ -318,15 +319,18 @@ def main():
             log(f"{key} backward: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
             backward[key] = r
 
-    fp8 = {}
+    fp8, fp8_all = {}, {}
     if not args.no_fp8:
         for key, c in inputs.CONFIGS.items():
             if key != cfg.key and args.no_per_config:
                 continue
             steps = 200 if c.N <= 1024 else max(5, min(args.steps, 20))
-            r = time_fp8(c, steps, min(args.warmup, 5))
+            r = time_fp8(c, steps, min(args.warmup, 5), fm.FM_FP8_SCORES)
             log(f"{key} fp8: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
             fp8[key] = r
+            r = time_fp8(c, steps, min(args.warmup, 5), fm.FM_FP8_ALL)
+            log(f"{key} fp8 weights: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
+            fp8_all[key] = r
 
     if args.copy_mib:
         n = args.copy_mib << 20
@@ -385,6 +389,7 @@ def main():
         "per_config": per_config,
         "backward": backward,
         "fp8_forward": fp8,
+        "fp8_all_forward": fp8_all,
     }
     print(json.dumps(line), flush=True)
 

@@ -152,22 +152,31 @@ FM_API int fm_attn_fwd_per_head(const void* q, const void* k, const void* v,
 /*
  * fm_attn_fwd_fp8 -- the forward pass on FP8 inputs.  The FlashMask article
  * names an FP8 mode of its H100 path (§4.2) without saying which products run
- * in FP8.  Reading used here: Q, K and V are stored as OCP FP8 e4m3 (the
+ * in FP8.  Readings used here: Q, K and V are stored as OCP FP8 e4m3 (the
  * "e4m3fn" encoding: bias 7, no infinities, 0x7F/0xFF NaN) with one
  * dequantization scale per tensor (the real value of a code x is
  * scale * e4m3(x)); the score product Q K^T runs on the FP8 matrix units with
- * fp32 accumulation; V is widened exactly to bf16 and the weights and the
- * P V product stay bf16, as in fm_attn_fwd.  The result is therefore
- * fm_attn_fwd's result for the dequantized inputs, to the same accuracy.
+ * fp32 accumulation.  Then, by mode:
+ *   FM_FP8_SCORES -- V is widened exactly to bf16 and the weights and the P V
+ *     product stay bf16, as in fm_attn_fwd: the result is fm_attn_fwd's for
+ *     the dequantized inputs, to the same accuracy.
+ *   FM_FP8_ALL -- the P V product runs on the FP8 units as well: each weight
+ *     (its row's running maximum subtracted, times 2^8) is rounded to e4m3
+ *     (nearest even; relative error <= 2^-4 above 2^-14 of the row maximum)
+ *     and the output divides by the sum of the rounded weights.  LSE stays
+ *     the fp32 weights' (identical in both modes).
  *
  *   q8, k8, v8 : uint8 (e4m3) [B][H][N][d] device, contiguous, 16-byte aligned.
  *   q_scale, k_scale, v_scale : dequantization scales, finite and > 0.
+ *   mode : FM_FP8_SCORES or FM_FP8_ALL.
  *   col_start, col_end, n_ranges : as fm_attn_fwd_multi ([B][n_ranges][N]).
  *   B, H, N, d, scale, out, lse, stream : as fm_attn_fwd (out is bfloat16).
- * Errors as fm_attn_fwd_multi; FM_ERR_INVALID_ARG for a bad scale.
+ * Errors as fm_attn_fwd_multi; FM_ERR_INVALID_ARG for a bad scale or mode.
  */
+#define FM_FP8_SCORES 0
+#define FM_FP8_ALL 1
 FM_API int fm_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
-                           float q_scale, float k_scale, float v_scale,
+                           float q_scale, float k_scale, float v_scale, int32_t mode,
                            const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
                            int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                            void* out, float* lse, hipStream_t stream);

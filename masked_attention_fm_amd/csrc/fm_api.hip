@@ -219,10 +219,10 @@ FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, in
 namespace {
 
 // The forward pass for bf16 inputs (fp8_scales == nullptr) or e4m3 inputs with
-// their three dequantization scales.
+// their three dequantization scales (and, with fp8_weights, e4m3 weights).
 int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* col_start, const int32_t* col_end,
                   int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
-                  hipStream_t stream, const float* fp8_scales, bool per_head = false) {
+                  hipStream_t stream, const float* fp8_scales, bool per_head = false, bool fp8_weights = false) {
     // ---- host-side checks, before any HIP call
     if (q == nullptr || k == nullptr || v == nullptr || col_start == nullptr || col_end == nullptr ||
         out == nullptr || lse == nullptr)
@@ -274,7 +274,8 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* co
         }
     }
     FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, n_ranges, meta, natural ? nullptr : order, B, H,
-                                N, d, scale, out, lse, stream, ev.first, ev.second, fp8_scales, (int)n_sets));
+                                N, d, scale, out, lse, stream, ev.first, ev.second, fp8_scales, (int)n_sets,
+                                fp8_weights));
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
         g_timing.pending.push_back(ev);
@@ -299,13 +300,15 @@ FM_API int fm_attn_fwd_per_head(const void* q, const void* k, const void* v, con
 }
 
 FM_API int fm_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_scale, float k_scale,
-                           float v_scale, const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
-                           int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
-                           hipStream_t stream) {
+                           float v_scale, int32_t mode, const int32_t* col_start, const int32_t* col_end,
+                           int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
+                           float* lse, hipStream_t stream) {
     const float scales[3] = {q_scale, k_scale, v_scale};
     for (float x : scales)
         if (!(x > 0.f) || !isfinite(x)) return FM_ERR_INVALID_ARG;
-    return attn_fwd_impl(q8, k8, v8, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, scales);
+    if (mode != FM_FP8_SCORES && mode != FM_FP8_ALL) return FM_ERR_INVALID_ARG;
+    return attn_fwd_impl(q8, k8, v8, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, scales,
+                         false, mode == FM_FP8_ALL);
 }
 
 FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_t* col_start,

@@ -216,8 +216,70 @@ __device__ __forceinline__ void store_block8(const Staging8<D>& st, Smem8<D, NIV
     }
 }
 
-// Types of one instantiation: bf16 inputs, or e4m3 inputs (F8).
-template <int D, int NIV, bool F8>
+// ---- e4m3 weights (PREC 2): the PV product on the FP8 unit as well.
+//
+// The weights P (in (0, 1], the row maximum subtracted) are scaled by 2^8, an
+// exact power of two that keeps every weight above 2^-14 out of the e4m3
+// subnormals, and rounded to e4m3 (round to nearest even, the hardware
+// conversion).  A 64-key block is one 32 x 32 x 64 contraction step; lane half
+// h of a row holds, as bytes e = 16 jb + v, the weights of keys
+// 32 jb + 8 (v / 4) + 4 h + v % 4 -- exactly the keys its S^T registers hold.
+// V^T is staged as bytes with the same key order: byte position
+// p = 32 h + e of a V^T row holds that key, so the A operand of lane half h is
+// 32 contiguous bytes.
+__device__ __forceinline__ int w8_pos(int key) {
+    const int r = key & 31;
+    return 32 * ((r >> 2) & 1) + 16 * (key >> 5) + 4 * (r >> 3) + (r & 3);
+}
+
+template <int D, int NIV>
+struct alignas(16) Smem8w {
+    alignas(16) uint8_t k8[2][kBc][D + kK8Pad];   // K block, row-major, e4m3
+    alignas(16) uint8_t vt8[2][D][kBc + kK8Pad];  // V block, transposed, e4m3, keys in w8_pos order
+    int start[NIV][kBr];
+    int width[NIV][kBr];
+};
+static_assert((kBc + kK8Pad) % 16 == 0, "fp8 V^T rows 16-byte aligned");
+static_assert(kBc == 64, "one 64-wide FP8 contraction step per key block");
+
+// Four rows x eight e4m3 columns (two dwords per row) written transposed:
+// column n0 + c of the four keys becomes one dword of V^T row n0 + c.
+__device__ __forceinline__ void store_transposed8_4x8(const u32x2 (&rows)[4], uint8_t* dst, int pitch, int n0,
+                                                      int p) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const uint32_t r0 = rows[0][w], r1 = rows[1][w], r2 = rows[2][w], r3 = rows[3][w];
+        // byte pairs of rows (0,1) and (2,3) for columns 0,1 and 2,3 of this dword
+        const uint32_t a = __builtin_amdgcn_perm(r1, r0, 0x05010400u);   // r0[0] r1[0] r0[1] r1[1]
+        const uint32_t b = __builtin_amdgcn_perm(r1, r0, 0x07030602u);   // r0[2] r1[2] r0[3] r1[3]
+        const uint32_t c = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+        const uint32_t d = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+        const uint32_t col[4] = {__builtin_amdgcn_perm(c, a, 0x05040100u), __builtin_amdgcn_perm(c, a, 0x07060302u),
+                                 __builtin_amdgcn_perm(d, b, 0x05040100u), __builtin_amdgcn_perm(d, b, 0x07060302u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(dst + (n0 + 4 * w + q) * pitch + p) = col[q];
+    }
+}
+
+template <int D, int NIV>
+__device__ __forceinline__ void store_block8w(const Staging8<D>& st, Smem8w<D, NIV>& sm, int buf, int tid) {
+#pragma unroll
+    for (int c = 0; c < Staging8<D>::kChunksK; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int row = chunk / (D / 16);
+        const int col16 = chunk % (D / 16);
+        *reinterpret_cast<u32x4*>(&sm.k8[buf][row][col16 * 16]) = st.k[c];
+    }
+    if (Staging8<D>::kItemsV == kThreads || tid < Staging8<D>::kItemsV) {
+        const int j0 = 4 * (tid % (kBc / 4));
+        const int n0 = 8 * (tid / (kBc / 4));
+        store_transposed8_4x8(st.v, &sm.vt8[buf][0][0], kBc + kK8Pad, n0, w8_pos(j0));
+    }
+}
+
+// Types of one instantiation: PREC 0 bf16 inputs; 1 e4m3 inputs (V widened to
+// bf16, bf16 weights); 2 e4m3 inputs and e4m3 weights.
+template <int D, int NIV, int PREC>
 struct FwdTypes {
     using In = uint16_t;
     using Shared = Smem<D, NIV>;
@@ -226,9 +288,17 @@ struct FwdTypes {
     static constexpr int kQRegs = D / 16;
 };
 template <int D, int NIV>
-struct FwdTypes<D, NIV, true> {
+struct FwdTypes<D, NIV, 1> {
     using In = uint8_t;
     using Shared = Smem8<D, NIV>;
+    using Stage = Staging8<D>;
+    using QReg = v8i;
+    static constexpr int kQRegs = D / 64;
+};
+template <int D, int NIV>
+struct FwdTypes<D, NIV, 2> {
+    using In = uint8_t;
+    using Shared = Smem8w<D, NIV>;
     using Stage = Staging8<D>;
     using QReg = v8i;
     static constexpr int kQRegs = D / 64;
@@ -237,15 +307,19 @@ struct FwdTypes<D, NIV, true> {
 // NIV: ranges per query row (the row attends their union).  col_start and
 // col_end are [B][NIV][N]; meta holds NIV records per query block.  F8: Q, K,
 // V are e4m3 (c then includes their dequantization scales, and v_scale
-// multiplies the output).
-template <int D, int NIV, bool F8>
+// multiplies the output); PREC 2 also rounds the weights to e4m3.
+template <int D, int NIV, int PREC>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
-    const typename FwdTypes<D, NIV, F8>::In* __restrict__ Q, const typename FwdTypes<D, NIV, F8>::In* __restrict__ K,
-    const typename FwdTypes<D, NIV, F8>::In* __restrict__ V, const int32_t* __restrict__ col_start,
+    const typename FwdTypes<D, NIV, PREC>::In* __restrict__ Q,
+    const typename FwdTypes<D, NIV, PREC>::In* __restrict__ K,
+    const typename FwdTypes<D, NIV, PREC>::In* __restrict__ V, const int32_t* __restrict__ col_start,
     const int32_t* __restrict__ col_end, const TileMeta* __restrict__ meta, const int32_t* __restrict__ order,
     int H, int N, int n_q, float c, float v_scale, int xcd_heads, int per_head, uint16_t* __restrict__ O,
     float* __restrict__ LSE) {
-    using T = FwdTypes<D, NIV, F8>;
+    using T = FwdTypes<D, NIV, PREC>;
+    constexpr bool F8 = PREC != 0;       // e4m3 inputs
+    constexpr bool W8 = PREC == 2;       // e4m3 weights
+    constexpr float kW8Shift = W8 ? 8.f : 0.f;   // log2 of the weights' scale
     constexpr int kElt = (int)sizeof(typename T::In);   // bytes per Q/K/V element
     __shared__ typename T::Shared sm;
 
@@ -365,7 +439,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     int j = union_next<NIV>(tm, -1);
     if (j != INT_MAX) {
         typename T::Stage stage;
-        if constexpr (F8) {
+        if constexpr (W8) {
+            load_block8<D>(stage, krs, vrs, j * kBc, tid);
+            store_block8w<D>(stage, sm, 0, tid);
+        } else if constexpr (F8) {
             load_block8<D>(stage, krs, vrs, j * kBc, tid);
             store_block8<D>(stage, sm, 0, tid);
         } else {
@@ -480,7 +557,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                     for (int nb = 0; nb < D / 32; ++nb) oacc[nb] *= alpha;
                     m_run = m_new;
                 }
-                const float m_use = m_run == -INFINITY ? 0.f : m_run;
+                // e4m3 weights are formed as 2^8 P: the exponent offset is folded in here
+                const float m_use = (m_run == -INFINITY ? 0.f : m_run) - kW8Shift;
                 float rs = 0.f;
 #pragma unroll
                 for (int jb = 0; jb < kBc / 32; ++jb)
@@ -496,24 +574,53 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 // bf16-rounded weights, so the rounding of P perturbs the weights
                 // of a proper weighted mean instead of biasing its scale.
                 float rs16 = 0.f;
+                if constexpr (W8) {
+                    // the weights (already 2^8 P) as e4m3, bytes e = 16 jb + v (see
+                    // w8_pos); the normaliser is the sum of the rounded weights, read back
+                    uint32_t pw[8];
 #pragma unroll
-                for (int ks = 0; ks < kBc / 16; ++ks) {
-                    bf16x8 pb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)st[ks >> 1][8 * (ks & 1) + e];
-                    rs16 = sum_bf16x8(pb, ones, rs16);
+                    for (int w = 0; w < 8; ++w) {
+                        const int jb = w >> 2, v0 = 4 * (w & 3);
+                        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(st[jb][v0], st[jb][v0 + 1], 0, false);
+                        packed = __builtin_amdgcn_cvt_pk_fp8_f32(st[jb][v0 + 2], st[jb][v0 + 3], packed, true);
+                        pw[w] = (uint32_t)packed;
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
+                        rs16 += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+                    }
+                    const v8i pb8 = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
+                                     (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 #pragma unroll
                     for (int nb = 0; nb < D / 32; ++nb) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            &sm.vt[buf][nb * 32 + r32][16 * ks + 8 * half]);
-                        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
+                        const uint8_t* src = &sm.vt8[buf][nb * 32 + r32][32 * half];
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
+                        const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        oacc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb8, oacc[nb], 0, 0, 0,
+                                                                                   kUnitScales, 0, kUnitScales);
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < kBc / 16; ++ks) {
+                        bf16x8 pb;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)st[ks >> 1][8 * (ks & 1) + e];
+                        rs16 = sum_bf16x8(pb, ones, rs16);
+#pragma unroll
+                        for (int nb = 0; nb < D / 32; ++nb) {
+                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                                &sm.vt[buf][nb * 32 + r32][16 * ks + 8 * half]);
+                            oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
+                        }
                     }
                 }
                 l16_run += rs16;
             }
 
             if (has_next) {
-                if constexpr (F8)
+                if constexpr (W8)
+                    store_block8w<D>(stage, sm, buf ^ 1, tid);
+                else if constexpr (F8)
                     store_block8<D>(stage, sm, buf ^ 1, tid);
                 else
                     store_block<D>(stage, sm, buf ^ 1, tid);
@@ -541,7 +648,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 *reinterpret_cast<bf16x4*>(orow + nb * 32 + 8 * g + 4 * half) = o4;
             }
         }
-        if (half == 0) LSE[bh * N + qrow] = l > 0.f ? m_run * kLn2 + logf(l) : -INFINITY;
+        if (half == 0) LSE[bh * N + qrow] = l > 0.f ? (m_run - kW8Shift) * kLn2 + logf(l) : -INFINITY;
     }
 }
 
@@ -551,7 +658,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                            const float* fp8_scales, int n_sets) {
+                            const float* fp8_scales, int n_sets, bool fp8_weights) {
     const int64_t n_q = (N + kBr - 1) / kBr;
     const int64_t grid = B * H * n_q;
     const bool f8 = fp8_scales != nullptr;
@@ -569,7 +676,8 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
             const auto* Qp = static_cast<const uint8_t*>(q);
             const auto* Kp = static_cast<const uint8_t*>(k);
             const auto* Vp = static_cast<const uint8_t*>(v);
-            auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, true> : attn_fwd_kernel<64, NIV, true>;
+            auto kernel = fp8_weights ? (d == 128 ? attn_fwd_kernel<128, NIV, 2> : attn_fwd_kernel<64, NIV, 2>)
+                                      : (d == 128 ? attn_fwd_kernel<128, NIV, 1> : attn_fwd_kernel<64, NIV, 1>);
             hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
                                   xcd_heads, n_sets > 1 ? 1 : 0, Op, lse);
@@ -577,7 +685,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
             const auto* Qp = static_cast<const uint16_t*>(q);
             const auto* Kp = static_cast<const uint16_t*>(k);
             const auto* Vp = static_cast<const uint16_t*>(v);
-            auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, false> : attn_fwd_kernel<64, NIV, false>;
+            auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, 0> : attn_fwd_kernel<64, NIV, 0>;
             hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
                                   xcd_heads, n_sets > 1 ? 1 : 0, Op, lse);

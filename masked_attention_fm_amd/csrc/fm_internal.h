@@ -61,13 +61,14 @@ hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, i
 
 // Attention kernel.  order == nullptr runs query blocks in natural (b, t) order.
 // start/stop (may be null) are stamped at the kernel's own start and end.
-// fp8_scales == nullptr: q, k, v are bf16.  Otherwise they are e4m3 and
-// fp8_scales points to their three dequantization scales (host memory).
+// fp8_scales == nullptr: q, k, v are bf16.  Otherwise they are e4m3,
+// fp8_scales points to their three dequantization scales (host memory), and
+// fp8_weights also rounds the weights to e4m3 for an FP8 PV product.
 hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                            const float* fp8_scales = nullptr, int n_sets = 1);
+                            const float* fp8_scales = nullptr, int n_sets = 1, bool fp8_weights = false);
 
 // Backward pass (gradients of Q, K, V).  Shapes: the key-block kernel runs
 // kBwdKeys keys per workgroup against query chunks of kBwdRows rows; the

@@ -19,6 +19,7 @@ FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_BAD_INTERVAL, FM_ERR_HIP =
 FM_TILE_SKIP, FM_TILE_FULL, FM_TILE_PARTIAL = 0, 1, 2
 FM_OPT_SCHEDULE = 1
 FM_MAX_RANGES = 4
+FM_FP8_SCORES, FM_FP8_ALL = 0, 1
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -36,8 +37,8 @@ SIGNATURES = {
     "fm_classify_tiles_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P]),
     "fm_attn_fwd_per_head": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
                                             _P, _P, _P]),
-    "fm_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P, _I32,
-                                       _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P]),
+    "fm_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _I32, _P, _P,
+                                       _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P]),
     "fm_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                    _P, _P, _P, _P]),
     "fm_attn_bwd_per_head": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64,
@@ -288,9 +289,13 @@ def fm_attn_fwd_per_head(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_
 def fm_attn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float, k_scale: float,
                     v_scale: float, col_start: torch.Tensor, col_end: torch.Tensor, scale: Optional[float] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    stream=None, mode: int = FM_FP8_SCORES) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward pass on e4m3 inputs (uint8 or torch.float8_e4m3fn tensors [B,H,N,d]) with per-tensor
-    dequantization scales; intervals [B, N] or [B, K, N].  Returns (out bf16, lse fp32).  Asynchronous."""
+    dequantization scales; intervals [B, N] or [B, K, N].  mode FM_FP8_SCORES keeps the weights and
+    the PV product in bf16, FM_FP8_ALL rounds the weights to e4m3 for an FP8 PV product.  Returns
+    (out bf16, lse fp32).  Asynchronous."""
+    if mode not in (FM_FP8_SCORES, FM_FP8_ALL):
+        raise ValueError("mode must be FM_FP8_SCORES or FM_FP8_ALL")
     codes = []
     for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
         if isinstance(x, torch.Tensor) and x.dtype == torch.float8_e4m3fn:
@@ -324,7 +329,8 @@ def fm_attn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scal
         if tuple(lse.shape) != (B, H, N):
             raise ValueError("lse must be [B, H, N]")
     status = lib().fm_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), float(q_scale), float(k_scale),
-                                   float(v_scale), col_start.data_ptr(), col_end.data_ptr(), n_ranges, B, H, N, d,
+                                   float(v_scale), int(mode), col_start.data_ptr(), col_end.data_ptr(), n_ranges,
+                                   B, H, N, d,
                                    float(scale), out.data_ptr(), lse.data_ptr(), _stream_handle(stream))
     _check("fm_attn_fwd_fp8", status)
     return out, lse

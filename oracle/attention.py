@@ -97,16 +97,19 @@ def attention(q, k, v, col_start, col_end, scale: float,
     return O, LSE
 
 
-def attention_weights(q, k, col_start, col_end, scale: float) -> np.ndarray:
-    """Full softmax weight matrix P [B, H, N, N] (small N only)."""
+def attention_weights(q, k, col_start, col_end, scale: float,
+                      rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Softmax weight matrix P [B, H, R, N] of the chosen query rows (default
+    all: R = N; small N, or few rows, only)."""
     B, H, N, d = q.shape
     scale64 = float(np.float32(scale))
-    P = np.zeros((B, H, N, N), dtype=np.float64)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    P = np.zeros((B, H, rows.shape[0], N), dtype=np.float64)
     for b in range(B):
-        M = dense_mask(col_start[b], col_end[b], N)
+        M = dense_mask(col_start[b], col_end[b], N, rows)
         attended = M.any(axis=1)
         for h in range(H):
-            S = scale64 * (np.asarray(q[b, h], np.float64) @ np.asarray(k[b, h], np.float64).T)
+            S = scale64 * (np.asarray(q[b, h][rows], np.float64) @ np.asarray(k[b, h], np.float64).T)
             S = np.where(M, S, -np.inf)
             m = np.where(attended, S.max(axis=1), 0.0)
             p = np.exp(S - m[:, None])

@@ -213,13 +213,15 @@ def test_attn_bwd_multi_rejects_bad_range_count(L):
     ((1.0, 1.0, float("nan")), fmb.FM_ERR_INVALID_ARG),
     ((1.0, float("inf"), 1.0), fmb.FM_ERR_INVALID_ARG),
 ])
-def test_attn_fwd_fp8_rejects_bad_scales(L, scales, status):
-    assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, *scales, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
+@pytest.mark.parametrize("mode", [fmb.FM_FP8_SCORES, fmb.FM_FP8_ALL])
+def test_attn_fwd_fp8_rejects_bad_scales(L, scales, status, mode):
+    assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, *scales, mode, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
                              None) == status
 
 
-def test_attn_fwd_fp8_rejects_bad_arguments(L):
-    ok = (1.0, 1.0, 1.0)
+@pytest.mark.parametrize("mode", [fmb.FM_FP8_SCORES, fmb.FM_FP8_ALL])
+def test_attn_fwd_fp8_rejects_bad_arguments(L, mode):
+    ok = (1.0, 1.0, 1.0, mode)
     assert L.fm_attn_fwd_fp8(None, FAKE, FAKE, *ok, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
                              None) == fmb.FM_ERR_INVALID_ARG
     assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, *ok, FAKE, FAKE, 0, 1, 1, 128, 128, 0.125, FAKE, FAKE,
@@ -228,6 +230,18 @@ def test_attn_fwd_fp8_rejects_bad_arguments(L):
                              None) == fmb.FM_ERR_UNSUPPORTED
     assert L.fm_attn_fwd_fp8(FAKE + 8, FAKE, FAKE, *ok, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125, FAKE, FAKE,
                              None) == fmb.FM_ERR_INVALID_ARG
+
+
+def test_attn_fwd_fp8_rejects_bad_mode(L):
+    for mode in (-1, 2):
+        assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, 1.0, 1.0, 1.0, mode, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125,
+                                 FAKE, FAKE, None) == fmb.FM_ERR_INVALID_ARG
+
+
+def test_header_fp8_modes_match_binding():
+    text = open(HEADER, encoding="utf-8").read()
+    assert re.search(r"#define FM_FP8_SCORES (\d+)", text).group(1) == str(fmb.FM_FP8_SCORES)
+    assert re.search(r"#define FM_FP8_ALL (\d+)", text).group(1) == str(fmb.FM_FP8_ALL)
 
 
 def test_attn_fwd_per_head_rejects_bad_arguments(L):

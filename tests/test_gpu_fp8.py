@@ -1,8 +1,11 @@
 """GPU parity of the FP8-input forward pass (fm_attn_fwd_fp8): the oracle on the
 dequantized e4m3 inputs.  The score product is exact for FP8 inputs up to the FP8
-units' accumulation, and V widens exactly to bf16, so the bf16 path's error model
-applies: small cases are held to its elementwise bound (output and weight rounding),
-the full-size doc-packed workload to the 1e-2 / 1e-3 bars."""
+units' accumulation.  Mode FM_FP8_SCORES widens V exactly to bf16, so the bf16
+path's error model applies: small cases are held to its elementwise bound (output
+and weight rounding), the full-size doc-packed workload to the 1e-2 / 1e-3 bars.
+Mode FM_FP8_ALL rounds the weights to e4m3 (relative 2^-4): every case, the
+full-size workload included (on a row sample), is held to that mode's elementwise
+bound."""
 import numpy as np
 import pytest
 import torch
@@ -17,12 +20,16 @@ from test_gpu_multi import multi_intervals
 pytestmark = pytest.mark.gpu
 
 
-def run_fp8(qkv8, s, e, scale):
+MODES = [fm.FM_FP8_SCORES, fm.FM_FP8_ALL]
+MODE_IDS = ["scores", "all"]
+
+
+def run_fp8(qkv8, s, e, scale, mode=fm.FM_FP8_SCORES):
     (q8, qs), (k8, ks), (v8, vs) = qkv8
     qd, kd, vd = to_dev(q8, k8, v8)
     out = torch.full(q8.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
     lse = torch.full(q8.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
-    fm.fm_attn_fwd_fp8(qd, kd, vd, qs, ks, vs, *to_dev(s, e), scale, out=out, lse=lse)
+    fm.fm_attn_fwd_fp8(qd, kd, vd, qs, ks, vs, *to_dev(s, e), scale, out=out, lse=lse, mode=mode)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -43,17 +50,57 @@ def bf16_half_ulp(x):
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
 
 
-def check_fp8_model(qkv8, s, e, scale, what):
-    """Elementwise bound of the bf16 output path on the dequantized inputs: rounding O to
-    bf16 (half an ulp) plus rounding each weight to bf16 before the PV product (relative
-    2^-8, so |dO_i| <= 2^-8 sum_j P_ij |v_j - O_i|), plus 1e-4 for the fp32 arithmetic and
-    the FP8 score accumulation; LSE within 1e-3."""
-    O, L = run_fp8(qkv8, s, e, scale)
+def row_terms(P, v, O_ref):
+    """Per output element: sum_j P_ij |v_j - O_i|, P_max,i sum_j |v_j - O_i| (over the
+    row's keys), sum_j P_ij |v_j|; per row: the number of keys n_i."""
+    B, H, R, N = P.shape
+    spread, tail, mag = (np.zeros(O_ref.shape) for _ in range(3))
+    n = np.zeros((B, H, R, 1))
+    for b in range(B):
+        for h in range(H):
+            for i in range(R):
+                sup = np.flatnonzero(P[b, h, i] > 0)
+                if sup.size == 0:
+                    continue
+                w = P[b, h, i, sup]
+                dev = np.abs(v[b, h, sup] - O_ref[b, h, i])
+                spread[b, h, i] = w @ dev
+                tail[b, h, i] = w.max() * dev.sum(axis=0)
+                mag[b, h, i] = w @ np.abs(v[b, h, sup])
+                n[b, h, i] = sup.size
+    return spread, tail, mag, n
+
+
+def fp8_bound(mode, P, v, O_ref, O):
+    """Elementwise error bound of the output against the oracle on the dequantized inputs.
+
+    Both modes: half an ulp of the bf16 output, plus 1e-4 for the fp32 arithmetic and the
+    FP8 score accumulation.  With the weights w_j rounded to w'_j before the PV product
+    and the output divided by sum_j w'_j, the error is exactly
+    sum_j (w'_j - w_j)(v_j - O) / sum_j w'_j.
+      FM_FP8_SCORES: bf16 weights, |w' - w| <= 2^-8 w.
+      FM_FP8_ALL: e4m3 weights of 2^8 w (w <= 1 against the running row maximum):
+        |w' - w| <= 2^-4 w, or 2^-18 of the row maximum in the subnormal range, so the
+        sum of w' is at least (1 - 2^-4 - n 2^-18) sum_j w_j; plus the FP8 units'
+        accumulation, within 4e-5 of sum_j |w'_j v_j|."""
+    spread, tail, mag, n = row_terms(P, v, O_ref)
+    ulp = bf16_half_ulp(np.maximum(np.abs(O_ref), np.abs(O)))
+    if mode == fm.FM_FP8_SCORES:
+        return ulp + 2.0 ** -8 * spread + 1e-4
+    u = 2.0 ** -4
+    den = 1.0 - u - n * 2.0 ** -18
+    return ulp + (u * spread + 2.0 ** -18 * tail + 4e-5 * (1 + u) * mag) / den + 1e-4
+
+
+def check_fp8_model(qkv8, s, e, scale, what, mode=fm.FM_FP8_SCORES, rows=None):
+    """The output within fp8_bound elementwise (on the chosen rows); LSE within 1e-3."""
+    O, L = run_fp8(qkv8, s, e, scale, mode)
     q, k, v = (inputs.dequantize_e4m3(c, sc) for c, sc in qkv8)
-    O_ref, L_ref = oracle.attention(q, k, v, s, e, scale)
-    P = oracle.attention_weights(q, k, s, e, scale)                  # [B, H, N, N]
-    spread = np.einsum("bhij,bhijc->bhic", P, np.abs(v[:, :, None, :, :] - O_ref[:, :, :, None, :]))
-    bound = bf16_half_ulp(O_ref) + 2.0 ** -8 * spread + 1e-4
+    O_ref, L_ref = oracle.attention(q, k, v, s, e, scale, rows=rows)
+    if rows is not None:
+        O, L = O[:, :, rows], L[:, :, rows]
+    P = oracle.attention_weights(q, k, s, e, scale, rows=rows)       # [B, H, R, N]
+    bound = fp8_bound(mode, P, v, O_ref, O)
     err = np.abs(O - O_ref)
     empty = np.isneginf(L_ref)
     assert np.array_equal(np.isneginf(L), empty), f"{what}: -inf LSE pattern differs"
@@ -76,22 +123,38 @@ FP8_CASES = [
 ]
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_fp8_small(case):
+def test_fp8_small(case, mode):
     B, H, N, d, mask = case
     rng = np.random.default_rng(N * 13 + d)
     s, e = small_intervals(mask, B, N, rng)
     qkv8 = inputs.make_qkv_fp8(B, H, N, d, seed=N + 3 * d)
-    log(f"fp8 small {case}")
-    check_fp8_model(qkv8, s, e, inputs.default_scale(d), f"fp8 {case}")
+    log(f"fp8 small {case} mode {mode}")
+    check_fp8_model(qkv8, s, e, inputs.default_scale(d), f"fp8 {case} mode {mode}", mode)
 
 
-def test_fp8_multi_range():
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_fp8_multi_range(mode):
     B, H, N, d, K = 2, 2, 900, 128, 3
     rng = np.random.default_rng(33)
     s, e = multi_intervals("random_empty", B, K, N, rng)
     qkv8 = inputs.make_qkv_fp8(B, H, N, d, seed=33)
-    check_fp8_model(qkv8, s, e, inputs.default_scale(d), "fp8 multi")
+    check_fp8_model(qkv8, s, e, inputs.default_scale(d), f"fp8 multi mode {mode}", mode)
+
+
+def test_fp8_weights_doc_packed_workload_sampled_rows():
+    """FM_FP8_ALL on the doc-packed workload (B=1, H=16, N=8192, d=128), the elementwise
+    bound on a sample of rows from every query tile (first, last and a random row)."""
+    cfg = inputs.CONFIGS["C2"]
+    spec = inputs.config_intervals(cfg)
+    qkv8 = inputs.make_qkv_fp8(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    rng = np.random.default_rng(5)
+    tiles = np.arange(0, cfg.N, 128)
+    rows = np.unique(np.concatenate([tiles, tiles + 127, tiles + rng.integers(0, 128, tiles.size)]))
+    log(f"fp8 all C2, {rows.size} rows")
+    check_fp8_model(qkv8, spec.col_start, spec.col_end, inputs.default_scale(cfg.d), "fp8 all C2",
+                    fm.FM_FP8_ALL, rows=rows)
 
 
 def test_fp8_doc_packed_workload():
@@ -104,14 +167,16 @@ def test_fp8_doc_packed_workload():
     log(f"fp8 C2: max|dO|={dO:.3e} max|dLSE|={dL:.3e}")
 
 
-def test_fp8_zero_q_is_mean_of_v():
-    """Q = 0: O_r is the mean of the dequantized v over the row's keys, LSE_r = ln(#keys)."""
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_fp8_zero_q_is_mean_of_v(mode):
+    """Q = 0: O_r is the mean of the dequantized v over the row's keys, LSE_r = ln(#keys)
+    (every weight is 1, exact in both weight formats)."""
     B, H, N, d = 1, 2, 500, 128
     rng = np.random.default_rng(41)
     s, e = inputs.random_intervals(rng, B, N, empty_frac=0.05, max_width=250)
     qkv8 = list(inputs.make_qkv_fp8(B, H, N, d, seed=41))
     qkv8[0] = (torch.zeros_like(qkv8[0][0]), qkv8[0][1])
-    O, L = run_fp8(qkv8, s, e, inputs.default_scale(d))
+    O, L = run_fp8(qkv8, s, e, inputs.default_scale(d), mode)
     v = inputs.dequantize_e4m3(*qkv8[2])
     for i in range(N):
         if s[0, i] > e[0, i]:

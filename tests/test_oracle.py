@@ -290,6 +290,9 @@ def test_sampled_rows_equal_full_rows():
     Os, Ls = oracle.attention(q, k, v, s, e, SCALE(d), rows=rows, row_block=3)
     np.testing.assert_allclose(Os, O[:, :, rows], rtol=0, atol=1e-14)
     np.testing.assert_allclose(Ls, L[:, :, rows], rtol=0, atol=1e-14)
+    P = oracle.attention_weights(q, k, s, e, SCALE(d))
+    Ps = oracle.attention_weights(q, k, s, e, SCALE(d), rows=rows)
+    np.testing.assert_allclose(Ps, P[:, :, rows], rtol=0, atol=1e-15)
 
 
 def test_bf16_round_matches_torch():
