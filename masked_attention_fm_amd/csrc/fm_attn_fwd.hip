@@ -22,10 +22,16 @@
 //     never leaves its lane.  P^T is taken straight from the S^T registers
 //     (converted to bf16) as the B operand; the contraction index of the two
 //     operands is permuted consistently so no data moves between lanes.
-//   * K (row-major) and V^T (transposed while staging) pass through a
-//     double-buffered LDS ring: while block j is computed, block j+1 is
-//     loaded from HBM with 128-bit loads into registers and then written to
-//     the other buffer; one barrier per key block.
+//   * K and V pass through a double-buffered LDS ring: while block j is
+//     computed, block j+1 is loaded from HBM straight into the other buffer
+//     (buffer loads with an LDS destination, no registers involved); one
+//     barrier per key block.  K is read row-major as the A operand of the
+//     score product, V transposed (ds_read_b64_tr_b16) as the A operand of
+//     the PV product.  (FP8 inputs are staged through registers instead, see
+//     below.)
+//   * Softmax with lazy rescaling: a row's reference maximum may lag its
+//     running maximum by up to 2^8 in weight, so the accumulator is rescaled
+//     only when some row of the wavefront outgrows that margin.
 //   * Key blocks outside the query block's non-skip range are never visited
 //     (range from the interval preprocessor).  Inside the range each
 //     wavefront tests its own 32 rows: it skips blocks none of its rows
@@ -56,8 +62,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = kBr / kWaves;     // 32
-constexpr int kKPad = 8;                       // bf16 padding per K row in LDS (16 B)
-constexpr int kVPad = 8;                       // bf16 padding per V^T row in LDS (16 B)
+constexpr int kVPad = 8;                       // bf16 padding per V^T row in LDS (16 B), FP8 inputs
 
 static_assert(kRowsPerWave == 32, "one 32x32 MFMA column block per wavefront");
 static_assert(kBc % 32 == 0 && kBc % 16 == 0, "key block is a multiple of the MFMA shapes");
@@ -71,65 +76,172 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, bf16x2 ones, float acc) {
     return acc;
 }
 
+// ---- bf16 K and V blocks, loaded straight from global memory into LDS.
+//
+// A `buffer_load_dwordx4 ... lds` writes the 16 bytes of lane l to LDS
+// address M0 + 16 l: one instruction fills a contiguous 1 KB segment, each
+// lane fetching whichever 16 bytes of the block it is given.  Rows past N
+// read as zero (the buffer range check), so their scores are masked and their
+// values meet a weight of exactly 0.  No registers, VALU work or LDS store
+// instructions are spent on staging.
+//
+// A segment holds kSegKeys = 1024 / (2 D) key rows (4 at d = 128, 8 at
+// d = 64): key kappa of the block sits in segment kappa % kSegs, slot
+// kappa / kSegs.  Segments are padded so that the operand reads below are
+// free of bank conflicts:
+//   * K, pitch 1024 + 16 B.  The score product reads 16 bytes of one key per
+//     lane, eight consecutive keys per 8-lane phase: consecutive keys are in
+//     consecutive segments, 16 bytes apart modulo 128.
+//   * V, pitch 1024 + 32 B.  The PV product needs V^T, read with
+//     ds_read_b64_tr_b16: within each 16-lane group, local lane i receives
+//     element i % 4 of the 8-byte pieces addressed by lanes 4 e + i / 4,
+//     e = 0..3 (verified by an in-bounds probe).  Lane 4 e + c addresses key
+//     kappa0 + e, columns n0 + 4 c .. + 3, so lane i ends up with column
+//     n0 + i of keys kappa0 .. kappa0 + 3.  The four keys are in consecutive
+//     segments, 32 bytes apart modulo 128: one 128-byte sweep per group.
+template <int D>
+struct Direct {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kSegKeys = 1024 / kRowBytes;
+    static constexpr int kSegs = kBc / kSegKeys;
+    static constexpr int kKPitch = 1024 + 16;
+    static constexpr int kVPitch = 1024 + 32;
+    static constexpr int kKBytes = kSegs * kKPitch;
+    static constexpr int kVBytes = kSegs * kVPitch;
+    static constexpr int kSegsPerWave = kSegs / kWaves;
+    static_assert(kSegKeys * kSegs == kBc && kSegsPerWave * kWaves == kSegs, "segments split evenly");
+    static_assert(kSegs % 8 == 0, "eight consecutive keys in distinct segments");
+};
+
 template <int D, int NIV>
 struct alignas(16) Smem {
-    alignas(16) uint16_t k[2][kBc][D + kKPad];    // K block, row-major
-    alignas(16) uint16_t vt[2][D][kBc + kVPad];   // V block, transposed, keys permuted by vt_pos
+    alignas(16) uint8_t k[2][Direct<D>::kKBytes];
+    alignas(16) uint8_t v[2][Direct<D>::kVBytes];
     int start[NIV][kBr];                          // clamped start of each range of each query row
                                                   // (kEmptyStart: the range holds no key)
     int width[NIV][kBr];                          // end - start (0 for empty ranges)
 };
-static_assert(((128 + kKPad) * 2) % 16 == 0 && ((64 + kKPad) * 2) % 16 == 0, "K rows 16-byte aligned");
-static_assert(((kBc + kVPad) * 2) % 16 == 0, "V^T rows 16-byte aligned");
 
-template <int D>
-struct Staging {
-    static constexpr int kChunksK = kBc * D / 8 / kThreads;   // 16-byte K chunks per thread
-    static constexpr int kItemsV = (kBc / 4) * (D / 8);       // 4 keys x 8 columns per item
-    static_assert(kChunksK * kThreads * 8 == kBc * D, "K block splits evenly");
-    static_assert(kItemsV <= kThreads, "one V item per thread at most");
-    u32x4 k[kChunksK];
-    u32x4 v[4];
-};
+struct NoStage {};
 
-// Loads key block [kv0, kv0 + kBc) into registers.  Rows past N read as zero:
-// their scores are always masked (a block that reaches past N is never
-// treated as full) and their values meet a weight of exactly 0.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+// Byte offset, inside a block's slice of K or V, of this lane's 16 bytes in
+// the first segment its wavefront fills (wave_u: the wavefront index).
 template <int D>
-__device__ __forceinline__ void load_block(Staging<D>& st, __amdgpu_buffer_rsrc_t krs,
-                                           __amdgpu_buffer_rsrc_t vrs, int kv0, int tid) {
-    const int base = kv0 * D * 2;
-#pragma unroll
-    for (int c = 0; c < Staging<D>::kChunksK; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int row = chunk / (D / 8);
-        const int col8 = chunk % (D / 8);
-        st.k[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + row * D * 2 + col8 * 16, 0, 0);
-    }
-    if (Staging<D>::kItemsV == kThreads || tid < Staging<D>::kItemsV) {
-        const int j0 = 4 * (tid % (kBc / 4));
-        const int n0 = 8 * (tid / (kBc / 4));
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, base + (j0 + r) * D * 2 + n0 * 2, 0, 0);
+__device__ __forceinline__ int direct_lane_offset(int lane, int wave_u) {
+    using L = Direct<D>;
+    const int slot = lane / (D / 8);
+    const int chunk = lane % (D / 8);
+    return (wave_u * L::kSegsPerWave + L::kSegs * slot) * L::kRowBytes + 16 * chunk;
+}
+
+// ---- V^T operand reads for the PV product (bf16 path).
+//
+// The transposing read is issued through inline assembly: the compiler
+// treats the ds_read_tr builtin as a read of any LDS location and would wait
+// for the next block's in-flight loads before every one of them, which
+// serialises the prefetch with the compute.  The reads here target the
+// current buffer only, which no in-flight load writes.  Their completion is
+// waited for explicitly (LDS operations complete in issue order, so
+// lgkmcnt(n) after n younger reads guarantees the older ones), and each wait
+// passes the registers through itself so nothing can use them earlier.
+// `after` is not used by the instruction: it only orders the read after the
+// computation of that value.
+template <int OFF>
+__device__ __forceinline__ v4s lds_read_tr16(uint32_t addr, float after) {
+    v4s r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF), "v"(after));
+    return r;
+}
+
+// The 2 D / 32 reads of step KS (16 keys): part[2 nb + r] holds, for lane
+// (column i, half h), keys 16 KS + 8 r + 4 h + 0..3 of column 32 nb + i.
+template <int D, int KS, int I = 0>
+__device__ __forceinline__ void issue_v_reads(v4s (&part)[2 * D / 32], uint32_t addr, float after = 0.f) {
+    using L = Direct<D>;
+    if constexpr (I < 2 * D / 32) {
+        constexpr int nb = I / 2, r = I % 2;
+        constexpr int key0 = 16 * KS + 8 * r;
+        constexpr int off = (key0 % L::kSegs) * L::kVPitch + (key0 / L::kSegs) * L::kRowBytes + nb * 64;
+        static_assert(off >= 0 && off < 65536, "ds offset field");
+        part[I] = lds_read_tr16<off>(addr, after);
+        issue_v_reads<D, KS, I + 1>(part, addr, after);
     }
 }
 
-template <int D, int NIV>
-__device__ __forceinline__ void store_block(const Staging<D>& st, Smem<D, NIV>& sm, int buf, int tid) {
+// Wait until at most CNT LDS operations are outstanding; part is passed
+// through the wait.
+template <int CNT, int NP>
+__device__ __forceinline__ void wait_lds_tied(v4s (&p)[NP]) {
+    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
+    if constexpr (NP == 8)
+        asm volatile("s_waitcnt lgkmcnt(%8)"
+                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                       "+v"(p[7])
+                     : "i"(CNT));
+    else if constexpr (NP == 4)
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]) : "i"(CNT));
+    else
+        static_assert(NP == 8 || NP == 4, "d = 64 or 128");
+}
+
+// O^T += V^T P^T over steps KS.. of one key block.  cur holds step KS's
+// reads (issued earlier); the next step's reads are issued before waiting
+// for them.
+template <int D, int KS>
+__device__ __forceinline__ void pv_direct(const floatx16 (&st)[kBc / 32], floatx16 (&oacc)[D / 32],
+                                          uint32_t addr, float& rs16, bf16x2 ones, v4s (&cur)[2 * D / 32]) {
+    constexpr int NP = 2 * D / 32;
+    if constexpr (KS < kBc / 16) {
+        bf16x8 pb;
 #pragma unroll
-    for (int c = 0; c < Staging<D>::kChunksK; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int row = chunk / (D / 8);
-        const int col8 = chunk % (D / 8);
-        *reinterpret_cast<u32x4*>(&sm.k[buf][row][col8 * 8]) = st.k[c];
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)st[KS >> 1][8 * (KS & 1) + e];
+        rs16 = sum_bf16x8(pb, ones, rs16);
+        v4s next[NP];
+        if constexpr (KS + 1 < kBc / 16) {
+            issue_v_reads<D, KS + 1>(next, addr);
+            wait_lds_tied<NP>(cur);
+        } else {
+            wait_lds_tied<0>(cur);
+        }
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(cur[2 * nb], cur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
+        }
+        pv_direct<D, KS + 1>(st, oacc, addr, rs16, ones, next);
     }
-    if (Staging<D>::kItemsV == kThreads || tid < Staging<D>::kItemsV) {
-        const int j0 = 4 * (tid % (kBc / 4));
-        const int n0 = 8 * (tid / (kBc / 4));
-        // 4 keys x 8 columns -> 8 columns x 4 keys
-        store_transposed_4x8(st.v, &sm.vt[buf][0][0], kBc + kVPad, n0, vt_pos(j0));
+}
+
+// Segment U of this wavefront's share.  The key row is selected through the
+// lane offset: an instruction offset would move the LDS destination as well.
+template <int D, int NIV, int U>
+__device__ __forceinline__ void load_segment(Smem<D, NIV>& sm, int buf, __amdgpu_buffer_rsrc_t krs,
+                                             __amdgpu_buffer_rsrc_t vrs, int off, int wave_u) {
+    using L = Direct<D>;
+    if constexpr (U < L::kSegsPerWave) {
+        const int seg = wave_u * L::kSegsPerWave + U;
+        const int row_off = off + U * L::kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)&sm.k[buf][seg * L::kKPitch], 16, row_off, 0, 0,
+                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)&sm.v[buf][seg * L::kVPitch], 16, row_off, 0, 0,
+                                                 0);
+        load_segment<D, NIV, U + 1>(sm, buf, krs, vrs, off, wave_u);
     }
+}
+
+// Key block starting at key kv0 into buffer buf (voff = direct_lane_offset).
+template <int D, int NIV>
+__device__ __forceinline__ void load_block_direct(Smem<D, NIV>& sm, int buf, __amdgpu_buffer_rsrc_t krs,
+                                                  __amdgpu_buffer_rsrc_t vrs, int voff, int kv0, int wave_u) {
+    load_segment<D, NIV, 0>(sm, buf, krs, vrs, voff + kv0 * Direct<D>::kRowBytes, wave_u);
 }
 
 // ---------------------------------------------------------------- FP8 inputs
@@ -283,7 +395,7 @@ template <int D, int NIV, int PREC>
 struct FwdTypes {
     using In = uint16_t;
     using Shared = Smem<D, NIV>;
-    using Stage = Staging<D>;
+    using Stage = NoStage;
     using QReg = bf16x8;
     static constexpr int kQRegs = D / 16;
 };
@@ -410,6 +522,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         }
     }
 
+    // bf16 blocks (loaded straight into LDS): this lane's load offset and its
+    // operand read offsets in the segment layout.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int dvoff = F8 ? 0 : direct_lane_offset<D>(lane, wave_u);
+    const int k_lane = F8 ? 0 : (r32 % Direct<D>::kSegs) * Direct<D>::kKPitch +
+                                    (r32 / Direct<D>::kSegs) * Direct<D>::kRowBytes + 16 * half;
+    const int v_lane = F8 ? 0 : (4 * (lane >> 5) + ((lane & 15) >> 2)) * Direct<D>::kVPitch +
+                                    32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
     floatx16 oacc[D / 32];
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) oacc[nb] = floatx16{};
@@ -446,8 +567,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             load_block8<D>(stage, krs, vrs, j * kBc, tid);
             store_block8<D>(stage, sm, 0, tid);
         } else {
-            load_block<D>(stage, krs, vrs, j * kBc, tid);
-            store_block<D>(stage, sm, 0, tid);
+            load_block_direct<D>(sm, 0, krs, vrs, dvoff, j * kBc, wave_u);
+            __builtin_amdgcn_s_waitcnt(0);
         }
         __syncthreads();
 
@@ -458,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 if constexpr (F8)
                     load_block8<D>(stage, krs, vrs, j_next * kBc, tid);
                 else
-                    load_block<D>(stage, krs, vrs, j_next * kBc, tid);
+                    load_block_direct<D>(sm, buf ^ 1, krs, vrs, dvoff, j_next * kBc, wave_u);
             }
 
             const int klo = j * kBc;
@@ -496,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
                         for (int jb = 0; jb < kBc / 32; ++jb) {
                             const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                                &sm.k[buf][jb * 32 + r32][cs * 16 + half * 8]);
+                                &sm.k[buf][k_lane + jb * (32 / Direct<D>::kSegs) * Direct<D>::kRowBytes + cs * 32]);
                             st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
                         }
                     }
@@ -542,13 +663,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 for (int jb = 0; jb < kBc / 32; ++jb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[jb][v]);
-                // The accumulator is rescaled only when some row of the wavefront
-                // raised its maximum.  The reference stays the exact running maximum
-                // (not a stale one): the dominant weight of a row is then 1 and
-                // survives the bf16 rounding of P exactly.
+                // Lazy rescaling: the reference m_run of a row may lag its true
+                // running maximum by up to kSlack (log2 units), so weights reach
+                // 2^kSlack at most (fine for bf16 and the fp32 sums), and the
+                // accumulator is rescaled only when some row of the wavefront
+                // exceeds its reference by more than that -- in practice after the
+                // first block of a row, instead of on most blocks.  A rescale then
+                // moves every row that grew to its exact maximum.  The e4m3 weights
+                // keep the exact maximum (kSlack 0): 2^8 P must stay below 448.
+                constexpr float kSlack = W8 ? 0.f : 8.f;
                 const float m_blk = halves_max(mx) * c;
-                const bool grow = m_blk > m_run;
-                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kSlack) != 0) {
+                    const bool grow = m_blk > m_run;
                     const float m_new = grow ? m_blk : m_run;
                     const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
                     l_run *= alpha;
@@ -559,6 +685,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 }
                 // e4m3 weights are formed as 2^8 P: the exponent offset is folded in here
                 const float m_use = (m_run == -INFINITY ? 0.f : m_run) - kW8Shift;
+                // V^T reads of the PV product's first step, issued once the
+                // score product's operand reads are done, so that their
+                // latency overlaps the exponentials.
+                [[maybe_unused]] v4s vpart[2 * D / 32];
+                [[maybe_unused]] uint32_t vaddr = 0;
+                if constexpr (!F8) {
+                    vaddr = lds_address(&sm.v[buf][0]) + v_lane;
+                    issue_v_reads<D, 0>(vpart, vaddr, m_use);
+                }
                 float rs = 0.f;
 #pragma unroll
                 for (int jb = 0; jb < kBc / 32; ++jb)
@@ -599,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                         oacc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb8, oacc[nb], 0, 0, 0,
                                                                                    kUnitScales, 0, kUnitScales);
                     }
-                } else {
+                } else if constexpr (F8) {
 #pragma unroll
                     for (int ks = 0; ks < kBc / 16; ++ks) {
                         bf16x8 pb;
@@ -613,6 +748,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                             oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
                         }
                     }
+                } else {
+                    // A operand lane (i, half h), element e: V^T[column i][key
+                    // 16 ks + 8 (e / 4) + 4 h + e % 4], the key order of the P^T
+                    // registers: two transposing reads of four keys each.
+                    pv_direct<D, 0>(st, oacc, vaddr, rs16, ones, vpart);
                 }
                 l16_run += rs16;
             }
@@ -623,7 +763,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 else if constexpr (F8)
                     store_block8<D>(stage, sm, buf ^ 1, tid);
                 else
-                    store_block<D>(stage, sm, buf ^ 1, tid);
+                    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
             }
             __syncthreads();
             if (!has_next) break;
