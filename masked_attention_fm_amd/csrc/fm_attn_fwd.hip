@@ -92,20 +92,24 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, bf16x2 ones, float acc) {
 //   * K, pitch 1024 + 16 B.  The score product reads 16 bytes of one key per
 //     lane, eight consecutive keys per 8-lane phase: consecutive keys are in
 //     consecutive segments, 16 bytes apart modulo 128.
-//   * V, pitch 1024 + 32 B.  The PV product needs V^T, read with
+//   * V, pitch 1024 + 64 B.  The PV product needs V^T, read with
 //     ds_read_b64_tr_b16: within each 16-lane group, local lane i receives
 //     element i % 4 of the 8-byte pieces addressed by lanes 4 e + i / 4,
 //     e = 0..3 (verified by an in-bounds probe).  Lane 4 e + c addresses key
 //     kappa0 + e, columns n0 + 4 c .. + 3, so lane i ends up with column
-//     n0 + i of keys kappa0 .. kappa0 + 3.  The four keys are in consecutive
-//     segments, 32 bytes apart modulo 128: one 128-byte sweep per group.
+//     n0 + i of keys kappa0 .. kappa0 + 3.  The read serves 32 lanes per pass
+//     (two groups: the two 16-column halves of the same four keys); the four
+//     keys are in consecutive segments, 64 bytes apart modulo 256, and the
+//     column halves 32 bytes apart: one 256-byte sweep per pass (a probe
+//     measured no bank conflicts; a 32-byte pitch remainder gave two-way
+//     conflicts).
 template <int D>
 struct Direct {
     static constexpr int kRowBytes = 2 * D;
     static constexpr int kSegKeys = 1024 / kRowBytes;
     static constexpr int kSegs = kBc / kSegKeys;
     static constexpr int kKPitch = 1024 + 16;
-    static constexpr int kVPitch = 1024 + 32;
+    static constexpr int kVPitch = 1024 + 64;
     static constexpr int kKBytes = kSegs * kKPitch;
     static constexpr int kVBytes = kSegs * kVPitch;
     static constexpr int kSegsPerWave = kSegs / kWaves;
