@@ -1,10 +1,13 @@
 """Benchmark of the FlashMask forward path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2] [--no-per-config]
-                    [--no-cpu-baseline] [--no-backward] [--no-fp8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-seconds S] [--config C2]
+                    [--no-per-config] [--no-cpu-baseline] [--no-backward] [--no-fp8]
 
 A step is one fm_attn_fwd call (interval preprocessor + scheduler + attention
-kernel) over one batch of the workload, inputs resident in HBM.  Prints ONE
+kernel) over one batch of the workload, inputs resident in HBM.  Untimed
+warm-up: W steps, then more until S seconds (default 1) have run, so that the
+GPU's clocks have reached their sustained level (S / 4 for the other legs).
+Prints ONE
 JSON line: effective TFLOP/s counting 4*d FLOPs per attended (query, key)
 pair, the attention kernel's roofline figures (its own duration measured with
 HIP events the library records on its stream), the other workloads' figures
@@ -33,6 +36,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="after the W warm-up steps, keep warming up (untimed) until this many seconds of "
+                         "GPU work have run (the main workload; other legs use a quarter of it): the "
+                         "GPU's clocks take a while to reach their sustained level")
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -71,7 +78,20 @@ def tile_stats(fm, spec, cfg, dev):
             "tile_executed_flops": executed}
 
 
-def time_config(cfg, steps, warmup, with_kernel_timer=True):
+def warm_up(step, count, seconds):
+    """count untimed calls of step(), then more until `seconds` of wall time have passed."""
+    import torch
+    for _ in range(count):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
+def time_config(cfg, steps, warmup, with_kernel_timer=True, warm_s=0.0):
     import torch
     from masked_attention_fm_amd import flashmask as fm
     from masked_attention_fm_amd import inputs, metrics
@@ -94,9 +114,7 @@ def time_config(cfg, steps, warmup, with_kernel_timer=True):
     # rows with several ranges ([B, K, N] intervals) take the multi-range entry point
     attn = fm.fm_attn_fwd_multi if spec.col_start.ndim == 3 else fm.fm_attn_fwd
 
-    for _ in range(warmup):
-        attn(q, k, v, cs, ce, scale, out=out, lse=lse, stream=stream)
-    torch.cuda.synchronize()
+    warm_up(lambda: attn(q, k, v, cs, ce, scale, out=out, lse=lse, stream=stream), warmup, warm_s)
     fm.fm_profile_read()                       # drop anything recorded before
 
     # Pass 1: the timed steps, uninstrumented.
@@ -148,7 +166,7 @@ def time_config(cfg, steps, warmup, with_kernel_timer=True):
     return res
 
 
-def time_backward(cfg, steps, warmup):
+def time_backward(cfg, steps, warmup, warm_s=0.0):
     """fm_attn_bwd steps on the workload (inputs resident: q, k, v, the forward's out and
     lse, and a bf16 N(0,1) upstream gradient).  Algorithmic work: 10 d FLOPs per attended
     pair (five products of 2 d: the recomputed scores, dV, dP, dK, dQ)."""
@@ -170,8 +188,8 @@ def time_backward(cfg, steps, warmup):
     dout = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        bwd(q, k, v, out, dout, lse, cs, ce, scale, dq=dq, dk=dk, dv=dv, stream=stream)
+    warm_up(lambda: bwd(q, k, v, out, dout, lse, cs, ce, scale, dq=dq, dk=dk, dv=dv, stream=stream), warmup,
+            warm_s)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -188,7 +206,7 @@ def time_backward(cfg, steps, warmup):
     return {"ms_per_step": ms, "effective_flops": flops, "effective_tflops": flops / (ms * 1e-3) / 1e12}
 
 
-def time_fp8(cfg, steps, warmup, mode):
+def time_fp8(cfg, steps, warmup, mode, warm_s=0.0):
     """fm_attn_fwd_fp8 steps in the given mode on the workload's draws quantized per tensor
     to e4m3 (inputs resident); same 4 d FLOPs per attended pair as the bf16 forward."""
     import torch
@@ -205,8 +223,8 @@ def time_fp8(cfg, steps, warmup, mode):
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
     scale = inputs.default_scale(cfg.d)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream, mode=mode)
+    warm_up(lambda: fm.fm_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, cs, ce, scale, out=out, lse=lse, stream=stream,
+                                       mode=mode), warmup, warm_s)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -293,7 +311,8 @@ def main():
     fm.lib()
 
     cfg = inputs.CONFIGS[args.config]
-    main_res = time_config(cfg, args.steps, args.warmup)
+    leg_s = args.warmup_seconds / 4
+    main_res = time_config(cfg, args.steps, args.warmup, warm_s=args.warmup_seconds)
     log(f"{cfg.key}: {main_res['effective_tflops']:.1f} TFLOP/s effective, {main_res['ms_per_step']:.4f} ms/step")
 
     per_config = {}
@@ -302,7 +321,7 @@ def main():
             if key == cfg.key:
                 continue
             steps = 200 if c.N <= 1024 else max(5, min(args.steps, 20))
-            r = time_config(c, steps, min(args.warmup, 5))
+            r = time_config(c, steps, min(args.warmup, 5), warm_s=leg_s)
             log(f"{key}: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
             per_config[key] = {k: r[k] for k in ("workload", "ranges_per_row", "ms_per_step", "effective_tflops",
                                                  "pct_of_bf16_peak", "attn_kernel_ms", "attn_kernel_tflops",
@@ -315,7 +334,7 @@ def main():
             if key != cfg.key and args.no_per_config:
                 continue
             steps = 100 if c.N <= 1024 else max(5, min(args.steps, 20))
-            r = time_backward(c, steps, min(args.warmup, 3))
+            r = time_backward(c, steps, min(args.warmup, 3), warm_s=leg_s)
             log(f"{key} backward: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
             backward[key] = r
 
@@ -325,10 +344,10 @@ def main():
             if key != cfg.key and args.no_per_config:
                 continue
             steps = 200 if c.N <= 1024 else max(5, min(args.steps, 20))
-            r = time_fp8(c, steps, min(args.warmup, 5), fm.FM_FP8_SCORES)
+            r = time_fp8(c, steps, min(args.warmup, 5), fm.FM_FP8_SCORES, warm_s=leg_s)
             log(f"{key} fp8: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
             fp8[key] = r
-            r = time_fp8(c, steps, min(args.warmup, 5), fm.FM_FP8_ALL)
+            r = time_fp8(c, steps, min(args.warmup, 5), fm.FM_FP8_ALL, warm_s=leg_s)
             log(f"{key} fp8 weights: {r['effective_tflops']:.1f} TFLOP/s effective, {r['ms_per_step']:.4f} ms/step")
             fp8_all[key] = r
 
@@ -354,7 +373,7 @@ def main():
         "traffic_source": counters.get("file") if counters else None,
         "mfma_busy": counters.get("mfma_busy_per_cu_busy") if counters else None,
         "lds_bank_conflict_cycles": counters.get("lds_bank_conflict_cycles") if counters else None,
-        "kernel": f"attn_fwd_kernel<{cfg.d}, {main_res['ranges_per_row']}>",
+        "kernel": f"attn_fwd_kernel<{cfg.d}, {main_res['ranges_per_row']}, 0>",   # <d, ranges per row, bf16>
         "kernel_ms": kms,
         "algorithmic_flops_per_launch": main_res["effective_flops"],
     }
@@ -370,6 +389,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_seconds": args.warmup_seconds,
         "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
