@@ -21,9 +21,12 @@
 //   * bwd_dq_kernel: one workgroup per (b, h, query block of kBr = 128 rows),
 //     the forward's structure: S^T = K Q^T and dP^T = V dO^T with Q and dO in
 //     registers, then dQ^T += K^T dS^T, walking the union of the non-skip key
-//     blocks.  A lane ends up holding one query's dQ row.
-// Both double-buffer their operands through LDS (one barrier per step) and
-// run one workgroup per CU (their LDS rings exceed half of the 160 KB).
+//     blocks.  K and V are loaded straight into LDS; K^T is read with
+//     transposing LDS reads.  Two workgroups per CU.  A lane ends up holding
+//     one query's dQ row.
+// Both double-buffer their operands through LDS (one barrier per step); the
+// dK/dV kernel runs one workgroup per CU (its LDS ring exceeds half of the
+// 160 KB).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -409,54 +412,146 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------- dQ
 
+// K and V blocks loaded straight from global memory into LDS (buffer loads
+// with an LDS destination: one instruction writes lane l's 16 bytes to
+// M0 + 16 l, a 1 KB segment per wavefront).  A segment holds kSegKeys key
+// rows (4 at d = 128, 8 at d = 64); segments are padded to 1024 + 16 bytes.
+// Rows past N read as zero (the buffer range check).
+//   * V is read row-major only (dP^T = V dO^T): key kappa sits in segment
+//     kappa % kSegs, slot kappa / kSegs, so the eight consecutive keys of a
+//     ds_read_b128 phase land 16 bytes apart modulo 128.
+//   * K is read row-major (S^T = K Q^T) and transposed (dQ^T += K^T dS^T,
+//     ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+//     i % 4 of the 8-byte pieces addressed by lanes 4 e + i / 4).  Its segment
+//     index is swizzled at d = 128, kappa % 16 = 4 a + b -> segment 4 b + a, so
+//     that both patterns are free of bank conflicts: sixteen consecutive keys
+//     still occupy sixteen segments, and the four consecutive keys of a
+//     transposing read sit four segments (64 bytes modulo 256) apart, the two
+//     column halves of a 32-lane pass 32 bytes apart.
+template <int D>
+struct DqLayout {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kSegKeys = 1024 / kRowBytes;
+    static constexpr int kSegs = kBc / kSegKeys;
+    static constexpr int kPitch = 1024 + 16;
+    static constexpr int kBytes = kSegs * kPitch;
+    static constexpr int kSegsPerWave = kSegs / kWaves;
+    static_assert(kSegKeys * kSegs == kBc && kSegsPerWave * kWaves == kSegs, "segments split evenly");
+};
+
+// segment of K holding key kappa (x = kappa % kSegs)
+template <int D>
+__device__ __forceinline__ int k_segment(int x) {
+    if constexpr (D == 128)
+        return 4 * (x & 3) + (x >> 2);
+    else
+        return x;
+}
+
 template <int D, int NIV>
 struct alignas(16) DqSmem {
-    alignas(16) uint16_t k[2][kBc][D + kPad];       // K block, row-major
-    alignas(16) uint16_t v[2][kBc][D + kPad];       // V block, row-major
-    alignas(16) uint16_t kt[2][D][kBc + kPad];      // K block, transposed, keys in vt_pos order
+    alignas(16) uint8_t k[2][DqLayout<D>::kBytes];
+    alignas(16) uint8_t v[2][DqLayout<D>::kBytes];
     int start[NIV][kBr];
     int width[NIV][kBr];
 };
 
-template <int D>
-struct DqStage {
-    static constexpr int kItems = (kBc / 4) * (D / 8);   // 4 keys x 8 columns per item
-    static_assert(kItems <= kThreads, "one item per thread at most");
-    u32x4 k[4];
-    u32x4 v[4];
-};
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int D>
-__device__ __forceinline__ void dq_load(DqStage<D>& st, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                        int kv0, int tid) {
-    if (DqStage<D>::kItems == kThreads || tid < DqStage<D>::kItems) {
-        const int j0 = 4 * (tid % (kBc / 4));
-        const int n0 = 8 * (tid / (kBc / 4));
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+// This wavefront's segments of the key block at kv0: K (kvoff: K's lane
+// offset) and V (vvoff), segment U of the wavefront's share per instruction.
+template <int D, int NIV, int U = 0>
+__device__ __forceinline__ void dq_load_direct(DqSmem<D, NIV>& sm, int buf, __amdgpu_buffer_rsrc_t krs,
+                                               __amdgpu_buffer_rsrc_t vrs, int kvoff, int vvoff, int kv0,
+                                               int wave_u) {
+    using L = DqLayout<D>;
+    if constexpr (U < L::kSegsPerWave) {
+        const int seg = wave_u * L::kSegsPerWave + U;
+        const int base = kv0 * L::kRowBytes;
+        // K segment seg = wave_u kSegsPerWave + U holds keys whose swizzled index is seg
+        constexpr int kUStep = D == 128 ? 4 * L::kRowBytes : L::kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)&sm.k[buf][seg * L::kPitch], 16,
+                                                 base + kvoff + U * kUStep, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)&sm.v[buf][seg * L::kPitch], 16,
+                                                 base + vvoff + U * L::kRowBytes, 0, 0, 0);
+        dq_load_direct<D, NIV, U + 1>(sm, buf, krs, vrs, kvoff, vvoff, kv0, wave_u);
+    }
+}
+
+// ---- transposing K reads for the dQ product, issued through inline assembly
+// (the builtin would make the compiler wait for the next block's in-flight
+// loads before each read).  LDS operations complete in issue order, so
+// lgkmcnt(n) after n younger reads guarantees the older ones; each wait
+// passes the registers through itself so nothing can use them earlier.
+template <int OFF>
+__device__ __forceinline__ v4s lds_read_tr16(uint32_t addr) {
+    v4s r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// Step KS (16 keys): part[2 nb + r] holds, for lane (column i, half h), keys
+// 16 KS + 8 r + 4 h + 0..3 of column 32 nb + i.
+template <int D, int KS, int I = 0>
+__device__ __forceinline__ void issue_kt_reads(v4s (&part)[2 * D / 32], uint32_t addr) {
+    using L = DqLayout<D>;
+    if constexpr (I < 2 * D / 32) {
+        constexpr int nb = I / 2, r = I % 2;
+        constexpr int off = D == 128 ? 2 * r * L::kPitch + KS * L::kRowBytes + nb * 64
+                                     : (2 * KS + r) * L::kRowBytes + nb * 64;
+        static_assert(off >= 0 && off < 65536, "ds offset field");
+        part[I] = lds_read_tr16<off>(addr);
+        issue_kt_reads<D, KS, I + 1>(part, addr);
+    }
+}
+
+template <int CNT, int NP>
+__device__ __forceinline__ void wait_lds_tied(v4s (&p)[NP]) {
+    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
+    if constexpr (NP == 8)
+        asm volatile("s_waitcnt lgkmcnt(%8)"
+                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                       "+v"(p[7])
+                     : "i"(CNT));
+    else if constexpr (NP == 4)
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]) : "i"(CNT));
+    else
+        static_assert(NP == 8 || NP == 4, "d = 64 or 128");
+}
+
+// dQ^T += K^T dS^T over steps KS.. of one key block (cur: step KS's reads).
+template <int D, int KS>
+__device__ __forceinline__ void dq_product(const floatx16 (&dst)[kBc / 32], floatx16 (&dqacc)[D / 32],
+                                           uint32_t addr, v4s (&cur)[2 * D / 32]) {
+    constexpr int NP = 2 * D / 32;
+    if constexpr (KS < kBc / 16) {
+        bf16x8 sb;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int off = ((kv0 + j0 + r) * D + n0) * 2;
-            st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-            st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+        for (int e = 0; e < 8; ++e) sb[e] = (__bf16)dst[KS >> 1][8 * (KS & 1) + e];
+        v4s next[NP];
+        if constexpr (KS + 1 < kBc / 16) {
+            issue_kt_reads<D, KS + 1>(next, addr);
+            wait_lds_tied<NP>(cur);
+        } else {
+            wait_lds_tied<0>(cur);
         }
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(cur[2 * nb], cur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            dqacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dqacc[nb], 0, 0, 0);
+        }
+        dq_product<D, KS + 1>(dst, dqacc, addr, next);
     }
 }
 
 template <int D, int NIV>
-__device__ __forceinline__ void dq_store(const DqStage<D>& st, DqSmem<D, NIV>& sm, int buf, int tid) {
-    if (DqStage<D>::kItems == kThreads || tid < DqStage<D>::kItems) {
-        const int j0 = 4 * (tid % (kBc / 4));
-        const int n0 = 8 * (tid / (kBc / 4));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<u32x4*>(&sm.k[buf][j0 + r][n0]) = st.k[r];
-            *reinterpret_cast<u32x4*>(&sm.v[buf][j0 + r][n0]) = st.v[r];
-        }
-        store_transposed_4x8(st.k, &sm.kt[buf][0][0], kBc + kPad, n0, vt_pos(j0));
-    }
-}
-
-template <int D, int NIV>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, const TileMeta* __restrict__ meta,
@@ -532,16 +627,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + bh * N * D, N * D * 2);
     const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + bh * N * D, N * D * 2);
 
+    // Lane offsets of the loads and of the operand reads (see DqLayout).
+    using DL = DqLayout<D>;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int slot_l = lane / (D / 8), chunk_l = lane % (D / 8);
+    const int kvoff = ((D == 128 ? wave_u : 2 * wave_u) + DL::kSegs * slot_l) * DL::kRowBytes + 16 * chunk_l;
+    const int vvoff = (wave_u * DL::kSegsPerWave + DL::kSegs * slot_l) * DL::kRowBytes + 16 * chunk_l;
+    const int k_lane = k_segment<D>(r32 % DL::kSegs) * DL::kPitch + (r32 / DL::kSegs) * DL::kRowBytes + 16 * half;
+    const int v_lane = (r32 % DL::kSegs) * DL::kPitch + (r32 / DL::kSegs) * DL::kRowBytes + 16 * half;
+    const int a4 = (lane & 15) >> 2;
+    const int kt_lane = (D == 128 ? 4 * a4 + half : 4 * half + a4) * DL::kPitch + 32 * ((lane >> 4) & 1) +
+                        8 * (lane & 3);
+
     int j = union_next<NIV>(tm, -1);
     if (j != INT_MAX) {
-        DqStage<D> stage;
-        dq_load<D>(stage, krs, vrs, j * kBc, tid);
-        dq_store<D, NIV>(stage, sm, 0, tid);
+        dq_load_direct<D, NIV>(sm, 0, krs, vrs, kvoff, vvoff, j * kBc, wave_u);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int buf = 0;; buf ^= 1) {
             const int j_next = union_next<NIV>(tm, j);
             const bool has_next = j_next != INT_MAX;
-            if (has_next) dq_load<D>(stage, krs, vrs, j_next * kBc, tid);
+            if (has_next) dq_load_direct<D, NIV>(sm, buf ^ 1, krs, vrs, kvoff, vvoff, j_next * kBc, wave_u);
 
             const int klo = j * kBc;
             const int khi = min(klo + kBc, N) - 1;
@@ -564,9 +670,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
                 for (int cs = 0; cs < D / 16; ++cs) {
 #pragma unroll
                     for (int jb = 0; jb < kBc / 32; ++jb) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][jb * 32 + r32][cs * 16 + half * 8]);
+                        const int at = jb * (32 / DL::kSegs) * DL::kRowBytes + cs * 32;
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][k_lane + at]);
                         st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
-                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&sm.v[buf][jb * 32 + r32][cs * 16 + half * 8]);
+                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&sm.v[buf][v_lane + at]);
                         dpt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, greg[cs], dpt[jb], 0, 0, 0);
                     }
                 }
@@ -590,20 +697,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
                         dpt[jb][v] = pm * (dpt[jb][v] - drow);
                     }
                 }
-                // ---- dQ^T += K^T dS^T
-#pragma unroll
-                for (int ks = 0; ks < kBc / 16; ++ks) {
-                    bf16x8 sb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sb[e] = (__bf16)dpt[ks >> 1][8 * (ks & 1) + e];
-#pragma unroll
-                    for (int nb = 0; nb < D / 32; ++nb) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.kt[buf][nb * 32 + r32][16 * ks + 8 * half]);
-                        dqacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dqacc[nb], 0, 0, 0);
-                    }
-                }
+                // ---- dQ^T += K^T dS^T: A operand lane (column i, half h), element e:
+                // K^T[i][key 16 ks + 8 (e / 4) + 4 h + e % 4], the key order of dS^T
+                // in the registers; two transposing reads of four keys each.
+                const uint32_t kaddr = lds_address(&sm.k[buf][0]) + kt_lane;
+                v4s kpart[2 * D / 32];
+                issue_kt_reads<D, 0>(kpart, kaddr);
+                dq_product<D, 0>(dpt, dqacc, kaddr, kpart);
             }
-            if (has_next) dq_store<D, NIV>(stage, sm, buf ^ 1, tid);
+            if (has_next) __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
             __syncthreads();
             if (!has_next) break;
             j = j_next;
