@@ -16,8 +16,9 @@
 //     as MFMA B operands and walks the query chunks (kBwdRows = 64 rows) whose
 //     non-skip ranges hold its key block: S = Q K^T and dP = dO V^T with Q and
 //     dO read from LDS; then dV^T += dO^T P and dK^T += Q^T dS with P and dS
-//     taken straight from the registers (the vt_pos key order) and Q^T, dO^T
-//     staged transposed in LDS.  A lane ends up holding one key's dK and dV row.
+//     taken straight from the registers and Q^T, dO^T read with transposing
+//     LDS reads in the same row order.  Q and dO are loaded straight into LDS.
+//     A lane ends up holding one key's dK and dV row.
 //   * bwd_dq_kernel: one workgroup per (b, h, query block of kBr = 128 rows),
 //     the forward's structure: S^T = K Q^T and dP^T = V dO^T with Q and dO in
 //     registers, then dQ^T += K^T dS^T, walking the union of the non-skip key
@@ -25,8 +26,8 @@
 //     transposing LDS reads.  Two workgroups per CU.  A lane ends up holding
 //     one query's dQ row.
 // Both double-buffer their operands through LDS (one barrier per step); the
-// dK/dV kernel runs one workgroup per CU (its LDS ring exceeds half of the
-// 160 KB).
+// dK/dV kernel runs one wavefront per SIMD (its live state fills the register
+// file).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -39,7 +40,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPad = 8;                        // bf16 padding per LDS operand row (16 B)
 
 static_assert(kBwdKeys == 32 * kWaves, "one 32-key MFMA column block per wavefront");
 static_assert(kBr == 32 * kWaves, "one 32-row MFMA column block per wavefront");
@@ -132,45 +132,237 @@ __device__ __forceinline__ int4 wave_row_bounds(int s, int w, bool in_seq) {
                      wave_min(any ? s + w : (in_seq ? INT_MIN : INT_MAX)));
 }
 
+// Blocks of 64 rows (keys for dQ, query rows for dK/dV) loaded straight from
+// global memory into LDS (buffer loads with an LDS destination: one
+// instruction writes lane l's 16 bytes to M0 + 16 l, a 1 KB segment per
+// wavefront).  A segment holds kSegKeys rows (4 at d = 128, 8 at d = 64);
+// segments are padded to 1024 + 16 bytes.  Rows past N read as zero (the
+// buffer range check).
+//   * A block read row-major only (V in dP^T = V dO^T) keeps row rho in
+//     segment rho % kSegs, slot rho / kSegs, so the eight consecutive rows of a
+//     ds_read_b128 phase land 16 bytes apart modulo 128.
+//   * A block read row-major and transposed (K for dQ; Q and dO for dK/dV;
+//     ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+//     i % 4 of the 8-byte pieces addressed by lanes 4 e + i / 4) has its
+//     segment index swizzled at d = 128, rho % 16 = 4 a + b -> segment 4 b + a,
+//     so that both patterns are free of bank conflicts: sixteen consecutive
+//     rows still occupy sixteen segments, and the four consecutive rows of a
+//     transposing read sit four segments (64 bytes modulo 256) apart, the two
+//     column halves of a 32-lane pass 32 bytes apart.
+template <int D>
+struct SegLayout {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kSegKeys = 1024 / kRowBytes;
+    static constexpr int kSegs = kBc / kSegKeys;
+    static constexpr int kPitch = 1024 + 16;
+    static constexpr int kBytes = kSegs * kPitch;
+    static constexpr int kSegsPerWave = kSegs / kWaves;
+    static_assert(kSegKeys * kSegs == kBc && kSegsPerWave * kWaves == kSegs, "segments split evenly");
+};
+
+// segment of a swizzled block holding row rho (x = rho % kSegs)
+template <int D>
+__device__ __forceinline__ int k_segment(int x) {
+    if constexpr (D == 128)
+        return 4 * (x & 3) + (x >> 2);
+    else
+        return x;
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+// This lane's byte offset, inside a 64-row block, of its 16 bytes in the
+// first segment its wavefront fills.
+template <int D, bool SWZ>
+__device__ __forceinline__ int seg_lane_offset(int lane, int wave_u) {
+    using L = SegLayout<D>;
+    const int slot = lane / (D / 8), chunk = lane % (D / 8);
+    const int first = (SWZ && D == 128) ? wave_u : wave_u * L::kSegsPerWave;
+    return (first + L::kSegs * slot) * L::kRowBytes + 16 * chunk;
+}
+
+// This wavefront's segments of the 64-row block starting at row0 into dst
+// (the segment of index wave_u kSegsPerWave + U per instruction; the row is
+// selected through the lane offset, since an instruction offset would move
+// the LDS destination as well).
+template <int D, bool SWZ, int U = 0, typename Ptr>
+__device__ __forceinline__ void dma_rows(Ptr dst, __amdgpu_buffer_rsrc_t rs, int lane_off, int row0, int wave_u) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the LDS address-space cast exists in the device pass only
+    using L = SegLayout<D>;
+    if constexpr (U < L::kSegsPerWave) {
+        const int seg = wave_u * L::kSegsPerWave + U;
+        constexpr int kUStep = (SWZ && D == 128) ? 4 * L::kRowBytes : L::kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + seg * L::kPitch), 16,
+                                                 row0 * L::kRowBytes + lane_off + U * kUStep, 0, 0, 0);
+        dma_rows<D, SWZ, U + 1, Ptr>(dst, rs, lane_off, row0, wave_u);
+    }
+#endif
+}
+
+// ---- transposing K reads for the dQ product, issued through inline assembly
+// (the builtin would make the compiler wait for the next block's in-flight
+// loads before each read).  LDS operations complete in issue order, so
+// lgkmcnt(n) after n younger reads guarantees the older ones; each wait
+// passes the registers through itself so nothing can use them earlier.
+template <int OFF>
+__device__ __forceinline__ v4s lds_read_tr16(uint32_t addr) {
+    v4s r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// Step KS (16 keys): part[2 nb + r] holds, for lane (column i, half h), keys
+// 16 KS + 8 r + 4 h + 0..3 of column 32 nb + i.
+template <int D, int KS, int I = 0>
+__device__ __forceinline__ void issue_kt_reads(v4s (&part)[2 * D / 32], uint32_t addr) {
+    using L = SegLayout<D>;
+    if constexpr (I < 2 * D / 32) {
+        constexpr int nb = I / 2, r = I % 2;
+        constexpr int off = D == 128 ? 2 * r * L::kPitch + KS * L::kRowBytes + nb * 64
+                                     : (2 * KS + r) * L::kRowBytes + nb * 64;
+        static_assert(off >= 0 && off < 65536, "ds offset field");
+        part[I] = lds_read_tr16<off>(addr);
+        issue_kt_reads<D, KS, I + 1>(part, addr);
+    }
+}
+
+template <int CNT, int NP>
+__device__ __forceinline__ void wait_lds_tied(v4s (&p)[NP]) {
+    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
+    if constexpr (NP == 8)
+        asm volatile("s_waitcnt lgkmcnt(%8)"
+                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                       "+v"(p[7])
+                     : "i"(CNT));
+    else if constexpr (NP == 4)
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]) : "i"(CNT));
+    else
+        static_assert(NP == 8 || NP == 4, "d = 64 or 128");
+}
+
+// dQ^T += K^T dS^T over steps KS.. of one key block (cur: step KS's reads).
+template <int D, int KS>
+__device__ __forceinline__ void dq_product(const floatx16 (&dst)[kBc / 32], floatx16 (&dqacc)[D / 32],
+                                           uint32_t addr, v4s (&cur)[2 * D / 32]) {
+    constexpr int NP = 2 * D / 32;
+    if constexpr (KS < kBc / 16) {
+        bf16x8 sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb[e] = (__bf16)dst[KS >> 1][8 * (KS & 1) + e];
+        v4s next[NP];
+        if constexpr (KS + 1 < kBc / 16) {
+            issue_kt_reads<D, KS + 1>(next, addr);
+            wait_lds_tied<NP>(cur);
+        } else {
+            wait_lds_tied<0>(cur);
+        }
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(cur[2 * nb], cur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            dqacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dqacc[nb], 0, 0, 0);
+        }
+        dq_product<D, KS + 1>(dst, dqacc, addr, next);
+    }
+}
+
+// Two-operand variant of wait_lds_tied (both arrays passed through).
+template <int CNT, int NP>
+__device__ __forceinline__ void wait_lds_tied2(v4s (&p)[NP], v4s (&q)[NP]) {
+    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
+    if constexpr (NP == 8)
+        asm volatile("s_waitcnt lgkmcnt(%16)"
+                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                       "+v"(p[7]), "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
+                       "+v"(q[6]), "+v"(q[7])
+                     : "i"(CNT));
+    else if constexpr (NP == 4)
+        asm volatile("s_waitcnt lgkmcnt(%8)"
+                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(q[0]), "+v"(q[1]), "+v"(q[2]),
+                       "+v"(q[3])
+                     : "i"(CNT));
+    else
+        static_assert(NP == 8 || NP == 4, "d = 64 or 128");
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS over steps KS.. of one query chunk (gcur,
+// qcur: step KS's transposing reads of dO and Q).  Per step: the next step's
+// dO reads are issued, then this step's reads of both are waited for (they
+// are older than those), the dV products run, the next step's Q reads are
+// issued, and the dK products run.
+template <int D, int KS>
+__device__ __forceinline__ void dkv_products(const floatx16 (&p)[kBwdRows / 32], const floatx16 (&ds)[kBwdRows / 32],
+                                             floatx16 (&dvacc)[D / 32], floatx16 (&dkacc)[D / 32], uint32_t gaddr,
+                                             uint32_t qaddr, v4s (&gcur)[2 * D / 32], v4s (&qcur)[2 * D / 32]) {
+    constexpr int NP = 2 * D / 32;
+    if constexpr (KS < kBwdRows / 16) {
+        bf16x8 pb, sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pb[e] = (__bf16)p[KS >> 1][8 * (KS & 1) + e];
+            sb[e] = (__bf16)ds[KS >> 1][8 * (KS & 1) + e];
+        }
+        v4s gnext[NP], qnext[NP];
+        if constexpr (KS + 1 < kBwdRows / 16) {
+            issue_kt_reads<D, KS + 1>(gnext, gaddr);
+            wait_lds_tied2<NP>(gcur, qcur);
+        } else {
+            wait_lds_tied2<0>(gcur, qcur);
+        }
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(gcur[2 * nb], gcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            dvacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, dvacc[nb], 0, 0, 0);
+        }
+        if constexpr (KS + 1 < kBwdRows / 16) issue_kt_reads<D, KS + 1>(qnext, qaddr);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(qcur[2 * nb], qcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            dkacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dkacc[nb], 0, 0, 0);
+        }
+        dkv_products<D, KS + 1>(p, ds, dvacc, dkacc, gaddr, qaddr, gnext, qnext);
+    }
+}
+
 // ---------------------------------------------------------------- dK, dV
+
+static_assert(kBwdRows == kBc, "query chunks use the 64-row segment layout");
 
 template <int D, int NIV>
 struct alignas(16) DkvSmem {
-    alignas(16) uint16_t q[2][kBwdRows][D + kPad];      // Q chunk, row-major
-    alignas(16) uint16_t qt[2][D][kBwdRows + kPad];     // Q chunk, transposed, rows in vt_pos order
-    alignas(16) uint16_t go[2][kBwdRows][D + kPad];     // dO chunk, row-major
-    alignas(16) uint16_t got[2][D][kBwdRows + kPad];    // dO chunk, transposed, rows in vt_pos order
+    alignas(16) uint8_t q[2][SegLayout<D>::kBytes];     // Q chunk, swizzled segments
+    alignas(16) uint8_t go[2][SegLayout<D>::kBytes];    // dO chunk, swizzled segments
     alignas(16) float lse2[2][kBwdRows];                // LSE * log2 e (+inf past N)
     alignas(16) float dd[2][kBwdRows];                  // D (0 past N)
     alignas(16) int start[2][NIV][kBwdRows];
     alignas(16) int width[2][NIV][kBwdRows];
 };
 
+// Per-row values of a chunk staged through registers (Q and dO go straight
+// into LDS).
 template <int D, int NIV>
 struct DkvStage {
-    static constexpr int kItems = (kBwdRows / 4) * (D / 8);    // 4 rows x 8 columns per item
-    static_assert(kItems <= kThreads, "one item per thread at most");
-    u32x4 q[4];
-    u32x4 go[4];
     float lse2, dd;
     int s[NIV], w[NIV];
 };
 
+// Chunk starting at row0 into buffer buf: Q and dO straight into LDS (loff:
+// this lane's segment offset), the per-row values into registers.
 template <int D, int NIV>
-__device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, __amdgpu_buffer_rsrc_t qrs,
-                                         __amdgpu_buffer_rsrc_t grs, const float* __restrict__ lse_bh,
+__device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, DkvSmem<D, NIV>& sm, int buf,
+                                         __amdgpu_buffer_rsrc_t qrs, __amdgpu_buffer_rsrc_t grs, int loff,
+                                         int wave_u, const float* __restrict__ lse_bh,
                                          const float* __restrict__ dd_bh, const int32_t* __restrict__ cs_b,
                                          const int32_t* __restrict__ ce_b, int row0, int N, int tid) {
-    if (DkvStage<D, NIV>::kItems == kThreads || tid < DkvStage<D, NIV>::kItems) {
-        const int r0 = 4 * (tid % (kBwdRows / 4));
-        const int n0 = 8 * (tid / (kBwdRows / 4));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int off = ((row0 + r0 + r) * D + n0) * 2;
-            st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
-            st.go[r] = __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0);
-        }
-    }
+    dma_rows<D, true>(&sm.q[buf][0], qrs, loff, row0, wave_u);
+    dma_rows<D, true>(&sm.go[buf][0], grs, loff, row0, wave_u);
     if (tid < kBwdRows) {
         const int row = row0 + tid;
         if (row < N) {
@@ -196,17 +388,6 @@ __device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, __amdgpu_buffer_r
 
 template <int D, int NIV>
 __device__ __forceinline__ void dkv_store(const DkvStage<D, NIV>& st, DkvSmem<D, NIV>& sm, int buf, int tid) {
-    if (DkvStage<D, NIV>::kItems == kThreads || tid < DkvStage<D, NIV>::kItems) {
-        const int r0 = 4 * (tid % (kBwdRows / 4));
-        const int n0 = 8 * (tid / (kBwdRows / 4));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<u32x4*>(&sm.q[buf][r0 + r][n0]) = st.q[r];
-            *reinterpret_cast<u32x4*>(&sm.go[buf][r0 + r][n0]) = st.go[r];
-        }
-        store_transposed_4x8(st.q, &sm.qt[buf][0][0], kBwdRows + kPad, n0, vt_pos(r0));
-        store_transposed_4x8(st.go, &sm.got[buf][0][0], kBwdRows + kPad, n0, vt_pos(r0));
-    }
     if (tid < kBwdRows) {
         sm.lse2[buf][tid] = st.lse2;
         sm.dd[buf][tid] = st.dd;
@@ -288,18 +469,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int32_t* ce_b = col_end + ((int64_t)b * n_sets + set) * NIV * N;
     const int64_t meta_row = ((int64_t)set * (L / n_kb) + b) * n_qc;
 
+    // Lane offsets of the loads and of the operand reads (see SegLayout).
+    using SL = SegLayout<D>;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int loff = seg_lane_offset<D, true>(lane, wave_u);
+    const int q_lane = k_segment<D>(r32 % SL::kSegs) * SL::kPitch + (r32 / SL::kSegs) * SL::kRowBytes + 16 * half;
+    const int a4 = (lane & 15) >> 2;
+    const int t_lane = (D == 128 ? 4 * a4 + half : 4 * half + a4) * SL::kPitch + 32 * ((lane >> 4) & 1) +
+                       8 * (lane & 3);
+
     int t = range.z > 0 ? range.x : INT_MAX;
     if (t != INT_MAX) {
         DkvStage<D, NIV> stage;
-        dkv_load<D, NIV>(stage, qrs, grs, lse_bh, dd_bh, cs_b, ce_b, t * kBwdRows, N, tid);
+        dkv_load<D, NIV>(stage, sm, 0, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b, t * kBwdRows, N, tid);
         dkv_store<D, NIV>(stage, sm, 0, tid);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int buf = 0;; buf ^= 1) {
             int t_next = t + 1;
             while (t_next <= range.y && !chunk_live<NIV>(meta_c, meta_row + t_next, J)) ++t_next;
             const bool has_next = t_next <= range.y;
             if (has_next)
-                dkv_load<D, NIV>(stage, qrs, grs, lse_bh, dd_bh, cs_b, ce_b, t_next * kBwdRows, N, tid);
+                dkv_load<D, NIV>(stage, sm, buf ^ 1, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b,
+                                 t_next * kBwdRows, N, tid);
 
             // Does some row of the chunk attend the wavefront's keys, and does
             // one range cover them for every row?  Lane l looks at row l.
@@ -326,12 +518,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                 for (int cs = 0; cs < D / 16; ++cs) {
 #pragma unroll
                     for (int qb = 0; qb < kBwdRows / 32; ++qb) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.q[buf][qb * 32 + r32][cs * 16 + half * 8]);
+                        const int at = q_lane + qb * (32 / SL::kSegs) * SL::kRowBytes + cs * 32;
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.q[buf][at]);
                         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[cs], s[qb], 0, 0, 0);
-                        const bf16x8 g = *reinterpret_cast<const bf16x8*>(&sm.go[buf][qb * 32 + r32][cs * 16 + half * 8]);
+                        const bf16x8 g = *reinterpret_cast<const bf16x8*>(&sm.go[buf][at]);
                         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, vreg[cs], dp[qb], 0, 0, 0);
                     }
                 }
+                // transposing reads of the first step of the dV / dK products,
+                // issued now so that their latency overlaps the softmax
+                const uint32_t gaddr = lds_address(&sm.go[buf][0]) + t_lane;
+                const uint32_t qaddr = lds_address(&sm.q[buf][0]) + t_lane;
+                v4s gpart[2 * D / 32], qpart[2 * D / 32];
+                issue_kt_reads<D, 0>(gpart, gaddr);
+                issue_kt_reads<D, 0>(qpart, qaddr);
                 // ---- P = exp(scale s - LSE) inside the ranges, dS = P (dP - D)
 #pragma unroll
                 for (int qb = 0; qb < kBwdRows / 32; ++qb) {
@@ -367,24 +567,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     }
                 }
                 // ---- dV^T += dO^T P, dK^T += Q^T dS (contraction over the chunk's queries)
-#pragma unroll
-                for (int ks = 0; ks < kBwdRows / 16; ++ks) {
-                    bf16x8 pb, sb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        pb[e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
-                        sb[e] = (__bf16)dp[ks >> 1][8 * (ks & 1) + e];
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < D / 32; ++nb) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.got[buf][nb * 32 + r32][16 * ks + 8 * half]);
-                        dvacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, dvacc[nb], 0, 0, 0);
-                        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.qt[buf][nb * 32 + r32][16 * ks + 8 * half]);
-                        dkacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, dkacc[nb], 0, 0, 0);
-                    }
-                }
+                dkv_products<D, 0>(s, dp, dvacc, dkacc, gaddr, qaddr, gpart, qpart);
             }
-            if (has_next) dkv_store<D, NIV>(stage, sm, buf ^ 1, tid);
+            if (has_next) {
+                dkv_store<D, NIV>(stage, sm, buf ^ 1, tid);
+                __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
+            }
             __syncthreads();
             if (!has_next) break;
             t = t_next;
@@ -412,143 +600,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------- dQ
 
-// K and V blocks loaded straight from global memory into LDS (buffer loads
-// with an LDS destination: one instruction writes lane l's 16 bytes to
-// M0 + 16 l, a 1 KB segment per wavefront).  A segment holds kSegKeys key
-// rows (4 at d = 128, 8 at d = 64); segments are padded to 1024 + 16 bytes.
-// Rows past N read as zero (the buffer range check).
-//   * V is read row-major only (dP^T = V dO^T): key kappa sits in segment
-//     kappa % kSegs, slot kappa / kSegs, so the eight consecutive keys of a
-//     ds_read_b128 phase land 16 bytes apart modulo 128.
-//   * K is read row-major (S^T = K Q^T) and transposed (dQ^T += K^T dS^T,
-//     ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
-//     i % 4 of the 8-byte pieces addressed by lanes 4 e + i / 4).  Its segment
-//     index is swizzled at d = 128, kappa % 16 = 4 a + b -> segment 4 b + a, so
-//     that both patterns are free of bank conflicts: sixteen consecutive keys
-//     still occupy sixteen segments, and the four consecutive keys of a
-//     transposing read sit four segments (64 bytes modulo 256) apart, the two
-//     column halves of a 32-lane pass 32 bytes apart.
-template <int D>
-struct DqLayout {
-    static constexpr int kRowBytes = 2 * D;
-    static constexpr int kSegKeys = 1024 / kRowBytes;
-    static constexpr int kSegs = kBc / kSegKeys;
-    static constexpr int kPitch = 1024 + 16;
-    static constexpr int kBytes = kSegs * kPitch;
-    static constexpr int kSegsPerWave = kSegs / kWaves;
-    static_assert(kSegKeys * kSegs == kBc && kSegsPerWave * kWaves == kSegs, "segments split evenly");
-};
-
-// segment of K holding key kappa (x = kappa % kSegs)
-template <int D>
-__device__ __forceinline__ int k_segment(int x) {
-    if constexpr (D == 128)
-        return 4 * (x & 3) + (x >> 2);
-    else
-        return x;
-}
-
 template <int D, int NIV>
 struct alignas(16) DqSmem {
-    alignas(16) uint8_t k[2][DqLayout<D>::kBytes];
-    alignas(16) uint8_t v[2][DqLayout<D>::kBytes];
+    alignas(16) uint8_t k[2][SegLayout<D>::kBytes];
+    alignas(16) uint8_t v[2][SegLayout<D>::kBytes];
     int start[NIV][kBr];
     int width[NIV][kBr];
 };
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
-}
-
-// This wavefront's segments of the key block at kv0: K (kvoff: K's lane
-// offset) and V (vvoff), segment U of the wavefront's share per instruction.
-template <int D, int NIV, int U = 0>
-__device__ __forceinline__ void dq_load_direct(DqSmem<D, NIV>& sm, int buf, __amdgpu_buffer_rsrc_t krs,
-                                               __amdgpu_buffer_rsrc_t vrs, int kvoff, int vvoff, int kv0,
-                                               int wave_u) {
-    using L = DqLayout<D>;
-    if constexpr (U < L::kSegsPerWave) {
-        const int seg = wave_u * L::kSegsPerWave + U;
-        const int base = kv0 * L::kRowBytes;
-        // K segment seg = wave_u kSegsPerWave + U holds keys whose swizzled index is seg
-        constexpr int kUStep = D == 128 ? 4 * L::kRowBytes : L::kRowBytes;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)&sm.k[buf][seg * L::kPitch], 16,
-                                                 base + kvoff + U * kUStep, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)&sm.v[buf][seg * L::kPitch], 16,
-                                                 base + vvoff + U * L::kRowBytes, 0, 0, 0);
-        dq_load_direct<D, NIV, U + 1>(sm, buf, krs, vrs, kvoff, vvoff, kv0, wave_u);
-    }
-}
-
-// ---- transposing K reads for the dQ product, issued through inline assembly
-// (the builtin would make the compiler wait for the next block's in-flight
-// loads before each read).  LDS operations complete in issue order, so
-// lgkmcnt(n) after n younger reads guarantees the older ones; each wait
-// passes the registers through itself so nothing can use them earlier.
-template <int OFF>
-__device__ __forceinline__ v4s lds_read_tr16(uint32_t addr) {
-    v4s r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
-
-// Step KS (16 keys): part[2 nb + r] holds, for lane (column i, half h), keys
-// 16 KS + 8 r + 4 h + 0..3 of column 32 nb + i.
-template <int D, int KS, int I = 0>
-__device__ __forceinline__ void issue_kt_reads(v4s (&part)[2 * D / 32], uint32_t addr) {
-    using L = DqLayout<D>;
-    if constexpr (I < 2 * D / 32) {
-        constexpr int nb = I / 2, r = I % 2;
-        constexpr int off = D == 128 ? 2 * r * L::kPitch + KS * L::kRowBytes + nb * 64
-                                     : (2 * KS + r) * L::kRowBytes + nb * 64;
-        static_assert(off >= 0 && off < 65536, "ds offset field");
-        part[I] = lds_read_tr16<off>(addr);
-        issue_kt_reads<D, KS, I + 1>(part, addr);
-    }
-}
-
-template <int CNT, int NP>
-__device__ __forceinline__ void wait_lds_tied(v4s (&p)[NP]) {
-    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
-    if constexpr (NP == 8)
-        asm volatile("s_waitcnt lgkmcnt(%8)"
-                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
-                       "+v"(p[7])
-                     : "i"(CNT));
-    else if constexpr (NP == 4)
-        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]) : "i"(CNT));
-    else
-        static_assert(NP == 8 || NP == 4, "d = 64 or 128");
-}
-
-// dQ^T += K^T dS^T over steps KS.. of one key block (cur: step KS's reads).
-template <int D, int KS>
-__device__ __forceinline__ void dq_product(const floatx16 (&dst)[kBc / 32], floatx16 (&dqacc)[D / 32],
-                                           uint32_t addr, v4s (&cur)[2 * D / 32]) {
-    constexpr int NP = 2 * D / 32;
-    if constexpr (KS < kBc / 16) {
-        bf16x8 sb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sb[e] = (__bf16)dst[KS >> 1][8 * (KS & 1) + e];
-        v4s next[NP];
-        if constexpr (KS + 1 < kBc / 16) {
-            issue_kt_reads<D, KS + 1>(next, addr);
-            wait_lds_tied<NP>(cur);
-        } else {
-            wait_lds_tied<0>(cur);
-        }
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(cur[2 * nb], cur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            dqacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dqacc[nb], 0, 0, 0);
-        }
-        dq_product<D, KS + 1>(dst, dqacc, addr, next);
-    }
-}
 
 template <int D, int NIV>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
@@ -627,12 +685,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + bh * N * D, N * D * 2);
     const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + bh * N * D, N * D * 2);
 
-    // Lane offsets of the loads and of the operand reads (see DqLayout).
-    using DL = DqLayout<D>;
+    // Lane offsets of the loads and of the operand reads (see SegLayout).
+    using DL = SegLayout<D>;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int slot_l = lane / (D / 8), chunk_l = lane % (D / 8);
-    const int kvoff = ((D == 128 ? wave_u : 2 * wave_u) + DL::kSegs * slot_l) * DL::kRowBytes + 16 * chunk_l;
-    const int vvoff = (wave_u * DL::kSegsPerWave + DL::kSegs * slot_l) * DL::kRowBytes + 16 * chunk_l;
+    const int kvoff = seg_lane_offset<D, true>(lane, wave_u);
+    const int vvoff = seg_lane_offset<D, false>(lane, wave_u);
     const int k_lane = k_segment<D>(r32 % DL::kSegs) * DL::kPitch + (r32 / DL::kSegs) * DL::kRowBytes + 16 * half;
     const int v_lane = (r32 % DL::kSegs) * DL::kPitch + (r32 / DL::kSegs) * DL::kRowBytes + 16 * half;
     const int a4 = (lane & 15) >> 2;
@@ -641,13 +698,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
     int j = union_next<NIV>(tm, -1);
     if (j != INT_MAX) {
-        dq_load_direct<D, NIV>(sm, 0, krs, vrs, kvoff, vvoff, j * kBc, wave_u);
+        dma_rows<D, true>(&sm.k[0][0], krs, kvoff, j * kBc, wave_u);
+        dma_rows<D, false>(&sm.v[0][0], vrs, vvoff, j * kBc, wave_u);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int buf = 0;; buf ^= 1) {
             const int j_next = union_next<NIV>(tm, j);
             const bool has_next = j_next != INT_MAX;
-            if (has_next) dq_load_direct<D, NIV>(sm, buf ^ 1, krs, vrs, kvoff, vvoff, j_next * kBc, wave_u);
+            if (has_next) {
+                dma_rows<D, true>(&sm.k[buf ^ 1][0], krs, kvoff, j_next * kBc, wave_u);
+                dma_rows<D, false>(&sm.v[buf ^ 1][0], vrs, vvoff, j_next * kBc, wave_u);
+            }
 
             const int klo = j * kBc;
             const int khi = min(klo + kBc, N) - 1;
