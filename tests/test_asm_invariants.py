@@ -1,0 +1,86 @@
+"""Properties of the generated gfx950 code that the kernels rely on (CPU: hipcc
+cross-compiles; no GPU involved).
+
+* The transposing LDS reads are issued through inline assembly, which the
+  compiler's hazard tracking does not inspect.  They must never write a VGPR that
+  a recently issued MFMA writes (Dst) or reads over its passes (SrcC): checked on
+  every instantiation, over a window of instructions after each MFMA.  (Overlap
+  with SrcA/SrcB is harmless: those are read when the MFMA issues, long before an
+  LDS read returns.)
+* No packed fp32 arithmetic (v_pk_add/mul/fma_f32) anywhere.
+* No scratch (register spills) in the attention kernels.
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+from masked_attention_fm_amd import build as fmbuild
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+SOURCES = ["fm_attn_fwd.hip", "fm_attn_bwd.hip"]
+WINDOW = 24          # instructions after an MFMA during which it may still be in flight
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+@pytest.fixture(scope="module")
+def device_asm():
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = {}
+    with tempfile.TemporaryDirectory() as tmp:
+        procs = []
+        for src in SOURCES:
+            dst = os.path.join(tmp, src + ".s")
+            cmd = [HIPCC, *fmbuild.HIP_FLAGS, "--cuda-device-only", "-S", os.path.join(fmbuild.CSRC, src),
+                   "-o", dst]
+            procs.append((src, dst, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        for src, dst, p in procs:
+            p.communicate()
+            assert p.returncode == 0, f"hipcc failed on {src}"
+            out[src] = open(dst).read()
+    return out
+
+
+def _kernels(asm):
+    for m in re.finditer(r"^(_ZN2fm\S*kernel\S*):[^\n]*\n(.*?)^\s*s_endpgm", asm, re.S | re.M):
+        ins = [l.split(";")[0].strip() for l in m.group(2).split("\n")]
+        yield m.group(1), [l for l in ins if l and not l.startswith(".") and not l.endswith(":")]
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_transposing_reads_do_not_overlap_inflight_mfma_results(device_asm, src):
+    checked = 0
+    for name, ins in _kernels(device_asm[src]):
+        for i, line in enumerate(ins):
+            if not line.startswith("ds_read_b64_tr_b16"):
+                continue
+            checked += 1
+            dst = _regs(line.split()[1].rstrip(","))
+            for prev in ins[max(0, i - WINDOW):i]:
+                if "mfma" not in prev:
+                    continue
+                ops = [t.rstrip(",") for t in prev.split()[1:5]]
+                assert not dst & (_regs(ops[0]) | _regs(ops[3])), f"{name}: {line} overlaps {prev}"
+    assert checked > 0
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_packed_fp32_arithmetic(device_asm, src):
+    assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", device_asm[src])
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_scratch(device_asm, src):
+    for name, ins in _kernels(device_asm[src]):
+        assert not any(l.startswith("scratch_") for l in ins), name
