@@ -340,56 +340,113 @@ __device__ __forceinline__ void store_block8(const Staging8<D>& st, Smem8<D, NIV
 // conversion).  A 64-key block is one 32 x 32 x 64 contraction step; lane half
 // h of a row holds, as bytes e = 16 jb + v, the weights of keys
 // 32 jb + 8 (v / 4) + 4 h + v % 4 -- exactly the keys its S^T registers hold.
-// V^T is staged as bytes with the same key order: byte position
-// p = 32 h + e of a V^T row holds that key, so the A operand of lane half h is
-// 32 contiguous bytes.
-__device__ __forceinline__ int w8_pos(int key) {
-    const int r = key & 31;
-    return 32 * ((r >> 2) & 1) + 16 * (key >> 5) + 4 * (r >> 3) + (r & 3);
-}
+// The A operand (V^T) of lane half h must hold the same keys in the same
+// byte order; it is read transposed from V's rows (below).
+
+// K and V of e4m3 weights mode loaded straight into LDS (as in the bf16 path):
+// 1 KB segments of kSegKeys = 1024 / D byte rows (8 at d = 128, 16 at d = 64),
+// key kappa in segment kappa % kSegs, slot kappa / kSegs.
+//   * K, pitch 1024 + 16 B, read row-major: 32 bytes of one key per lane (two
+//     16-byte reads); consecutive keys land 16 bytes apart modulo 256.
+//   * V, pitch 1024 + 32 B, read transposed with ds_read_b64_tr_b8: within
+//     each 16-lane group, lane i receives byte i % 8 of the 8-byte pieces
+//     addressed by lanes 2 e + i / 8, e = 0..7 (verified by an in-bounds
+//     probe).  Lane 2 e + c addresses the key of byte e of the weights'
+//     order, columns n0 + 8 c .., so lane i ends up with column n0 + i of
+//     those eight keys; a lane's 32 bytes are four such reads.  The eight keys
+//     of a read are 32 bytes apart modulo 256 per segment step and 128 per
+//     slot step: one 256-byte sweep per 32-lane pass.
+template <int D>
+struct Direct8 {
+    static constexpr int kRowBytes = D;
+    static constexpr int kSegKeys = 1024 / kRowBytes;
+    static constexpr int kSegs = kBc / kSegKeys;
+    static constexpr int kKPitch = 1024 + 16;
+    static constexpr int kVPitch = 1024 + 32;
+    static constexpr int kKBytes = kSegs * kKPitch;
+    static constexpr int kVBytes = kSegs * kVPitch;
+    static constexpr int kSegsPerWave = kSegs / kWaves;
+    static_assert(kSegKeys * kSegs == kBc && kSegsPerWave * kWaves == kSegs, "segments split evenly");
+};
 
 template <int D, int NIV>
 struct alignas(16) Smem8w {
-    alignas(16) uint8_t k8[2][kBc][D + kK8Pad];   // K block, row-major, e4m3
-    alignas(16) uint8_t vt8[2][D][kBc + kK8Pad];  // V block, transposed, e4m3, keys in w8_pos order
+    alignas(16) uint8_t k8[2][Direct8<D>::kKBytes];
+    alignas(16) uint8_t v8[2][Direct8<D>::kVBytes];
     int start[NIV][kBr];
     int width[NIV][kBr];
 };
-static_assert((kBc + kK8Pad) % 16 == 0, "fp8 V^T rows 16-byte aligned");
-static_assert(kBc == 64, "one 64-wide FP8 contraction step per key block");
 
-// Four rows x eight e4m3 columns (two dwords per row) written transposed:
-// column n0 + c of the four keys becomes one dword of V^T row n0 + c.
-__device__ __forceinline__ void store_transposed8_4x8(const u32x2 (&rows)[4], uint8_t* dst, int pitch, int n0,
-                                                      int p) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t r0 = rows[0][w], r1 = rows[1][w], r2 = rows[2][w], r3 = rows[3][w];
-        // byte pairs of rows (0,1) and (2,3) for columns 0,1 and 2,3 of this dword
-        const uint32_t a = __builtin_amdgcn_perm(r1, r0, 0x05010400u);   // r0[0] r1[0] r0[1] r1[1]
-        const uint32_t b = __builtin_amdgcn_perm(r1, r0, 0x07030602u);   // r0[2] r1[2] r0[3] r1[3]
-        const uint32_t c = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-        const uint32_t d = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-        const uint32_t col[4] = {__builtin_amdgcn_perm(c, a, 0x05040100u), __builtin_amdgcn_perm(c, a, 0x07060302u),
-                                 __builtin_amdgcn_perm(d, b, 0x05040100u), __builtin_amdgcn_perm(d, b, 0x07060302u)};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(dst + (n0 + 4 * w + q) * pitch + p) = col[q];
+// This lane's byte offset inside a key block's e4m3 slice, for the first
+// segment its wavefront fills.
+template <int D>
+__device__ __forceinline__ int direct8_lane_offset(int lane, int wave_u) {
+    using L = Direct8<D>;
+    const int slot = lane / (L::kRowBytes / 16);
+    const int chunk = lane % (L::kRowBytes / 16);
+    return (wave_u * L::kSegsPerWave + L::kSegs * slot) * L::kRowBytes + 16 * chunk;
+}
+
+template <int D, int NIV, int U = 0>
+__device__ __forceinline__ void load_block8_direct(Smem8w<D, NIV>& sm, int buf, __amdgpu_buffer_rsrc_t krs,
+                                                   __amdgpu_buffer_rsrc_t vrs, int voff, int kv0, int wave_u) {
+    using L = Direct8<D>;
+    if constexpr (U < L::kSegsPerWave) {
+        const int seg = wave_u * L::kSegsPerWave + U;
+        const int row_off = voff + kv0 * L::kRowBytes + U * L::kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)&sm.k8[buf][seg * L::kKPitch], 16, row_off, 0, 0,
+                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)&sm.v8[buf][seg * L::kVPitch], 16, row_off, 0, 0,
+                                                 0);
+        load_block8_direct<D, NIV, U + 1>(sm, buf, krs, vrs, voff, kv0, wave_u);
     }
 }
 
-template <int D, int NIV>
-__device__ __forceinline__ void store_block8w(const Staging8<D>& st, Smem8w<D, NIV>& sm, int buf, int tid) {
-#pragma unroll
-    for (int c = 0; c < Staging8<D>::kChunksK; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int row = chunk / (D / 16);
-        const int col16 = chunk % (D / 16);
-        *reinterpret_cast<u32x4*>(&sm.k8[buf][row][col16 * 16]) = st.k[c];
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+template <int OFF>
+__device__ __forceinline__ v2i lds_read_tr8(uint32_t addr, float after) {
+    v2i r;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF), "v"(after));
+    return r;
+}
+
+// The four reads of output columns 32 NB + (0..31): part[t] holds bytes
+// 8 t .. 8 t + 7 of the lane's A operand, keys 32 (t / 2) + 16 (t % 2) +
+// 8 (u / 4) + 4 h + u % 4 for byte u.
+template <int D, int NB, int T = 0>
+__device__ __forceinline__ void issue_v8_reads(v2i (&part)[4], uint32_t addr, float after) {
+    using L = Direct8<D>;
+    if constexpr (T < 4) {
+        constexpr int base = 32 * (T / 2) + 16 * (T % 2);
+        constexpr int off = (base / L::kSegs) * L::kRowBytes + 32 * NB;
+        static_assert(off >= 0 && off < 65536 && base % L::kSegs == 0, "ds offset field");
+        part[T] = lds_read_tr8<off>(addr, after);
+        issue_v8_reads<D, NB, T + 1>(part, addr, after);
     }
-    if (Staging8<D>::kItemsV == kThreads || tid < Staging8<D>::kItemsV) {
-        const int j0 = 4 * (tid % (kBc / 4));
-        const int n0 = 8 * (tid / (kBc / 4));
-        store_transposed8_4x8(st.v, &sm.vt8[buf][0][0], kBc + kK8Pad, n0, w8_pos(j0));
+}
+
+template <int CNT>
+__device__ __forceinline__ void wait_lds_tied8(v2i (&p)[4]) {
+    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]) : "i"(CNT));
+}
+
+// O^T += V^T P^T on the FP8 units, column blocks NB.. (cur: block NB's reads).
+template <int D, int NB>
+__device__ __forceinline__ void pv8_direct(const v8i& pb8, floatx16 (&oacc)[D / 32], uint32_t addr, v2i (&cur)[4]) {
+    if constexpr (NB < D / 32) {
+        v2i next[4];
+        if constexpr (NB + 1 < D / 32) {
+            issue_v8_reads<D, NB + 1>(next, addr, 0.f);
+            wait_lds_tied8<4>(cur);
+        } else {
+            wait_lds_tied8<0>(cur);
+        }
+        const v8i a = {cur[0][0], cur[0][1], cur[1][0], cur[1][1], cur[2][0], cur[2][1], cur[3][0], cur[3][1]};
+        oacc[NB] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb8, oacc[NB], 0, 0, 0, kUnitScales, 0,
+                                                                   kUnitScales);
+        pv8_direct<D, NB + 1>(pb8, oacc, addr, next);
     }
 }
 
@@ -415,7 +472,7 @@ template <int D, int NIV>
 struct FwdTypes<D, NIV, 2> {
     using In = uint8_t;
     using Shared = Smem8w<D, NIV>;
-    using Stage = Staging8<D>;
+    using Stage = NoStage;
     using QReg = v8i;
     static constexpr int kQRegs = D / 64;
 };
@@ -534,6 +591,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                                     (r32 / Direct<D>::kSegs) * Direct<D>::kRowBytes + 16 * half;
     const int v_lane = F8 ? 0 : (4 * (lane >> 5) + ((lane & 15) >> 2)) * Direct<D>::kVPitch +
                                     32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+    // e4m3 weights: load offset, K read offset, V transposing-read offset
+    const int dvoff8 = W8 ? direct8_lane_offset<D>(lane, wave_u) : 0;
+    const int k8_lane = W8 ? (r32 % Direct8<D>::kSegs) * Direct8<D>::kKPitch +
+                                 (r32 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes + 32 * half
+                           : 0;
+    const int lp8 = 8 * ((lane & 15) >> 3) + 4 * (lane >> 5) + ((lane & 15) >> 1) % 4;
+    const int v8_lane = W8 ? (lp8 % Direct8<D>::kSegs) * Direct8<D>::kVPitch +
+                                 (lp8 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes + 16 * ((lane >> 4) & 1) +
+                                 8 * (lane & 1)
+                           : 0;
 
     floatx16 oacc[D / 32];
 #pragma unroll
@@ -565,8 +632,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     if (j != INT_MAX) {
         typename T::Stage stage;
         if constexpr (W8) {
-            load_block8<D>(stage, krs, vrs, j * kBc, tid);
-            store_block8w<D>(stage, sm, 0, tid);
+            load_block8_direct<D>(sm, 0, krs, vrs, dvoff8, j * kBc, wave_u);
+            __builtin_amdgcn_s_waitcnt(0);
         } else if constexpr (F8) {
             load_block8<D>(stage, krs, vrs, j * kBc, tid);
             store_block8<D>(stage, sm, 0, tid);
@@ -580,7 +647,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             const int j_next = union_next<NIV>(tm, j);
             const bool has_next = j_next != INT_MAX;
             if (has_next) {
-                if constexpr (F8)
+                if constexpr (W8)
+                    load_block8_direct<D>(sm, buf ^ 1, krs, vrs, dvoff8, j_next * kBc, wave_u);
+                else if constexpr (F8)
                     load_block8<D>(stage, krs, vrs, j_next * kBc, tid);
                 else
                     load_block_direct<D>(sm, buf ^ 1, krs, vrs, dvoff, j_next * kBc, wave_u);
@@ -607,7 +676,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                     for (int cs = 0; cs < D / 64; ++cs) {
 #pragma unroll
                         for (int jb = 0; jb < kBc / 32; ++jb) {
-                            const uint8_t* src = &sm.k8[buf][jb * 32 + r32][cs * 64 + half * 32];
+                            const uint8_t* src;
+                            if constexpr (W8)
+                                src = &sm.k8[buf][k8_lane + jb * (32 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes +
+                                                  cs * 64];
+                            else
+                                src = &sm.k8[buf][jb * 32 + r32][cs * 64 + half * 32];
                             const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
                             const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
                             const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -698,6 +772,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                     vaddr = lds_address(&sm.v[buf][0]) + v_lane;
                     issue_v_reads<D, 0>(vpart, vaddr, m_use);
                 }
+                [[maybe_unused]] v2i v8part[4];
+                [[maybe_unused]] uint32_t v8addr = 0;
+                if constexpr (W8) {
+                    v8addr = lds_address(&sm.v8[buf][0]) + v8_lane;
+                    issue_v8_reads<D, 0>(v8part, v8addr, m_use);
+                }
                 float rs = 0.f;
 #pragma unroll
                 for (int jb = 0; jb < kBc / 32; ++jb)
@@ -714,8 +794,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 // of a proper weighted mean instead of biasing its scale.
                 float rs16 = 0.f;
                 if constexpr (W8) {
-                    // the weights (already 2^8 P) as e4m3, bytes e = 16 jb + v (see
-                    // w8_pos); the normaliser is the sum of the rounded weights, read back
+                    // the weights (already 2^8 P) as e4m3, bytes e = 16 jb + v; the
+                    // normaliser is the sum of the rounded weights, read back
                     uint32_t pw[8];
 #pragma unroll
                     for (int w = 0; w < 8; ++w) {
@@ -729,15 +809,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                     }
                     const v8i pb8 = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
                                      (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-#pragma unroll
-                    for (int nb = 0; nb < D / 32; ++nb) {
-                        const uint8_t* src = &sm.vt8[buf][nb * 32 + r32][32 * half];
-                        const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
-                        const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
-                        const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        oacc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb8, oacc[nb], 0, 0, 0,
-                                                                                   kUnitScales, 0, kUnitScales);
-                    }
+                    pv8_direct<D, 0>(pb8, oacc, v8addr, v8part);
                 } else if constexpr (F8) {
 #pragma unroll
                     for (int ks = 0; ks < kBc / 16; ++ks) {
@@ -763,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
             if (has_next) {
                 if constexpr (W8)
-                    store_block8w<D>(stage, sm, buf ^ 1, tid);
+                    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
                 else if constexpr (F8)
                     store_block8<D>(stage, sm, buf ^ 1, tid);
                 else

@@ -1,7 +1,7 @@
 """Properties of the generated gfx950 code that the kernels rely on (CPU: hipcc
 cross-compiles; no GPU involved).
 
-* The transposing LDS reads are issued through inline assembly, which the
+* The transposing LDS reads (16- and 8-bit) are issued through inline assembly, which the
   compiler's hazard tracking does not inspect.  They must never write a VGPR that
   a recently issued MFMA writes (Dst) or reads over its passes (SrcC): checked on
   every instantiation, over a window of instructions after each MFMA.  (Overlap
@@ -63,7 +63,7 @@ def test_transposing_reads_do_not_overlap_inflight_mfma_results(device_asm, src)
     checked = 0
     for name, ins in _kernels(device_asm[src]):
         for i, line in enumerate(ins):
-            if not line.startswith("ds_read_b64_tr_b16"):
+            if not line.startswith(("ds_read_b64_tr_b16", "ds_read_b64_tr_b8")):
                 continue
             checked += 1
             dst = _regs(line.split()[1].rstrip(","))
