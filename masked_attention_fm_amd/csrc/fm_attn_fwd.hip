@@ -27,8 +27,7 @@
 //     (buffer loads with an LDS destination, no registers involved); one
 //     barrier per key block.  K is read row-major as the A operand of the
 //     score product, V transposed (ds_read_b64_tr_b16) as the A operand of
-//     the PV product.  (FP8 inputs are staged through registers instead, see
-//     below.)
+//     the PV product (FP8 inputs: the same with bytes, see below).
 //   * Softmax with lazy rescaling: a row's reference maximum may lag its
 //     running maximum by up to 2^8 in weight, so the accumulator is rescaled
 //     only when some row of the wavefront outgrows that margin.
@@ -45,8 +44,9 @@
 //     the compare keeps a key that lies in any of the row's ranges.  With
 //     NIV = 1 this is the single-range kernel.
 //   * A second instantiation (F8) takes e4m3 Q, K, V: the score product runs
-//     on the FP8 matrix instruction and V is widened to bf16 as it is staged
-//     (see the FP8 section below).
+//     on the FP8 matrix instruction; V is widened to bf16 as it is read for
+//     the PV product, or, with e4m3 weights as well, that product runs on the
+//     FP8 matrix instruction too (see the FP8 section below).
 //   * With one interval set per head, head h reads set h; the work items of
 //     each set are a contiguous, separately ranked segment of the order.
 
@@ -125,8 +125,6 @@ struct alignas(16) Smem {
                                                   // (kEmptyStart: the range holds no key)
     int width[NIV][kBr];                          // end - start (0 for empty ranges)
 };
-
-struct NoStage {};
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -257,79 +255,19 @@ __device__ __forceinline__ void load_block_direct(Smem<D, NIV>& sm, int buf, __a
 // contraction index depends only on (lane / 32, byte) in the same way for A
 // and B (checked by an in-bounds probe), so any consistent order of the head
 // dimension is correct: lane half h of a 64-wide step holds columns
-// 64 cs + 32 h + (0..31).  V is widened to bf16 while it is staged (exact: the
-// three mantissa bits of e4m3 fit in bf16), so the PV product, the weights
-// and the output keep the bf16 path's arithmetic.
-constexpr int kK8Pad = 16;                     // bytes of padding per fp8 K row in LDS
+// 64 cs + 32 h + (0..31).  K and V reach LDS as bytes (straight from global
+// memory, below).  In the FP8-scores mode V is widened to bf16 as it is read
+// for the PV product (exact: the three mantissa bits of e4m3 fit in bf16), so
+// the PV product, the weights and the output keep the bf16 path's arithmetic.
 constexpr int kUnitScales = 0x7F7F7F7F;        // E8M0 block scale 2^0 in every byte
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-
-template <int D, int NIV>
-struct alignas(16) Smem8 {
-    alignas(16) uint8_t k8[2][kBc][D + kK8Pad];   // K block, row-major, e4m3
-    alignas(16) uint16_t vt[2][D][kBc + kVPad];   // V block widened to bf16, transposed, vt_pos order
-    int start[NIV][kBr];
-    int width[NIV][kBr];
-};
-static_assert((128 + kK8Pad) % 16 == 0 && (64 + kK8Pad) % 16 == 0, "fp8 K rows 16-byte aligned");
-
-template <int D>
-struct Staging8 {
-    static constexpr int kChunksK = kBc * D / 16 / kThreads;  // 16-byte K chunks per thread
-    static constexpr int kItemsV = (kBc / 4) * (D / 8);       // 4 keys x 8 columns per item
-    static_assert(kChunksK >= 1 && kChunksK * kThreads * 16 == kBc * D, "K block splits evenly");
-    static_assert(kItemsV <= kThreads, "one V item per thread at most");
-    u32x4 k[kChunksK];
-    u32x2 v[4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_block8(Staging8<D>& st, __amdgpu_buffer_rsrc_t krs,
-                                            __amdgpu_buffer_rsrc_t vrs, int kv0, int tid) {
-    const int base = kv0 * D;
-#pragma unroll
-    for (int c = 0; c < Staging8<D>::kChunksK; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int row = chunk / (D / 16);
-        const int col16 = chunk % (D / 16);
-        st.k[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + row * D + col16 * 16, 0, 0);
-    }
-    if (Staging8<D>::kItemsV == kThreads || tid < Staging8<D>::kItemsV) {
-        const int j0 = 4 * (tid % (kBc / 4));
-        const int n0 = 8 * (tid / (kBc / 4));
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            st.v[r] = __builtin_amdgcn_raw_buffer_load_b64(vrs, base + (j0 + r) * D + n0, 0, 0);
-    }
-}
 
 // Two e4m3 bytes of `w` (the low or the high half) as a packed bf16 pair.
 template <bool HIGH>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     const bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
     return __builtin_bit_cast(uint32_t, r);
-}
-
-template <int D, int NIV>
-__device__ __forceinline__ void store_block8(const Staging8<D>& st, Smem8<D, NIV>& sm, int buf, int tid) {
-#pragma unroll
-    for (int c = 0; c < Staging8<D>::kChunksK; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int row = chunk / (D / 16);
-        const int col16 = chunk % (D / 16);
-        *reinterpret_cast<u32x4*>(&sm.k8[buf][row][col16 * 16]) = st.k[c];
-    }
-    if (Staging8<D>::kItemsV == kThreads || tid < Staging8<D>::kItemsV) {
-        const int j0 = 4 * (tid % (kBc / 4));
-        const int n0 = 8 * (tid / (kBc / 4));
-        u32x4 rows[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            rows[r] = u32x4{e4m3x2_to_bf16x2<false>(st.v[r][0]), e4m3x2_to_bf16x2<true>(st.v[r][0]),
-                            e4m3x2_to_bf16x2<false>(st.v[r][1]), e4m3x2_to_bf16x2<true>(st.v[r][1])};
-        store_transposed_4x8(rows, &sm.vt[buf][0][0], kBc + kVPad, n0, vt_pos(j0));
-    }
 }
 
 // ---- e4m3 weights (PREC 2): the PV product on the FP8 unit as well.
@@ -450,32 +388,52 @@ __device__ __forceinline__ void pv8_direct(const v8i& pb8, floatx16 (&oacc)[D / 
     }
 }
 
+// FP8 scores, bf16 weights: O^T += V^T P^T on bf16 MFMAs, column blocks NB..,
+// V widened from the same transposing byte reads (read t is step ks = t:
+// keys 16 ks + 8 (e / 4) + 4 h + e % 4 for element e, the order of pbs[ks]).
+template <int D, int NB>
+__device__ __forceinline__ void pv8_bf16_direct(const bf16x8 (&pbs)[kBc / 16], floatx16 (&oacc)[D / 32],
+                                                uint32_t addr, v2i (&cur)[4]) {
+    if constexpr (NB < D / 32) {
+        v2i next[4];
+        if constexpr (NB + 1 < D / 32) {
+            issue_v8_reads<D, NB + 1>(next, addr, 0.f);
+            wait_lds_tied8<4>(cur);
+        } else {
+            wait_lds_tied8<0>(cur);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kBc / 16; ++ks) {
+            const uint32_t w0 = (uint32_t)cur[ks][0], w1 = (uint32_t)cur[ks][1];
+            const u32x4 wide = {e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)};
+            oacc[NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wide), pbs[ks], oacc[NB],
+                                                               0, 0, 0);
+        }
+        pv8_bf16_direct<D, NB + 1>(pbs, oacc, addr, next);
+    }
+}
+
 // Types of one instantiation: PREC 0 bf16 inputs; 1 e4m3 inputs (V widened to
 // bf16, bf16 weights); 2 e4m3 inputs and e4m3 weights.
 template <int D, int NIV, int PREC>
 struct FwdTypes {
     using In = uint16_t;
     using Shared = Smem<D, NIV>;
-    using Stage = NoStage;
     using QReg = bf16x8;
     static constexpr int kQRegs = D / 16;
 };
 template <int D, int NIV>
-struct FwdTypes<D, NIV, 1> {
+struct FwdTypes8 {
     using In = uint8_t;
-    using Shared = Smem8<D, NIV>;
-    using Stage = Staging8<D>;
+    using Shared = Smem8w<D, NIV>;
     using QReg = v8i;
     static constexpr int kQRegs = D / 64;
 };
 template <int D, int NIV>
-struct FwdTypes<D, NIV, 2> {
-    using In = uint8_t;
-    using Shared = Smem8w<D, NIV>;
-    using Stage = NoStage;
-    using QReg = v8i;
-    static constexpr int kQRegs = D / 64;
-};
+struct FwdTypes<D, NIV, 1> : FwdTypes8<D, NIV> {};
+template <int D, int NIV>
+struct FwdTypes<D, NIV, 2> : FwdTypes8<D, NIV> {};
 
 // NIV: ranges per query row (the row attends their union).  col_start and
 // col_end are [B][NIV][N]; meta holds NIV records per query block.  F8: Q, K,
@@ -591,13 +549,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                                     (r32 / Direct<D>::kSegs) * Direct<D>::kRowBytes + 16 * half;
     const int v_lane = F8 ? 0 : (4 * (lane >> 5) + ((lane & 15) >> 2)) * Direct<D>::kVPitch +
                                     32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-    // e4m3 weights: load offset, K read offset, V transposing-read offset
-    const int dvoff8 = W8 ? direct8_lane_offset<D>(lane, wave_u) : 0;
-    const int k8_lane = W8 ? (r32 % Direct8<D>::kSegs) * Direct8<D>::kKPitch +
+    // e4m3 inputs: load offset, K read offset, V transposing-read offset
+    const int dvoff8 = F8 ? direct8_lane_offset<D>(lane, wave_u) : 0;
+    const int k8_lane = F8 ? (r32 % Direct8<D>::kSegs) * Direct8<D>::kKPitch +
                                  (r32 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes + 32 * half
                            : 0;
     const int lp8 = 8 * ((lane & 15) >> 3) + 4 * (lane >> 5) + ((lane & 15) >> 1) % 4;
-    const int v8_lane = W8 ? (lp8 % Direct8<D>::kSegs) * Direct8<D>::kVPitch +
+    const int v8_lane = F8 ? (lp8 % Direct8<D>::kSegs) * Direct8<D>::kVPitch +
                                  (lp8 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes + 16 * ((lane >> 4) & 1) +
                                  8 * (lane & 1)
                            : 0;
@@ -630,13 +588,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     // blocks (one contiguous run for a single range).
     int j = union_next<NIV>(tm, -1);
     if (j != INT_MAX) {
-        typename T::Stage stage;
-        if constexpr (W8) {
+        if constexpr (F8) {
             load_block8_direct<D>(sm, 0, krs, vrs, dvoff8, j * kBc, wave_u);
             __builtin_amdgcn_s_waitcnt(0);
-        } else if constexpr (F8) {
-            load_block8<D>(stage, krs, vrs, j * kBc, tid);
-            store_block8<D>(stage, sm, 0, tid);
         } else {
             load_block_direct<D>(sm, 0, krs, vrs, dvoff, j * kBc, wave_u);
             __builtin_amdgcn_s_waitcnt(0);
@@ -647,10 +601,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             const int j_next = union_next<NIV>(tm, j);
             const bool has_next = j_next != INT_MAX;
             if (has_next) {
-                if constexpr (W8)
+                if constexpr (F8)
                     load_block8_direct<D>(sm, buf ^ 1, krs, vrs, dvoff8, j_next * kBc, wave_u);
-                else if constexpr (F8)
-                    load_block8<D>(stage, krs, vrs, j_next * kBc, tid);
                 else
                     load_block_direct<D>(sm, buf ^ 1, krs, vrs, dvoff, j_next * kBc, wave_u);
             }
@@ -676,12 +628,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                     for (int cs = 0; cs < D / 64; ++cs) {
 #pragma unroll
                         for (int jb = 0; jb < kBc / 32; ++jb) {
-                            const uint8_t* src;
-                            if constexpr (W8)
-                                src = &sm.k8[buf][k8_lane + jb * (32 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes +
-                                                  cs * 64];
-                            else
-                                src = &sm.k8[buf][jb * 32 + r32][cs * 64 + half * 32];
+                            const uint8_t* src =
+                                &sm.k8[buf][k8_lane + jb * (32 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes + cs * 64];
                             const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
                             const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
                             const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -774,7 +722,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 }
                 [[maybe_unused]] v2i v8part[4];
                 [[maybe_unused]] uint32_t v8addr = 0;
-                if constexpr (W8) {
+                if constexpr (F8) {
                     v8addr = lds_address(&sm.v8[buf][0]) + v8_lane;
                     issue_v8_reads<D, 0>(v8part, v8addr, m_use);
                 }
@@ -811,19 +759,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                                      (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
                     pv8_direct<D, 0>(pb8, oacc, v8addr, v8part);
                 } else if constexpr (F8) {
+                    bf16x8 pbs[kBc / 16];
 #pragma unroll
                     for (int ks = 0; ks < kBc / 16; ++ks) {
-                        bf16x8 pb;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)st[ks >> 1][8 * (ks & 1) + e];
-                        rs16 = sum_bf16x8(pb, ones, rs16);
-#pragma unroll
-                        for (int nb = 0; nb < D / 32; ++nb) {
-                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                                &sm.vt[buf][nb * 32 + r32][16 * ks + 8 * half]);
-                            oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
-                        }
+                        for (int e = 0; e < 8; ++e) pbs[ks][e] = (__bf16)st[ks >> 1][8 * (ks & 1) + e];
+                        rs16 = sum_bf16x8(pbs[ks], ones, rs16);
                     }
+                    pv8_bf16_direct<D, 0>(pbs, oacc, v8addr, v8part);
                 } else {
                     // A operand lane (i, half h), element e: V^T[column i][key
                     // 16 ks + 8 (e / 4) + 4 h + e % 4], the key order of the P^T
@@ -833,14 +776,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 l16_run += rs16;
             }
 
-            if (has_next) {
-                if constexpr (W8)
-                    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
-                else if constexpr (F8)
-                    store_block8<D>(stage, sm, buf ^ 1, tid);
-                else
-                    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
-            }
+            if (has_next) __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
             __syncthreads();
             if (!has_next) break;
             j = j_next;
