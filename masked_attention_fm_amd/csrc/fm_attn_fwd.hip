@@ -193,17 +193,74 @@ __device__ __forceinline__ void wait_lds_tied(v4s (&p)[NP]) {
         static_assert(NP == 8 || NP == 4, "d = 64 or 128");
 }
 
+// K operand read of the score product: 16 bytes of one key row per lane
+// (the compiler's schedule of these reads is not kept stable across changes
+// elsewhere in the kernel, so they are issued explicitly, like the V reads).
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int CNT>
+__device__ __forceinline__ void wait_lds_one(u32x4& r) {
+    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(CNT));
+}
+
+// S^T = K Q^T for one key block: MFMA i (i = 2 cs + jb) takes K rows of key
+// half jb, head-dimension chunk cs.  The reads run kAheadK ahead of the MFMA
+// that consumes them, through a ring of kAheadK registers.
+constexpr int kAheadK = 6;
+template <int D>
+constexpr int k_read_offset(int i) {
+    return (i % 2) * (32 / Direct<D>::kSegs) * Direct<D>::kRowBytes + (i / 2) * 32;
+}
+template <int D, int I = 0>
+__device__ __forceinline__ void issue_k_reads(u32x4 (&ring)[kAheadK], uint32_t addr) {
+    if constexpr (I < kAheadK) {
+        ring[I] = lds_read_b128<k_read_offset<D>(I)>(addr);
+        issue_k_reads<D, I + 1>(ring, addr);
+    }
+}
+template <int D, int I = 0>
+__device__ __forceinline__ void score_direct(floatx16 (&st)[kBc / 32], const bf16x8 (&q)[D / 16], uint32_t addr,
+                                             u32x4 (&ring)[kAheadK]) {
+    constexpr int kMfmas = (D / 16) * (kBc / 32);
+    static_assert(kBc / 32 == 2 && kMfmas > kAheadK, "two key halves, more MFMAs than reads in flight");
+    if constexpr (I < kMfmas) {
+        constexpr int issued = I + kAheadK < kMfmas ? I + kAheadK : kMfmas;
+        wait_lds_one<issued - (I + 1)>(ring[I % kAheadK]);
+        st[I % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ring[I % kAheadK]), q[I / 2],
+                                                            st[I % 2], 0, 0, 0);
+        if constexpr (I + kAheadK < kMfmas)
+            ring[I % kAheadK] = lds_read_b128<k_read_offset<D>(I + kAheadK)>(addr);
+        score_direct<D, I + 1>(st, q, addr, ring);
+    }
+}
+
 // O^T += V^T P^T over steps KS.. of one key block.  cur holds step KS's
 // reads (issued earlier); the next step's reads are issued before waiting
 // for them.
+//
+// The weights of step KS are formed here, from the scores: P = 2^(S c - m),
+// summed in fp32 into rs (in the same key order as a loop over the block) and
+// rounded to bf16 for the product, so that the exponentials of one step run
+// while the previous step's MFMAs execute.
 template <int D, int KS>
 __device__ __forceinline__ void pv_direct(const floatx16 (&st)[kBc / 32], floatx16 (&oacc)[D / 32],
-                                          uint32_t addr, float& rs16, bf16x2 ones, v4s (&cur)[2 * D / 32]) {
+                                          uint32_t addr, float c, float m_use, float& rs, float& rs16,
+                                          bf16x2 ones, v4s (&cur)[2 * D / 32]) {
     constexpr int NP = 2 * D / 32;
     if constexpr (KS < kBc / 16) {
         bf16x8 pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)st[KS >> 1][8 * (KS & 1) + e];
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(st[KS >> 1][8 * (KS & 1) + e], c, -m_use));
+            rs += p;
+            pb[e] = (__bf16)p;
+        }
         rs16 = sum_bf16x8(pb, ones, rs16);
         v4s next[NP];
         if constexpr (KS + 1 < kBc / 16) {
@@ -218,7 +275,7 @@ __device__ __forceinline__ void pv_direct(const floatx16 (&st)[kBc / 32], floatx
                 bf16x8, __builtin_shufflevector(cur[2 * nb], cur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
             oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[nb], 0, 0, 0);
         }
-        pv_direct<D, KS + 1>(st, oacc, addr, rs16, ones, next);
+        pv_direct<D, KS + 1>(st, oacc, addr, c, m_use, rs, rs16, ones, next);
     }
 }
 
@@ -638,29 +695,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                         }
                     }
                 } else {
-#pragma unroll
-                    for (int cs = 0; cs < D / 16; ++cs) {
-#pragma unroll
-                        for (int jb = 0; jb < kBc / 32; ++jb) {
-                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                                &sm.k[buf][k_lane + jb * (32 / Direct<D>::kSegs) * Direct<D>::kRowBytes + cs * 32]);
-                            st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
-                        }
-                    }
-                    // Keep the LDS operand reads kAhead ahead of the MFMA that
-                    // consumes them (the default schedule reads two ahead and
-                    // waits on LDS latency before most MFMAs).  Groups: kAhead
-                    // reads, then alternately one MFMA and one read, then the
-                    // last kAhead MFMAs.
-                    constexpr int kMfmas = (D / 16) * (kBc / 32);
-                    constexpr int kAhead = kMfmas >= 12 ? 6 : kMfmas / 2;
-                    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);     // DS reads
-#pragma unroll
-                    for (int i = 0; i < kMfmas - kAhead; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+                    u32x4 ring[kAheadK];
+                    const uint32_t kaddr = lds_address(&sm.k[buf][0]) + k_lane;
+                    issue_k_reads<D>(ring, kaddr);
+                    score_direct<D>(st, qreg, kaddr, ring);
                 }
 
                 // ---- interval compare, only where some row of the wavefront
@@ -727,15 +765,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                     issue_v8_reads<D, 0>(v8part, v8addr, m_use);
                 }
                 float rs = 0.f;
+                if constexpr (F8) {
 #pragma unroll
-                for (int jb = 0; jb < kBc / 32; ++jb)
+                    for (int jb = 0; jb < kBc / 32; ++jb)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(st[jb][v], c, -m_use));
-                        st[jb][v] = p;
-                        rs += p;
-                    }
-                l_run += rs;
+                        for (int v = 0; v < 16; ++v) {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(st[jb][v], c, -m_use));
+                            st[jb][v] = p;
+                            rs += p;
+                        }
+                }
 
                 // ---- O^T += V^T P^T.  O is later divided by the sum of the same
                 // bf16-rounded weights, so the rounding of P perturbs the weights
@@ -771,8 +810,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                     // A operand lane (i, half h), element e: V^T[column i][key
                     // 16 ks + 8 (e / 4) + 4 h + e % 4], the key order of the P^T
                     // registers: two transposing reads of four keys each.
-                    pv_direct<D, 0>(st, oacc, vaddr, rs16, ones, vpart);
+                    pv_direct<D, 0>(st, oacc, vaddr, c, m_use, rs, rs16, ones, vpart);
                 }
+                l_run += rs;
                 l16_run += rs16;
             }
 
