@@ -39,6 +39,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // ---------------------------------------------------------------- options
 
 int g_schedule_mode = 0;   // 0 longest first, 1 natural order
+int g_bwd_min_chunks = 32; // smallest piece of a split key block (query chunks); 0: never split
 
 // ---------------------------------------------------------------- workspace
 //
@@ -120,6 +121,11 @@ FM_API int fm_set_option(int option, int64_t value) {
     if (option == FM_OPT_SCHEDULE) {
         if (value != 0 && value != 1) return FM_ERR_INVALID_ARG;
         g_schedule_mode = (int)value;
+        return FM_OK;
+    }
+    if (option == FM_OPT_BWD_SPLIT_CHUNKS) {
+        if (value < 0 || value > (1 << 20)) return FM_ERR_INVALID_ARG;
+        g_bwd_min_chunks = (int)value;
         return FM_OK;
     }
     return FM_ERR_INVALID_ARG;
@@ -344,17 +350,25 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     if (B * H * n_qc >= (int64_t(1) << 31) || B * n_sets * n_ranges * N >= (int64_t(1) << 40))
         return FM_ERR_INVALID_ARG;
 
-    // ---- workspace: meta_q[Mq][n] | work_q | order_q | meta_c[Mc][n] | kvr[Mk] | work_k | order_k | D[B H N]
+    // ---- workspace: meta_q[Mq][n] | work_q | order_q | meta_c[Mc][n] | kvr[Mk] | work_k | pieces[Mp] |
+    // pslot[Mp] | pwork[Mp] | order_k[Mp] | splits | D[B H N] | partial sums of split key blocks
     const int64_t Mq = n_sets * B * n_q, Mc = n_sets * B * n_qc, Mk = n_sets * B * n_kb;
+    const int64_t Lp = fm::bwd_piece_entries(B * n_kb, (int)n_sets), Mp = n_sets * Lp;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t o_work_q = al((size_t)(Mq * n_ranges) * sizeof(fm::TileMeta));
     const size_t o_order_q = o_work_q + al((size_t)Mq * 4);
     const size_t o_meta_c = o_order_q + al((size_t)Mq * 4);
     const size_t o_kvr = o_meta_c + al((size_t)(Mc * n_ranges) * sizeof(fm::TileMeta));
     const size_t o_work_k = o_kvr + al((size_t)Mk * sizeof(int4));
-    const size_t o_order_k = o_work_k + al((size_t)Mk * 4);
-    const size_t o_dd = o_order_k + al((size_t)Mk * 4);
-    const size_t total = o_dd + al((size_t)(B * H * N) * sizeof(float));
+    const size_t o_pieces = o_work_k + al((size_t)Mk * 4);
+    const size_t o_pslot = o_pieces + al((size_t)Mp * sizeof(int4));
+    const size_t o_pwork = o_pslot + al((size_t)Mp * 4);
+    const size_t o_order_k = o_pwork + al((size_t)Mp * 4);
+    const size_t o_splits = o_order_k + al((size_t)Mp * 4);
+    const size_t o_dd = o_splits + al((size_t)(1 + fm::kBwdExtraPieces) * sizeof(int4));
+    const size_t o_part = o_dd + al((size_t)(B * H * N) * sizeof(float));
+    const size_t part_floats = n_sets == 1 ? (size_t)fm::kBwdExtraPieces * H * fm::kBwdKeys * d * 2 : 0;
+    const size_t total = o_part + al(part_floats * sizeof(float));
     void* ws = nullptr;
     FM_HIP(get_workspace(stream, total, &ws));
     char* w = static_cast<char*>(ws);
@@ -364,8 +378,13 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     auto* meta_c = reinterpret_cast<fm::TileMeta*>(w + o_meta_c);
     auto* kvr = reinterpret_cast<int4*>(w + o_kvr);
     auto* work_k = reinterpret_cast<int32_t*>(w + o_work_k);
+    auto* pieces = reinterpret_cast<int4*>(w + o_pieces);
+    auto* pslot = reinterpret_cast<int32_t*>(w + o_pslot);
+    auto* pwork = reinterpret_cast<int32_t*>(w + o_pwork);
     auto* order_k = reinterpret_cast<int32_t*>(w + o_order_k);
+    auto* splits = reinterpret_cast<int4*>(w + o_splits);
     auto* dd = reinterpret_cast<float*>(w + o_dd);
+    auto* part = reinterpret_cast<float*>(w + o_part);
 
     FM_HIP(fm::launch_bwd_rowdot(out, dout, B * H * N, d, dd, stream));
     // dQ: the forward's query blocks, key blocks and longest-first order
@@ -377,15 +396,19 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
                                      stream, (int)n_sets));
         FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q));
     }
-    // dK, dV: query chunks per key block, key blocks longest first (within each set)
+    // dK, dV: query chunks per key block, long key blocks split into pieces,
+    // pieces longest first (within each set)
     FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBwdRows, fm::kBwdKeys, meta_c, nullptr,
                                  nullptr, stream, (int)n_sets));
     FM_HIP(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream, (int)n_sets));
-    FM_HIP(fm::launch_schedule(work_k, Mk, order_k, stream, B * n_kb));
-    FM_HIP(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, kvr, order_k, B, H, N,
-                               d, scale, dk, dv, stream, (int)n_sets));
+    const int min_chunks = g_bwd_min_chunks > 0 ? g_bwd_min_chunks : (1 << 30);
+    FM_HIP(fm::launch_bwd_split(kvr, B * n_kb, (int)n_sets, min_chunks, pieces, pslot, pwork, splits, stream));
+    FM_HIP(fm::launch_schedule(pwork, Mp, order_k, stream, Lp));
+    FM_HIP(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, pieces, pslot, order_k,
+                               B, H, N, d, scale, dk, dv, part, stream, (int)n_sets));
     FM_HIP(fm::launch_bwd_dq(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_q, order_q, B, H, N, d,
                              scale, dq, stream, (int)n_sets));
+    if (n_sets == 1) FM_HIP(fm::launch_bwd_reduce(splits, part, H, N, d, n_kb, dk, dv, stream));
     return FM_OK;
 }
 

@@ -103,6 +103,139 @@ __global__ __launch_bounds__(256) void kv_ranges_kernel(const TileMeta* __restri
     }
 }
 
+// ---------------------------------------------------------------- key-block pieces
+
+constexpr int kSplitThreads = 1024;
+
+// Sum over the workgroup; every thread calls it and gets the total.
+__device__ __forceinline__ int split_block_sum(int v, int* red) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < kSplitThreads / 64; ++i) t += red[i];
+    __syncthreads();
+    return t;
+}
+
+// One workgroup.  Piece size S: at least min_chunks, at least twice the mean
+// live-chunk count of the non-empty blocks, doubled until the extra pieces fit
+// kBwdExtraPieces.  A block with c > S live chunks becomes P = ceil(c / S)
+// pieces over equal shares of its chunk-index range.  Which extra entries and
+// partial slots a block receives depends on arrival order, but not the
+// numbers: each block's partial sums are added in piece order.
+__global__ __launch_bounds__(kSplitThreads) void bwd_split_kernel(const int4* __restrict__ kvr, int items,
+                                                                  int n_sets, int min_chunks,
+                                                                  int4* __restrict__ pieces,
+                                                                  int32_t* __restrict__ pslot,
+                                                                  int32_t* __restrict__ pwork,
+                                                                  int4* __restrict__ splits) {
+    __shared__ int red[kSplitThreads / 64];
+    __shared__ int n_extra, n_split;
+    const int tid = threadIdx.x;
+    if (n_sets != 1) {                          // several interval sets: one piece per block
+        for (int e = tid; e < items * n_sets; e += kSplitThreads) {
+            const int4 r = kvr[e];
+            pieces[e] = make_int4(e, r.x, r.y, 1);
+            pslot[e] = -1;
+            pwork[e] = r.z;
+        }
+        if (tid == 0) splits[0] = make_int4(0, 0, 0, 0);
+        return;
+    }
+    int tot = 0, nz = 0;
+    for (int j = tid; j < items; j += kSplitThreads) {
+        const int c = kvr[j].z;
+        tot += c;
+        nz += c > 0;
+    }
+    tot = split_block_sum(tot, red);
+    nz = split_block_sum(nz, red);
+    int S = max(min_chunks, 1);
+    if (nz > 0) S = max(S, (2 * tot + nz - 1) / nz);
+    for (;;) {                                  // uniform: every thread sees the same sums
+        int extra = 0;
+        for (int j = tid; j < items; j += kSplitThreads) {
+            const int c = kvr[j].z;
+            extra += c > S ? (c + S - 1) / S - 1 : 0;
+        }
+        extra = split_block_sum(extra, red);
+        if (extra <= kBwdExtraPieces) break;
+        S *= 2;
+    }
+    if (tid == 0) {
+        n_extra = 0;
+        n_split = 0;
+    }
+    __syncthreads();
+    for (int j = tid; j < items; j += kSplitThreads) {
+        const int4 r = kvr[j];
+        const int c = r.z;
+        const int P = c > S ? (c + S - 1) / S : 1;
+        int base = 0;
+        if (P > 1) {
+            base = atomicAdd(&n_extra, P - 1);
+            splits[1 + atomicAdd(&n_split, 1)] = make_int4(j, P, base, 0);
+        }
+        const int len = r.y - r.x + 1;          // 0 for a block no chunk attends
+        const int w = (c + P - 1) / P;
+        for (int p = 0; p < P; ++p) {
+            const int lo = r.x + (int)((int64_t)len * p / P);
+            const int hi = r.x + (int)((int64_t)len * (p + 1) / P) - 1;
+            const int e = p == 0 ? j : items + base + p - 1;
+            pieces[e] = make_int4(j, lo, hi, (p << 16) | P);
+            pslot[e] = p == 0 ? -1 : base + p - 1;
+            pwork[e] = w;
+        }
+    }
+    __syncthreads();
+    for (int e = n_extra + tid; e < kBwdExtraPieces; e += kSplitThreads) {
+        pieces[items + e] = make_int4(-1, 0, -1, 0);
+        pslot[items + e] = -1;
+        pwork[items + e] = -1;
+    }
+    if (tid == 0) splits[0] = make_int4(n_split, 0, 0, 0);
+}
+
+// dK, dV of each split block (one interval set) += its pieces 1..P-1, in order.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const int4* __restrict__ splits,
+                                                         const float* __restrict__ part, int H, int N, int n_kb,
+                                                         float* __restrict__ dK, float* __restrict__ dV) {
+    const int pairs = splits[0].x * H;
+    for (int x = blockIdx.x; x < pairs; x += gridDim.x) {
+        const int4 sp = splits[1 + x / H];     // {item, P, first slot}
+        const int h = x % H;
+        const int b = sp.x / n_kb;
+        const int k0 = (sp.x - b * n_kb) * kBwdKeys;
+        const int64_t bh = (int64_t)b * H + h;
+        const int nk = min(kBwdKeys, N - k0);
+        for (int i = threadIdx.x; i < nk * (D / 4); i += 256) {
+            const int kl = i / (D / 4);
+            const int c4 = i % (D / 4);
+            float4* dk = reinterpret_cast<float4*>(dK + (bh * N + k0 + kl) * D) + c4;
+            float4* dv = reinterpret_cast<float4*>(dV + (bh * N + k0 + kl) * D) + c4;
+            float4 ak = *dk, av = *dv;
+            for (int p = 1; p < sp.y; ++p) {
+                const float* pb = part + ((int64_t)(sp.z + p - 1) * H + h) * (kBwdKeys * D * 2);
+                const float4 pk = reinterpret_cast<const float4*>(pb + kl * D)[c4];
+                const float4 pv = reinterpret_cast<const float4*>(pb + kBwdKeys * D + kl * D)[c4];
+                ak.x += pk.x;
+                ak.y += pk.y;
+                ak.z += pk.z;
+                ak.w += pk.w;
+                av.x += pv.x;
+                av.y += pv.y;
+                av.z += pv.z;
+                av.w += pv.w;
+            }
+            *dk = ak;
+            *dv = av;
+        }
+    }
+}
+
 // Launch slot -> (head, work item): the forward's XCD-local head order.
 __device__ __forceinline__ void slot_to_item(int xcd_heads, int H, int& h, int& item) {
     if (xcd_heads) {
@@ -415,9 +548,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
-    const TileMeta* __restrict__ meta_c, const int4* __restrict__ kvr, const int32_t* __restrict__ order, int H,
-    int N, int n_qc, int n_kb, float c, float scale, int xcd_heads, int per_head, float* __restrict__ dK,
-    float* __restrict__ dV) {
+    const TileMeta* __restrict__ meta_c, const int4* __restrict__ pieces, const int32_t* __restrict__ pslot,
+    const int32_t* __restrict__ order, int H, int N, int n_qc, int n_kb, int Lk, float c, float scale,
+    int xcd_heads, int per_head, float* __restrict__ dK, float* __restrict__ dV, float* __restrict__ part) {
     __shared__ DkvSmem<D, NIV> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -428,15 +561,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     int h, slot;
     slot_to_item(xcd_heads, H, h, slot);
     // With one interval set per head, head h reads set h: its key-block items
-    // are the segment [h L, h L + L) of the records and of the order.
-    const int L = gridDim.x / H;                 // key blocks per head (B n_kb)
+    // are the segment [h Lk, h Lk + Lk) of the records, its pieces the segment
+    // [h Lp, h Lp + Lp) of the piece table and of the order.
+    const int Lp = gridDim.x / H;                // piece entries per head
     const int set = per_head ? h : 0;
     const int n_sets = per_head ? H : 1;
-    const int bj = order[set * L + slot];
-    const int local = bj - set * L;
+    const int pe = order[set * Lp + slot];
+    const int4 piece = pieces[pe];              // {item, first chunk, last chunk, p << 16 | P}
+    if (piece.x < 0) return;                    // unused entry: the whole workgroup leaves
+    const int bj = piece.x;
+    const int local = bj - set * Lk;
     const int b = local / n_kb;
     const int J = local - b * n_kb;
-    const int4 range = kvr[bj];                 // {first chunk, last chunk, live chunks}
 
     const int64_t bh = (int64_t)b * H + h;
     const int key = J * kBwdKeys + wave * 32 + r32;     // this lane's key
@@ -467,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const float* dd_bh = Dd + bh * N;
     const int32_t* cs_b = col_start + ((int64_t)b * n_sets + set) * NIV * N;
     const int32_t* ce_b = col_end + ((int64_t)b * n_sets + set) * NIV * N;
-    const int64_t meta_row = ((int64_t)set * (L / n_kb) + b) * n_qc;
+    const int64_t meta_row = ((int64_t)set * (Lk / n_kb) + b) * n_qc;
 
     // Lane offsets of the loads and of the operand reads (see SegLayout).
     using SL = SegLayout<D>;
@@ -478,7 +614,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int t_lane = (D == 128 ? 4 * a4 + half : 4 * half + a4) * SL::kPitch + 32 * ((lane >> 4) & 1) +
                        8 * (lane & 3);
 
-    int t = range.z > 0 ? range.x : INT_MAX;
+    // The first live chunk of the piece's range.
+    int t = piece.y;
+    while (t <= piece.z && !chunk_live<NIV>(meta_c, meta_row + t, J)) ++t;
+    if (t > piece.z) t = INT_MAX;
     if (t != INT_MAX) {
         DkvStage<D, NIV> stage;
         dkv_load<D, NIV>(stage, sm, 0, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b, t * kBwdRows, N, tid);
@@ -487,8 +626,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         __syncthreads();
         for (int buf = 0;; buf ^= 1) {
             int t_next = t + 1;
-            while (t_next <= range.y && !chunk_live<NIV>(meta_c, meta_row + t_next, J)) ++t_next;
-            const bool has_next = t_next <= range.y;
+            while (t_next <= piece.z && !chunk_live<NIV>(meta_c, meta_row + t_next, J)) ++t_next;
+            const bool has_next = t_next <= piece.z;
             if (has_next)
                 dkv_load<D, NIV>(stage, sm, buf ^ 1, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b,
                                  t_next * kBwdRows, N, tid);
@@ -580,9 +719,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
 
     // ---- epilogue: lane holds dK, dV of its key at d = 32 nb + 8 g + 4 half + (0..3).
+    // Piece 0 writes dK, dV; a later piece of a split block its partial sums.
     if (key < N) {
         float* dk_row = dK + (bh * N + key) * D;
         float* dv_row = dV + (bh * N + key) * D;
+        if ((piece.w >> 16) != 0) {
+            float* pb = part + ((int64_t)pslot[pe] * H + h) * (kBwdKeys * D * 2);
+            dk_row = pb + (key - J * kBwdKeys) * D;
+            dv_row = dk_row + kBwdKeys * D;
+        }
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
 #pragma unroll
@@ -815,15 +960,30 @@ hipError_t launch_kv_ranges(const TileMeta* meta_c, int n_iv, int64_t B, int64_t
     });
 }
 
+hipError_t launch_bwd_split(const int4* kvr, int64_t items, int n_sets, int min_chunks, int4* pieces,
+                            int32_t* pslot, int32_t* pwork, int4* splits, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_split_kernel, dim3(1), dim3(kSplitThreads), 0, stream, kvr, (int)items, n_sets,
+                       min_chunks, pieces, pslot, pwork, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const int4* splits, const float* part, int64_t H, int64_t N, int64_t d, int64_t n_kb,
+                             float* dk, float* dv, hipStream_t stream) {
+    auto kernel = d == 128 ? bwd_reduce_kernel<128> : bwd_reduce_kernel<64>;
+    hipLaunchKernelGGL(kernel, dim3(256), dim3(256), 0, stream, splits, part, (int)H, (int)N, (int)n_kb, dk, dv);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
-                           const TileMeta* meta_c, const int4* kvr, const int32_t* order, int64_t B, int64_t H,
-                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream,
-                           int n_sets) {
+                           const TileMeta* meta_c, const int4* pieces, const int32_t* pslot, const int32_t* order,
+                           int64_t B, int64_t H, int64_t N, int64_t d, float scale, float* dk, float* dv,
+                           float* part, hipStream_t stream, int n_sets) {
     const int64_t n_qc = (N + kBwdRows - 1) / kBwdRows;
     const int64_t n_kb = (N + kBwdKeys - 1) / kBwdKeys;
-    const int64_t grid = B * H * n_kb;
-    const int xcd = use_xcd_heads(H, B * n_kb);
+    const int64_t Lp = bwd_piece_entries(B * n_kb, n_sets);
+    const int64_t grid = H * Lp;
+    const int xcd = use_xcd_heads(H, Lp);
     const float c = scale * kLog2e;
     return dispatch_ranges(n_iv, [&](auto niv) {
         constexpr int NIV = decltype(niv)::value;
@@ -831,8 +991,8 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                            static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), lse, dd, col_start,
-                           col_end, meta_c, kvr, order, (int)H, (int)N, (int)n_qc, (int)n_kb, c, scale, xcd,
-                           n_sets > 1 ? 1 : 0, dk, dv);
+                           col_end, meta_c, pieces, pslot, order, (int)H, (int)N, (int)n_qc, (int)n_kb,
+                           (int)(B * n_kb), c, scale, xcd, n_sets > 1 ? 1 : 0, dk, dv, part);
         return hipGetLastError();
     });
 }

@@ -87,12 +87,34 @@ hipError_t launch_bwd_rowdot(const void* out, const void* dout, int64_t rows, in
 hipError_t launch_kv_ranges(const TileMeta* meta_c, int n_iv, int64_t B, int64_t N, int4* kvr, int32_t* work,
                             hipStream_t stream, int n_sets = 1);
 
-// The two gradient kernels (see fm_attn_bwd.hip).
+// Key-block pieces of the dK/dV kernel.  A key block attended by many more
+// query chunks than the average is split into P pieces of consecutive chunks
+// (at most kBwdExtraPieces extra pieces per call, only with one interval set):
+// piece 0 writes dK/dV, pieces 1..P-1 write partial sums that the reduce kernel
+// adds to them in piece order (deterministic).  With items = B * n_kb key
+// blocks per set, the piece table has Lp = items + extra entries per set:
+//   pieces[e] = {key-block item (-1: unused), first chunk, last chunk, p << 16 | P}
+//   pslot[e]  = partial slot of piece p >= 1 (-1 otherwise)
+//   pwork[e]  = estimated live chunks (-1 for unused entries: ranked last)
+//   splits[0].x = number of split blocks; splits[1 + s] = {item, P, first slot, 0}
+// min_chunks: pieces hold at least this many chunks (more when the average
+// block is longer: twice the average).
+constexpr int kBwdExtraPieces = 32;
+inline int64_t bwd_piece_entries(int64_t items, int n_sets) { return n_sets == 1 ? items + kBwdExtraPieces : items; }
+hipError_t launch_bwd_split(const int4* kvr, int64_t items, int n_sets, int min_chunks, int4* pieces,
+                            int32_t* pslot, int32_t* pwork, int4* splits, hipStream_t stream);
+
+// The two gradient kernels (see fm_attn_bwd.hip).  The dK/dV kernel runs the
+// piece table's entries in `order` (longest first within each set);
+// part: kBwdExtraPieces * H * kBwdKeys * d * 2 floats.
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
-                           const TileMeta* meta_c, const int4* kvr, const int32_t* order, int64_t B, int64_t H,
-                           int64_t N, int64_t d, float scale, float* dk, float* dv, hipStream_t stream,
-                           int n_sets = 1);
+                           const TileMeta* meta_c, const int4* pieces, const int32_t* pslot, const int32_t* order,
+                           int64_t B, int64_t H, int64_t N, int64_t d, float scale, float* dk, float* dv,
+                           float* part, hipStream_t stream, int n_sets = 1);
+// Adds the partial sums of split key blocks to dK, dV.
+hipError_t launch_bwd_reduce(const int4* splits, const float* part, int64_t H, int64_t N, int64_t d, int64_t n_kb,
+                             float* dk, float* dv, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* dd, const int32_t* col_start, const int32_t* col_end, int n_iv,
                          const TileMeta* meta, const int32_t* order, int64_t B, int64_t H, int64_t N, int64_t d,

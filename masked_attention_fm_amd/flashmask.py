@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libf
 FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_BAD_INTERVAL, FM_ERR_HIP = range(5)
 FM_TILE_SKIP, FM_TILE_FULL, FM_TILE_PARTIAL = 0, 1, 2
 FM_OPT_SCHEDULE = 1
+FM_OPT_BWD_SPLIT_CHUNKS = 2
 FM_MAX_RANGES = 4
 FM_FP8_SCORES, FM_FP8_ALL = 0, 1
 

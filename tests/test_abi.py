@@ -111,6 +111,8 @@ def test_options_and_strings(L):
     assert L.fm_set_option(fmb.FM_OPT_SCHEDULE, 7) == fmb.FM_ERR_INVALID_ARG
     assert L.fm_set_option(999, 0) == fmb.FM_ERR_INVALID_ARG
     assert L.fm_set_option(fmb.FM_OPT_SCHEDULE, 0) == fmb.FM_OK
+    assert L.fm_set_option(fmb.FM_OPT_BWD_SPLIT_CHUNKS, -1) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_set_option(fmb.FM_OPT_BWD_SPLIT_CHUNKS, 32) == fmb.FM_OK
     for s in range(5):
         assert L.fm_status_string(s)
     assert b"unknown" in L.fm_status_string(42)
@@ -236,6 +238,12 @@ def test_attn_fwd_fp8_rejects_bad_mode(L):
     for mode in (-1, 2):
         assert L.fm_attn_fwd_fp8(FAKE, FAKE, FAKE, 1.0, 1.0, 1.0, mode, FAKE, FAKE, 1, 1, 1, 128, 128, 0.125,
                                  FAKE, FAKE, None) == fmb.FM_ERR_INVALID_ARG
+
+
+def test_header_options_match_binding():
+    text = open(HEADER, encoding="utf-8").read()
+    assert re.search(r"FM_OPT_SCHEDULE = (\d+)", text).group(1) == str(fmb.FM_OPT_SCHEDULE)
+    assert re.search(r"FM_OPT_BWD_SPLIT_CHUNKS = (\d+)", text).group(1) == str(fmb.FM_OPT_BWD_SPLIT_CHUNKS)
 
 
 def test_header_fp8_modes_match_binding():

@@ -145,3 +145,88 @@ def test_bwd_dv_within_rounding_bound_of_each_weight():
     excess = np.abs(dv - ref) - bound
     log(f"dV elementwise: max (err - bound) = {excess.max():.3e}, max err/bound = {(np.abs(dv - ref) / bound).max():.3f}")
     assert excess.max() <= 0.0
+
+
+# ---------------------------------------------------------------- split key blocks
+
+@pytest.fixture
+def forced_split():
+    """Split long key blocks into pieces of at least one query chunk (the default piece
+    is 32 chunks, which these sizes never reach); the default is restored afterwards."""
+    fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 1)
+    yield
+    fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 32)
+
+
+SPLIT_CASES = [
+    # (B, H, N, d, ranges, kind): attention sinks make the first key block far longer than the rest
+    (1, 2, 2500, 128, 2, "sinks"),
+    (2, 2, 1800, 64, 2, "sinks"),
+    (1, 2, 1500, 128, 3, "random"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_split_key_blocks(forced_split, case):
+    """Key blocks split into pieces whose partial dK, dV are summed afterwards: the oracle's
+    gradients, to the same bar."""
+    B, H, N, d, K, kind = case
+    rng = np.random.default_rng(N * 7 + K)
+    s, e = multi_intervals(kind, B, K, N, rng)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=N + 3 * K)
+    log(f"bwd split {case}")
+    check_bwd(q, k, v, s, e, inputs.default_scale(d), f"bwd split {case}", multi=True, seed=N + K)
+
+
+def _split_runs(q, k, v, do, s, e, scale):
+    try:
+        fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 1)
+        a = run_bwd(q, k, v, do, s, e, scale, True)
+        b = run_bwd(q, k, v, do, s, e, scale, True)
+        fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 0)
+        c = run_bwd(q, k, v, do, s, e, scale, True)
+    finally:
+        fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 32)
+    return a, b, c
+
+
+def test_bwd_split_deterministic_and_equal_to_unsplit_up_to_summation_order():
+    """With splitting: bitwise repeatable; against the unsplit kernel, dQ is identical (its
+    kernel is unchanged) and dK, dV differ only by the order of the fp32 chunk sums (and do
+    differ somewhere, so the split path ran)."""
+    B, H, N, d = 1, 2, 2500, 128
+    s, e = multi_intervals("sinks", B, 2, N, None)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=29)
+    do = dout_for(q.shape, 29)
+    a, b, c = _split_runs(q, k, v, do, s, e, inputs.default_scale(d))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert np.array_equal(a[0], c[0])
+    for x, y in zip(a[1:], c[1:]):
+        assert np.abs(x - y).max() <= 1e-4 * max(1.0, np.abs(y).max())
+    assert not (np.array_equal(a[1], c[1]) and np.array_equal(a[2], c[2]))
+
+
+def test_bwd_split_sinks_window_workload_heads():
+    """The sinks-plus-window workload (B=1, N=32768, d=128), two heads, with the default
+    piece size (its sink key block is split): dK, dV equal the unsplit kernel's up to the
+    order of the fp32 chunk sums, dQ exactly."""
+    cfg = inputs.CONFIGS["S1"]
+    spec = inputs.config_intervals(cfg)
+    H = 2
+    q, k, v = (x[:, :H].contiguous() for x in inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed))
+    do = dout_for(q.shape, cfg.seed)
+    log("bwd S1 two heads: split against unsplit")
+    try:
+        fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 32)
+        a = run_bwd(q, k, v, do, spec.col_start, spec.col_end, inputs.default_scale(cfg.d), True)
+        fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 0)
+        c = run_bwd(q, k, v, do, spec.col_start, spec.col_end, inputs.default_scale(cfg.d), True)
+    finally:
+        fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 32)
+    assert np.array_equal(a[0], c[0])
+    for name, x, y in zip(("dK", "dV"), a[1:], c[1:]):
+        err = float(np.abs(x - y).max())
+        log(f"S1 {name}: max|split - unsplit| = {err:.3e}")
+        assert err <= 1e-4 * max(1.0, float(np.abs(y).max()))
+    assert not (np.array_equal(a[1], c[1]) and np.array_equal(a[2], c[2]))
