@@ -30,6 +30,7 @@
 // file).
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <math.h>
 
 #include "fm_internal.h"
@@ -428,6 +429,96 @@ __device__ __forceinline__ void wait_lds_tied2(v4s (&p)[NP], v4s (&q)[NP]) {
 // dO reads are issued, then this step's reads of both are waited for (they
 // are older than those), the dV products run, the next step's Q reads are
 // issued, and the dK products run.
+// S = Q K^T and dP = dO V^T for one 32-query half QB of the chunk: read r
+// (r even: Q, odd: dO) holds head-dimension chunk r / 2 of the lane's query
+// row and feeds MFMA r.  The reads are issued as inline assembly and run
+// kAheadS ahead through a ring of registers (left to itself the compiler
+// hoists all of them, and the registers they hold push the dK/dV accumulators
+// out of the vector register file).
+constexpr int kAheadS = 6;
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int CNT>
+__device__ __forceinline__ void wait_lds_one(u32x4& r) {
+    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(CNT));
+}
+template <int D, int QB, int R>
+__device__ __forceinline__ u32x4 sdp_read(uint32_t qaddr, uint32_t gaddr) {
+    using SL = SegLayout<D>;
+    constexpr int off = QB * (32 / SL::kSegs) * SL::kRowBytes + (R / 2) * 32;
+    return lds_read_b128<off>(R % 2 == 0 ? qaddr : gaddr);
+}
+template <int D, int QB, int I = 0>
+__device__ __forceinline__ void sdp_issue(u32x4 (&ring)[kAheadS], uint32_t qaddr, uint32_t gaddr) {
+    if constexpr (I < kAheadS) {
+        ring[I] = sdp_read<D, QB, I>(qaddr, gaddr);
+        sdp_issue<D, QB, I + 1>(ring, qaddr, gaddr);
+    }
+}
+template <int D, int QB, int I = 0>
+__device__ __forceinline__ void sdp_products(floatx16& s1, floatx16& dp1, const bf16x8 (&kreg)[D / 16],
+                                             const bf16x8 (&vreg)[D / 16], uint32_t qaddr, uint32_t gaddr,
+                                             u32x4 (&ring)[kAheadS]) {
+    constexpr int kN = 2 * (D / 16);
+    static_assert(kN > kAheadS, "more MFMAs than reads in flight");
+    if constexpr (I < kN) {
+        constexpr int issued = I + kAheadS < kN ? I + kAheadS : kN;
+        wait_lds_one<issued - (I + 1)>(ring[I % kAheadS]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ring[I % kAheadS]);
+        if constexpr (I % 2 == 0)
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[I / 2], s1, 0, 0, 0);
+        else
+            dp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[I / 2], dp1, 0, 0, 0);
+        if constexpr (I + kAheadS < kN) ring[I % kAheadS] = sdp_read<D, QB, I + kAheadS>(qaddr, gaddr);
+        sdp_products<D, QB, I + 1>(s1, dp1, kreg, vreg, qaddr, gaddr, ring);
+    }
+}
+
+// Steps KS .. KEND-1 of one 32-query half of the chunk, whose P and dS are
+// the tile p, ds (step KS uses its elements 8 (KS % 2) ..): the same products,
+// with the next step's reads issued only inside the half.
+template <int D, int KS, int KEND>
+__device__ __forceinline__ void dkv_products_half(const floatx16& p, const floatx16& ds, floatx16 (&dvacc)[D / 32],
+                                                  floatx16 (&dkacc)[D / 32], uint32_t gaddr, uint32_t qaddr,
+                                                  v4s (&gcur)[2 * D / 32], v4s (&qcur)[2 * D / 32]) {
+    constexpr int NP = 2 * D / 32;
+    if constexpr (KS < KEND) {
+        bf16x8 pb, sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pb[e] = (__bf16)p[8 * (KS & 1) + e];
+            sb[e] = (__bf16)ds[8 * (KS & 1) + e];
+        }
+        v4s gnext[NP], qnext[NP];
+        if constexpr (KS + 1 < KEND) {
+            issue_kt_reads<D, KS + 1>(gnext, gaddr);
+            wait_lds_tied2<NP>(gcur, qcur);
+        } else {
+            wait_lds_tied2<0>(gcur, qcur);
+        }
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(gcur[2 * nb], gcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            dvacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, dvacc[nb], 0, 0, 0);
+        }
+        if constexpr (KS + 1 < KEND) issue_kt_reads<D, KS + 1>(qnext, qaddr);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(qcur[2 * nb], qcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            dkacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dkacc[nb], 0, 0, 0);
+        }
+        dkv_products_half<D, KS + 1, KEND>(p, ds, dvacc, dkacc, gaddr, qaddr, gnext, qnext);
+    }
+}
+
 template <int D, int KS>
 __device__ __forceinline__ void dkv_products(const floatx16 (&p)[kBwdRows / 32], const floatx16 (&ds)[kBwdRows / 32],
                                              floatx16 (&dvacc)[D / 32], floatx16 (&dkacc)[D / 32], uint32_t gaddr,
@@ -646,34 +737,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             }
             wave_skip |= klo >= N;               // every key of the wavefront lies past N
             if (!wave_skip) {
-                // ---- S = Q K^T, dP = dO V^T: lane holds [query 32 qb + 8 (v/4) + 4 half + v%4][key]
-                floatx16 s[kBwdRows / 32], dp[kBwdRows / 32];
-#pragma unroll
-                for (int qb = 0; qb < kBwdRows / 32; ++qb) {
-                    s[qb] = floatx16{};
-                    dp[qb] = floatx16{};
-                }
-#pragma unroll
-                for (int cs = 0; cs < D / 16; ++cs) {
-#pragma unroll
-                    for (int qb = 0; qb < kBwdRows / 32; ++qb) {
-                        const int at = q_lane + qb * (32 / SL::kSegs) * SL::kRowBytes + cs * 32;
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.q[buf][at]);
-                        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[cs], s[qb], 0, 0, 0);
-                        const bf16x8 g = *reinterpret_cast<const bf16x8*>(&sm.go[buf][at]);
-                        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, vreg[cs], dp[qb], 0, 0, 0);
-                    }
-                }
-                // transposing reads of the first step of the dV / dK products,
-                // issued now so that their latency overlaps the softmax
+                // The chunk in two halves of 32 queries, each taken through S, dP,
+                // the weights and its share of the dV / dK products before the
+                // next: only one half's S and dP tiles are live at a time.
                 const uint32_t gaddr = lds_address(&sm.go[buf][0]) + t_lane;
                 const uint32_t qaddr = lds_address(&sm.q[buf][0]) + t_lane;
-                v4s gpart[2 * D / 32], qpart[2 * D / 32];
-                issue_kt_reads<D, 0>(gpart, gaddr);
-                issue_kt_reads<D, 0>(qpart, qaddr);
-                // ---- P = exp(scale s - LSE) inside the ranges, dS = P (dP - D)
-#pragma unroll
-                for (int qb = 0; qb < kBwdRows / 32; ++qb) {
+                auto chunk_half = [&](auto qbc) {
+                    constexpr int qb = decltype(qbc)::value;
+                    // ---- S = Q K^T, dP = dO V^T: lane holds [query 32 qb + 8 (v/4) + 4 half + v%4][key]
+                    floatx16 s1 = {}, dp1 = {};
+                    {
+                        const uint32_t qrow = lds_address(&sm.q[buf][0]) + q_lane;
+                        const uint32_t grow = lds_address(&sm.go[buf][0]) + q_lane;
+                        u32x4 ring[kAheadS];
+                        sdp_issue<D, qb>(ring, qrow, grow);
+                        sdp_products<D, qb>(s1, dp1, kreg, vreg, qrow, grow, ring);
+                    }
+                    // transposing reads of the half's first product step, issued
+                    // now so that their latency overlaps the weights
+                    v4s gpart[2 * D / 32], qpart[2 * D / 32];
+                    issue_kt_reads<D, 2 * qb>(gpart, gaddr);
+                    issue_kt_reads<D, 2 * qb>(qpart, qaddr);
+                    // ---- P = exp(scale s - LSE) inside the ranges, dS = P (dP - D)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int qi = qb * 32 + 8 * g + 4 * half;     // four consecutive queries
@@ -698,15 +783,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int v = 4 * g + q;
-                            const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][v], c, -lv[q]));
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s1[v], c, -lv[q]));
                             const float pm = ok[q] ? p : 0.f;
-                            s[qb][v] = pm;
-                            dp[qb][v] = pm * (dp[qb][v] - dv4[q]);
+                            s1[v] = pm;
+                            dp1[v] = pm * (dp1[v] - dv4[q]);
                         }
                     }
-                }
-                // ---- dV^T += dO^T P, dK^T += Q^T dS (contraction over the chunk's queries)
-                dkv_products<D, 0>(s, dp, dvacc, dkacc, gaddr, qaddr, gpart, qpart);
+                    // ---- dV^T += dO^T P, dK^T += Q^T dS over the half's 32 queries
+                    dkv_products_half<D, 2 * qb, 2 * qb + 2>(s1, dp1, dvacc, dkacc, gaddr, qaddr, gpart, qpart);
+                };
+                static_assert(kBwdRows == 64, "two halves of 32 queries");
+                chunk_half(std::integral_constant<int, 0>{});
+                chunk_half(std::integral_constant<int, 1>{});
             }
             if (has_next) {
                 dkv_store<D, NIV>(stage, sm, buf ^ 1, tid);
