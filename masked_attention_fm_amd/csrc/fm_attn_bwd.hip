@@ -480,6 +480,42 @@ __device__ __forceinline__ void sdp_products(floatx16& s1, floatx16& dp1, const 
     }
 }
 
+// S^T = K Q^T and dP^T = V dO^T of the dQ kernel for one key block: read r
+// = 4 cs + 2 jb + {0: K, 1: V} holds head-dimension chunk cs of key half jb
+// and feeds MFMA r; issued kAheadS ahead like the dK/dV kernel's reads.
+template <int D, int R>
+__device__ __forceinline__ u32x4 dq_sdp_read(uint32_t kaddr, uint32_t vaddr) {
+    using SL = SegLayout<D>;
+    constexpr int off = ((R / 2) % (kBc / 32)) * (32 / SL::kSegs) * SL::kRowBytes + (R / (kBc / 16)) * 32;
+    return lds_read_b128<off>(R % 2 == 0 ? kaddr : vaddr);
+}
+template <int D, int I = 0>
+__device__ __forceinline__ void dq_sdp_issue(u32x4 (&ring)[kAheadS], uint32_t kaddr, uint32_t vaddr) {
+    if constexpr (I < kAheadS) {
+        ring[I] = dq_sdp_read<D, I>(kaddr, vaddr);
+        dq_sdp_issue<D, I + 1>(ring, kaddr, vaddr);
+    }
+}
+template <int D, int I = 0>
+__device__ __forceinline__ void dq_sdp_products(floatx16 (&st)[kBc / 32], floatx16 (&dpt)[kBc / 32],
+                                                const bf16x8 (&qreg)[D / 16], const bf16x8 (&greg)[D / 16],
+                                                uint32_t kaddr, uint32_t vaddr, u32x4 (&ring)[kAheadS]) {
+    constexpr int kN = 2 * (D / 16) * (kBc / 32);
+    static_assert(kN > kAheadS, "more MFMAs than reads in flight");
+    if constexpr (I < kN) {
+        constexpr int cs = I / (kBc / 16), jb = (I / 2) % (kBc / 32);
+        constexpr int issued = I + kAheadS < kN ? I + kAheadS : kN;
+        wait_lds_one<issued - (I + 1)>(ring[I % kAheadS]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ring[I % kAheadS]);
+        if constexpr (I % 2 == 0)
+            st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
+        else
+            dpt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, greg[cs], dpt[jb], 0, 0, 0);
+        if constexpr (I + kAheadS < kN) ring[I % kAheadS] = dq_sdp_read<D, I + kAheadS>(kaddr, vaddr);
+        dq_sdp_products<D, I + 1>(st, dpt, qreg, greg, kaddr, vaddr, ring);
+    }
+}
+
 // Steps KS .. KEND-1 of one 32-query half of the chunk, whose P and dS are
 // the tile p, ds (step KS uses its elements 8 (KS % 2) ..): the same products,
 // with the next step's reads issued only inside the half.
@@ -960,16 +996,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                     st[jb] = floatx16{};
                     dpt[jb] = floatx16{};
                 }
-#pragma unroll
-                for (int cs = 0; cs < D / 16; ++cs) {
-#pragma unroll
-                    for (int jb = 0; jb < kBc / 32; ++jb) {
-                        const int at = jb * (32 / DL::kSegs) * DL::kRowBytes + cs * 32;
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][k_lane + at]);
-                        st[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cs], st[jb], 0, 0, 0);
-                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&sm.v[buf][v_lane + at]);
-                        dpt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, greg[cs], dpt[jb], 0, 0, 0);
-                    }
+                {
+                    const uint32_t krow = lds_address(&sm.k[buf][0]) + k_lane;
+                    const uint32_t vrow = lds_address(&sm.v[buf][0]) + v_lane;
+                    u32x4 ring[kAheadS];
+                    dq_sdp_issue<D>(ring, krow, vrow);
+                    dq_sdp_products<D>(st, dpt, qreg, greg, krow, vrow, ring);
                 }
                 // ---- dS^T = P^T (dP^T - D) with P = exp(scale s - LSE) inside the ranges
                 int base[NIV];
