@@ -471,6 +471,37 @@ __device__ __forceinline__ void pv8_bf16_direct(const bf16x8 (&pbs)[kBc / 16], f
     }
 }
 
+// The score product for e4m3 inputs: MFMA i (i = 2 cs + jb, 32 x 32 x 64) takes 32
+// bytes of K per lane half, two 16-byte reads.  All reads of the block are
+// issued first (two per MFMA, 2 D / 32 in all), then each MFMA waits for its
+// own two.
+template <int D>
+constexpr int k8_read_offset(int r) {
+    return ((r / 2) % 2) * (32 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes + (r / 4) * 64 + (r % 2) * 16;
+}
+template <int D, int R = 0>
+__device__ __forceinline__ void issue_k8_reads(u32x4 (&rd)[2 * (D / 64) * (kBc / 32)], uint32_t addr) {
+    if constexpr (R < 2 * (D / 64) * (kBc / 32)) {
+        rd[R] = lds_read_b128<k8_read_offset<D>(R)>(addr);
+        issue_k8_reads<D, R + 1>(rd, addr);
+    }
+}
+template <int D, int I = 0>
+__device__ __forceinline__ void score8_direct(floatx16 (&st)[kBc / 32], const v8i (&q)[D / 64],
+                                              u32x4 (&rd)[2 * (D / 64) * (kBc / 32)]) {
+    constexpr int kMfmas = (D / 64) * (kBc / 32);
+    static_assert(kBc / 32 == 2 && 2 * kMfmas <= 16, "two key halves; reads fit the lgkm counter");
+    if constexpr (I < kMfmas) {
+        wait_lds_one<2 * kMfmas - 2 * (I + 1)>(rd[2 * I + 1]);   // in order: 2 I done too
+        asm volatile("" : "+v"(rd[2 * I]));
+        const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(rd[2 * I], rd[2 * I + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        st[I % 2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q[I / 2], st[I % 2], 0, 0, 0, kUnitScales, 0,
+                                                                    kUnitScales);
+        __builtin_amdgcn_sched_barrier(0);   // keep MFMA i ahead of the wait for MFMA i + 1
+        score8_direct<D, I + 1>(st, q, rd);
+    }
+}
+
 // Types of one instantiation: PREC 0 bf16 inputs; 1 e4m3 inputs (V widened to
 // bf16, bf16 weights); 2 e4m3 inputs and e4m3 weights.
 template <int D, int NIV, int PREC>
@@ -681,19 +712,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
                 for (int jb = 0; jb < kBc / 32; ++jb) st[jb] = floatx16{};
                 if constexpr (F8) {
-#pragma unroll
-                    for (int cs = 0; cs < D / 64; ++cs) {
-#pragma unroll
-                        for (int jb = 0; jb < kBc / 32; ++jb) {
-                            const uint8_t* src =
-                                &sm.k8[buf][k8_lane + jb * (32 / Direct8<D>::kSegs) * Direct8<D>::kRowBytes + cs * 64];
-                            const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
-                            const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 16);
-                            const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                            st[jb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qreg[cs], st[jb], 0, 0, 0,
-                                                                                     kUnitScales, 0, kUnitScales);
-                        }
-                    }
+                    u32x4 rd[2 * (D / 64) * (kBc / 32)];
+                    issue_k8_reads<D>(rd, lds_address(&sm.k8[buf][0]) + k8_lane);
+                    score8_direct<D>(st, qreg, rd);
                 } else {
                     u32x4 ring[kAheadK];
                     const uint32_t kaddr = lds_address(&sm.k[buf][0]) + k_lane;
