@@ -424,11 +424,6 @@ __device__ __forceinline__ void wait_lds_tied2(v4s (&p)[NP], v4s (&q)[NP]) {
         static_assert(NP == 8 || NP == 4, "d = 64 or 128");
 }
 
-// dV^T += dO^T P and dK^T += Q^T dS over steps KS.. of one query chunk (gcur,
-// qcur: step KS's transposing reads of dO and Q).  Per step: the next step's
-// dO reads are issued, then this step's reads of both are waited for (they
-// are older than those), the dV products run, the next step's Q reads are
-// issued, and the dK products run.
 // S = Q K^T and dP = dO V^T for one 32-query half QB of the chunk: read r
 // (r even: Q, odd: dO) holds head-dimension chunk r / 2 of the lane's query
 // row and feeds MFMA r.  The reads are issued as inline assembly and run
@@ -516,9 +511,12 @@ __device__ __forceinline__ void dq_sdp_products(floatx16 (&st)[kBc / 32], floatx
     }
 }
 
-// Steps KS .. KEND-1 of one 32-query half of the chunk, whose P and dS are
-// the tile p, ds (step KS uses its elements 8 (KS % 2) ..): the same products,
-// with the next step's reads issued only inside the half.
+// dV^T += dO^T P and dK^T += Q^T dS over steps KS .. KEND-1 (16 queries each)
+// of one 32-query half of the chunk, whose P and dS are the tiles p, ds (step
+// KS uses their elements 8 (KS % 2) ..); gcur, qcur: step KS's transposing
+// reads of dO and Q.  Per step: the next step's dO reads are issued, then this
+// step's reads of both are waited for (they are older than those), the dV
+// products run, the next step's Q reads are issued, and the dK products run.
 template <int D, int KS, int KEND>
 __device__ __forceinline__ void dkv_products_half(const floatx16& p, const floatx16& ds, floatx16 (&dvacc)[D / 32],
                                                   floatx16 (&dkacc)[D / 32], uint32_t gaddr, uint32_t qaddr,
@@ -552,42 +550,6 @@ __device__ __forceinline__ void dkv_products_half(const floatx16& p, const float
             dkacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dkacc[nb], 0, 0, 0);
         }
         dkv_products_half<D, KS + 1, KEND>(p, ds, dvacc, dkacc, gaddr, qaddr, gnext, qnext);
-    }
-}
-
-template <int D, int KS>
-__device__ __forceinline__ void dkv_products(const floatx16 (&p)[kBwdRows / 32], const floatx16 (&ds)[kBwdRows / 32],
-                                             floatx16 (&dvacc)[D / 32], floatx16 (&dkacc)[D / 32], uint32_t gaddr,
-                                             uint32_t qaddr, v4s (&gcur)[2 * D / 32], v4s (&qcur)[2 * D / 32]) {
-    constexpr int NP = 2 * D / 32;
-    if constexpr (KS < kBwdRows / 16) {
-        bf16x8 pb, sb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pb[e] = (__bf16)p[KS >> 1][8 * (KS & 1) + e];
-            sb[e] = (__bf16)ds[KS >> 1][8 * (KS & 1) + e];
-        }
-        v4s gnext[NP], qnext[NP];
-        if constexpr (KS + 1 < kBwdRows / 16) {
-            issue_kt_reads<D, KS + 1>(gnext, gaddr);
-            wait_lds_tied2<NP>(gcur, qcur);
-        } else {
-            wait_lds_tied2<0>(gcur, qcur);
-        }
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(gcur[2 * nb], gcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            dvacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, dvacc[nb], 0, 0, 0);
-        }
-        if constexpr (KS + 1 < kBwdRows / 16) issue_kt_reads<D, KS + 1>(qnext, qaddr);
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(qcur[2 * nb], qcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            dkacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dkacc[nb], 0, 0, 0);
-        }
-        dkv_products<D, KS + 1>(p, ds, dvacc, dkacc, gaddr, qaddr, gnext, qnext);
     }
 }
 
