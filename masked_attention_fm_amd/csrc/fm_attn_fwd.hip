@@ -26,8 +26,11 @@
 //     computed, block j+1 is loaded from HBM straight into the other buffer
 //     (buffer loads with an LDS destination, no registers involved); one
 //     barrier per key block.  K is read row-major as the A operand of the
-//     score product, V transposed (ds_read_b64_tr_b16) as the A operand of
-//     the PV product (FP8 inputs: the same with bytes, see below).
+//     score product (six reads ahead of the MFMAs), V transposed
+//     (ds_read_b64_tr_b16) as the A operand of the PV product (FP8 inputs:
+//     the same with bytes, see below).  These operand reads are issued as
+//     inline assembly with explicit waits, so their pipelining does not
+//     depend on the compiler's schedule.
 //   * Softmax with lazy rescaling: a row's reference maximum may lag its
 //     running maximum by up to 2^8 in weight, so the accumulator is rescaled
 //     only when some row of the wavefront outgrows that margin.
