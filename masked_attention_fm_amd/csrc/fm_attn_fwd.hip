@@ -55,6 +55,7 @@
 
 #include <hip/hip_ext.h>
 #include <math.h>
+#include <stddef.h>
 
 #include "fm_internal.h"
 #include "fm_mfma.h"
@@ -848,11 +849,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
 
     // ---- epilogue: O = O_acc / l16 (bf16, nearest even), LSE = ln(sum) in natural log.
+    // Where the K/V buffers can hold the block's output (bf16 inputs), O goes
+    // out through LDS so that every store writes whole rows: each wavefront
+    // stages its 32 rows in its own part of those buffers, idle now (after the
+    // last block's barrier no wavefront reads them, and no load into them is
+    // in flight), then writes 16 contiguous bytes per lane.  Otherwise each
+    // lane stores its own 8-byte pieces of its row.
     const float l = halves_sum(l_run);
     const float l16 = halves_sum(l16_run);
-    if (qrow < N) {
-        float inv = l16 > 0.f ? 1.f / l16 : 0.f;
-        if constexpr (F8) inv *= v_scale;
+    float inv = l16 > 0.f ? 1.f / l16 : 0.f;
+    if constexpr (F8) inv *= v_scale;
+    constexpr int kOPitch = 2 * D + 16;           // bytes per staged row (16-byte aligned, rows 4 banks apart)
+    constexpr bool kStageO = kWaves * kRowsPerWave * kOPitch <= offsetof(typename T::Shared, start);
+    if constexpr (kStageO) {
+        uint8_t* const ost = reinterpret_cast<uint8_t*>(&sm) + wave * kRowsPerWave * kOPitch;
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 o4;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o4[q] = (__bf16)(oacc[nb][4 * g + q] * inv);
+                *reinterpret_cast<bf16x4*>(ost + r32 * kOPitch + 2 * (nb * 32 + 8 * g + 4 * half)) = o4;
+            }
+        }
+        constexpr int kLanesPerRow = 2 * D / 16;  // 16 bytes per lane
+        constexpr int kRowsPerStore = 64 / kLanesPerRow;
+        uint8_t* const obh = reinterpret_cast<uint8_t*>(O + bh * N * D);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave / kRowsPerStore; ++i) {
+            const int r = i * kRowsPerStore + lane / kLanesPerRow;
+            const int cb = 16 * (lane % kLanesPerRow);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ost + r * kOPitch + cb);
+            const int grow = row0 + wave * kRowsPerWave + r;
+            if (grow < N) *reinterpret_cast<u32x4*>(obh + (int64_t)grow * (2 * D) + cb) = v;
+        }
+    } else if (qrow < N) {
         uint16_t* orow = O + bh * N * D + (int64_t)qrow * D;
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
@@ -864,8 +896,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 *reinterpret_cast<bf16x4*>(orow + nb * 32 + 8 * g + 4 * half) = o4;
             }
         }
-        if (half == 0) LSE[bh * N + qrow] = l > 0.f ? (m_run - kW8Shift) * kLn2 + logf(l) : -INFINITY;
     }
+    if (qrow < N && half == 0) LSE[bh * N + qrow] = l > 0.f ? (m_run - kW8Shift) * kLn2 + logf(l) : -INFINITY;
 }
 
 }  // namespace
