@@ -531,8 +531,11 @@ struct FwdTypes<D, NIV, 2> : FwdTypes8<D, NIV> {};
 // col_end are [B][NIV][N]; meta holds NIV records per query block.  F8: Q, K,
 // V are e4m3 (c then includes their dequantization scales, and v_scale
 // multiplies the output); PREC 2 also rounds the weights to e4m3.
+// Two workgroups per CU in bf16; the e4m3 kernels' smaller K/V buffers and
+// register sets leave room for three, which the register limit keeps.
 template <int D, int NIV, int PREC>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PREC != 0 ? 3 : 2)))
+void attn_fwd_kernel(
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ Q,
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ K,
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ V, const int32_t* __restrict__ col_start,
@@ -849,52 +852,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
 
     // ---- epilogue: O = O_acc / l16 (bf16, nearest even), LSE = ln(sum) in natural log.
-    // Where the K/V buffers can hold the block's output (bf16 inputs), O goes
-    // out through LDS so that every store writes whole rows: each wavefront
-    // stages its 32 rows in its own part of those buffers, idle now (after the
-    // last block's barrier no wavefront reads them, and no load into them is
-    // in flight), then writes 16 contiguous bytes per lane.  Otherwise each
-    // lane stores its own 8-byte pieces of its row.
+    // O goes out through LDS so that every store writes whole rows: each
+    // wavefront stages its rows in its own part of the K/V buffers, idle now
+    // (after the last block's barrier no wavefront reads them, and no load
+    // into them is in flight), then writes 16 contiguous bytes per lane.
+    // Where those buffers cannot hold all 128 rows at once (e4m3 inputs), the
+    // rows go in two passes of 16 per wavefront; LDS operations of one
+    // wavefront take effect in issue order, so a pass may overwrite what the
+    // previous one read.
     const float l = halves_sum(l_run);
     const float l16 = halves_sum(l16_run);
     float inv = l16 > 0.f ? 1.f / l16 : 0.f;
     if constexpr (F8) inv *= v_scale;
     constexpr int kOPitch = 2 * D + 16;           // bytes per staged row (16-byte aligned, rows 4 banks apart)
-    constexpr bool kStageO = kWaves * kRowsPerWave * kOPitch <= offsetof(typename T::Shared, start);
-    if constexpr (kStageO) {
-        uint8_t* const ost = reinterpret_cast<uint8_t*>(&sm) + wave * kRowsPerWave * kOPitch;
+    constexpr int kStageRoom = (int)offsetof(typename T::Shared, start);
+    constexpr int kOTile = kWaves * kRowsPerWave * kOPitch;
+    constexpr int kOPasses = kOTile <= kStageRoom ? 1 : 2;
+    static_assert(kOTile <= kOPasses * kStageRoom, "the K/V buffers hold the staged output");
+    constexpr int kPassRows = kRowsPerWave / kOPasses;
+    constexpr int kLanesPerRow = 2 * D / 16;      // 16 bytes per lane
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    static_assert(kPassRows % kRowsPerStore == 0, "whole stores per pass");
+    uint8_t* const ost = reinterpret_cast<uint8_t*>(&sm) + wave * kPassRows * kOPitch;
+    uint8_t* const obh = reinterpret_cast<uint8_t*>(O + bh * N * D);
+    // rounded to bf16 up front: half the registers of the accumulators
+    bf16x4 o4[D / 32][4];
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
+    for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 o4;
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o4[q] = (__bf16)(oacc[nb][4 * g + q] * inv);
-                *reinterpret_cast<bf16x4*>(ost + r32 * kOPitch + 2 * (nb * 32 + 8 * g + 4 * half)) = o4;
-            }
+            for (int q = 0; q < 4; ++q) o4[nb][g][q] = (__bf16)(oacc[nb][4 * g + q] * inv);
+#pragma unroll
+    for (int pass = 0; pass < kOPasses; ++pass) {
+        if (r32 / kPassRows == pass) {
+            uint8_t* const orow = ost + (r32 - pass * kPassRows) * kOPitch;
+#pragma unroll
+            for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<bf16x4*>(orow + 2 * (nb * 32 + 8 * g + 4 * half)) = o4[nb][g];
         }
-        constexpr int kLanesPerRow = 2 * D / 16;  // 16 bytes per lane
-        constexpr int kRowsPerStore = 64 / kLanesPerRow;
-        uint8_t* const obh = reinterpret_cast<uint8_t*>(O + bh * N * D);
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave / kRowsPerStore; ++i) {
+        for (int i = 0; i < kPassRows / kRowsPerStore; ++i) {
             const int r = i * kRowsPerStore + lane / kLanesPerRow;
             const int cb = 16 * (lane % kLanesPerRow);
             const u32x4 v = *reinterpret_cast<const u32x4*>(ost + r * kOPitch + cb);
-            const int grow = row0 + wave * kRowsPerWave + r;
+            const int grow = row0 + wave * kRowsPerWave + pass * kPassRows + r;
             if (grow < N) *reinterpret_cast<u32x4*>(obh + (int64_t)grow * (2 * D) + cb) = v;
-        }
-    } else if (qrow < N) {
-        uint16_t* orow = O + bh * N * D + (int64_t)qrow * D;
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 o4;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) o4[q] = (__bf16)(oacc[nb][4 * g + q] * inv);
-                *reinterpret_cast<bf16x4*>(orow + nb * 32 + 8 * g + 4 * half) = o4;
-            }
         }
     }
     if (qrow < N && half == 0) LSE[bh * N + qrow] = l > 0.f ? (m_run - kW8Shift) * kLn2 + logf(l) : -INFINITY;
