@@ -684,6 +684,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     for (int nb = 0; nb < D / 32; ++nb) {
         dkacc[nb] = floatx16{};
         dvacc[nb] = floatx16{};
+        // Start the accumulators in the matrix unit's accumulation registers,
+        // where the products keep them.  Started as zeros in the vector
+        // registers, they were assigned across the chunk loop so that each
+        // chunk copied all 128 of them out and back (256 moves per chunk).
+        asm volatile("" : "+a"(dkacc[nb]), "+a"(dvacc[nb]));
     }
 
     const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(Q + bh * N * D, N * D * 2);
