@@ -10,6 +10,7 @@ cross-compiles; no GPU involved).
   operation returns.)
 * No packed fp32 arithmetic (v_pk_add/mul/fma_f32) anywhere.
 * No scratch (register spills) in the attention kernels.
+* The dK/dV kernel keeps its accumulators in AGPRs across the chunk loop (no copies).
 """
 import os
 import re
@@ -97,3 +98,17 @@ def test_no_packed_fp32_arithmetic(device_asm, src):
 def test_no_scratch(device_asm, src):
     for name, ins in _kernels(device_asm[src]):
         assert not any(l.startswith("scratch_") for l in ins), name
+
+
+def test_dkdv_accumulators_stay_in_accumulation_registers(device_asm):
+    """The dK/dV kernel's 2·d/32 accumulator tiles live in AGPRs for the whole chunk loop:
+    no instantiation writes AGPRs from VGPRs (a copy-out/copy-back of the accumulators
+    around each chunk showed up as hundreds of v_accvgpr_write and cost 7-12 %)."""
+    seen = 0
+    for name, ins in _kernels(device_asm["fm_attn_bwd.hip"]):
+        if "bwd_dkdv_kernel" not in name:
+            continue
+        seen += 1
+        writes = sum(1 for l in ins if l.startswith("v_accvgpr_write"))
+        assert writes <= 4, f"{name}: {writes} v_accvgpr_write"
+    assert seen == 8, seen            # d in {64, 128} x 1..4 ranges
