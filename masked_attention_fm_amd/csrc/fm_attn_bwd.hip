@@ -745,8 +745,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                 // next: only one half's S and dP tiles are live at a time.
                 const uint32_t gaddr = lds_address(&sm.go[buf][0]) + t_lane;
                 const uint32_t qaddr = lds_address(&sm.q[buf][0]) + t_lane;
-                auto chunk_half = [&](auto qbc) {
+                auto chunk_half = [&](auto qbc, auto fullc) {
                     constexpr int qb = decltype(qbc)::value;
+                    constexpr bool kFull = decltype(fullc)::value;   // one range covers every row's keys
                     // ---- S = Q K^T, dP = dO V^T: lane holds [query 32 qb + 8 (v/4) + 4 half + v%4][key]
                     floatx16 s1 = {}, dp1 = {};
                     {
@@ -770,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
                         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
                         bool ok[4] = {true, true, true, true};
-                        if (!wave_full) {
+                        if constexpr (!kFull) {
 #pragma unroll
                             for (int q = 0; q < 4; ++q) ok[q] = false;
 #pragma unroll
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                         for (int q = 0; q < 4; ++q) {
                             const int v = 4 * g + q;
                             const float p = __builtin_amdgcn_exp2f(fmaf(s1[v], c, -lv[q]));
-                            const float pm = ok[q] ? p : 0.f;
+                            const float pm = kFull || ok[q] ? p : 0.f;
                             s1[v] = pm;
                             dp1[v] = pm * (dp1[v] - dv4[q]);
                         }
@@ -796,8 +797,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     dkv_products_half<D, 2 * qb, 2 * qb + 2>(s1, dp1, dvacc, dkacc, gaddr, qaddr, gpart, qpart);
                 };
                 static_assert(kBwdRows == 64, "two halves of 32 queries");
-                chunk_half(std::integral_constant<int, 0>{});
-                chunk_half(std::integral_constant<int, 1>{});
+                if (wave_full) {
+                    chunk_half(std::integral_constant<int, 0>{}, std::true_type{});
+                    chunk_half(std::integral_constant<int, 1>{}, std::true_type{});
+                } else {
+                    chunk_half(std::integral_constant<int, 0>{}, std::false_type{});
+                    chunk_half(std::integral_constant<int, 1>{}, std::false_type{});
+                }
             }
             if (has_next) {
                 dkv_store<D, NIV>(stage, sm, buf ^ 1, tid);
