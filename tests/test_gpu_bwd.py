@@ -128,6 +128,31 @@ def test_bwd_doc_packed_workload_heads():
     log(f"bwd C2: worst relative error {worst:.3e}")
 
 
+def test_bwd_prefix_lm_workload_full_size_sampled_heads():
+    """The prefix-LM workload at its full size and launch (B = 2, H = 32, N = 16384, d = 128,
+    every head in one call, as the benchmark runs it); two heads, one per batch element,
+    compared in full with the oracle's gradients."""
+    cfg = inputs.CONFIGS["C4"]
+    spec = inputs.config_intervals(cfg)
+    scale = inputs.default_scale(cfg.d)
+    q, k, v = inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    do = dout_for(q.shape, cfg.seed)
+    log("bwd C4 full size")
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    sd, ed = to_dev(spec.col_start, spec.col_end)
+    out, lse = fm.fm_attn_fwd(qd, kd, vd, sd, ed, scale)
+    grads = [torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV) for _ in range(3)]
+    fm.fm_attn_bwd(qd, kd, vd, out, dod, lse, sd, ed, scale, dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    for g in grads:
+        assert bool(torch.isfinite(g).all()), "non-finite gradient"
+    for b, h in ((0, 5), (1, 30)):
+        got = [g[b:b + 1, h:h + 1].cpu().numpy().astype(np.float64) for g in grads]
+        ref = oracle.attention_bwd(*(x[b:b + 1, h:h + 1].float().numpy() for x in (q, k, v, do)),
+                                   spec.col_start[b:b + 1], spec.col_end[b:b + 1], scale)
+        compare_grads(got, ref, f"bwd C4 head ({b}, {h})")
+
+
 def test_bwd_dv_within_rounding_bound_of_each_weight():
     """dV = P^T dO with every weight rounded to bfloat16 (relative error <= u = 2^-8)
     and exact bf16 dO: each element obeys |dV - dV_ref| <= 2u sum_i P_ij |dO_ic| (+ fp32
