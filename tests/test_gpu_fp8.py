@@ -157,6 +157,37 @@ def test_fp8_weights_doc_packed_workload_sampled_rows():
                     fm.FM_FP8_ALL, rows=rows)
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_fp8_prefix_lm_workload_full_size_sampled(mode):
+    """The prefix-LM workload at full size (B=2, H=32, N=16384, d=128) from FP8 inputs, all
+    heads in one launch as the benchmark runs it; the mode's elementwise bound and the LSE
+    bar on sampled rows (tile edges, both prefix boundaries, random rows) of four heads of
+    each batch element."""
+    cfg = inputs.CONFIGS["C4"]
+    spec = inputs.config_intervals(cfg)
+    scale = inputs.default_scale(cfg.d)
+    qkv8 = inputs.make_qkv_fp8(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    log(f"fp8 C4 full size, mode {mode}")
+    O, L = run_fp8(qkv8, spec.col_start, spec.col_end, scale, mode)
+    rng = np.random.default_rng(7)
+    prefix_edges = [p + o for p in (spec.col_end[:, 0] + 1).tolist() for o in (-1, 0, 1)]
+    rows = np.unique(np.concatenate([[0, 127, 128, cfg.N - 1], prefix_edges, rng.integers(0, cfg.N, 22)]))
+    heads = [0, 7, 19, 31]
+    q, k, v = (inputs.dequantize_e4m3(c, sc)[:, heads] for c, sc in qkv8)
+    O_ref, L_ref = oracle.attention(q, k, v, spec.col_start, spec.col_end, scale, rows=rows)
+    P = oracle.attention_weights(q, k, spec.col_start, spec.col_end, scale, rows=rows)
+    O, L = O[:, heads][:, :, rows], L[:, heads][:, :, rows]
+    bound = fp8_bound(mode, P, v, O_ref, O)
+    err = np.abs(O - O_ref)
+    empty = np.isneginf(L_ref)
+    assert not empty.any()
+    dL = float(np.abs(L - L_ref).max())
+    log(f"fp8 C4 mode {mode}: {rows.size} rows x {len(heads)} heads x 2: max|dO|={err.max():.3e} "
+        f"max err/bound={(err / bound).max():.3f} max|dLSE|={dL:.3e}")
+    assert np.all(err <= bound), f"{(err > bound).sum()} elements beyond the rounding bound"
+    assert dL <= 1e-3
+
+
 def test_fp8_doc_packed_workload():
     """The doc-packed workload (B=1, H=16, N=8192, d=128) from FP8 inputs, all rows."""
     cfg = inputs.CONFIGS["C2"]
