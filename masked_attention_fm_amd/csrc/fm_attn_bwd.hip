@@ -27,7 +27,10 @@
 //     one query's dQ row.
 // Both double-buffer their operands through LDS (one barrier per step); the
 // dK/dV kernel runs one wavefront per SIMD (its live state fills the register
-// file).
+// file; the dK/dV accumulators stay in the accumulation registers).  A key
+// block attended by far more query chunks than the others is split into
+// pieces over equal shares of its chunks (bwd_split_kernel); later pieces
+// write fp32 partial sums that bwd_reduce_kernel adds in piece order.
 
 #include <hip/hip_runtime.h>
 #include <type_traits>
