@@ -433,7 +433,7 @@ __device__ __forceinline__ void wait_lds_tied2(v4s (&p)[NP], v4s (&q)[NP]) {
 // kAheadS ahead through a ring of registers (left to itself the compiler
 // hoists all of them, and the registers they hold push the dK/dV accumulators
 // out of the vector register file).
-constexpr int kAheadS = 6;
+constexpr int kAheadS = 7;
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
     static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
