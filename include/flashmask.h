@@ -258,7 +258,9 @@ FM_API int fm_attn_tile_shape(int64_t d, int32_t* Br, int32_t* Bc);
  *   work_out  : int32 [B*ceil(N/Br)] device; non-skip key blocks of query
  *               block t of batch b at index b*ceil(N/Br) + t.
  *   order_out : int32 [B*ceil(N/Br)] device; those indices sorted by work,
- *               largest first, ties by increasing index.
+ *               largest first, ties by increasing index.  Above 256 query
+ *               blocks the sort key is floor(work / 32) (blocks of nearly
+ *               equal work keep their index order).
  * Br, Bc are fm_attn_tile_shape(d).  Synchronous (null stream).
  */
 FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end,

@@ -206,7 +206,8 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
     } else {
         e = fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work_out,
                                   nullptr, 0);
-        if (e == hipSuccess) e = fm::launch_schedule(work_out, B * n_q, order_out, 0);
+        if (e == hipSuccess)
+            e = fm::launch_schedule(work_out, B * n_q, order_out, 0, 0, fm::kScheduleBucketShift);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(0);
     hipError_t ef = hipFree(buf);
@@ -263,7 +264,7 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* co
     } else {
         FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work, nullptr,
                                      stream, (int)n_sets));
-        if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream, B * n_q));
+        if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream, B * n_q, fm::kScheduleBucketShift));
     }
 
     std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};

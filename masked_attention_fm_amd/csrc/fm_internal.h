@@ -49,8 +49,18 @@ hipError_t launch_class_table(const TileMeta* meta, int n_iv, int64_t n_q, int64
                               hipStream_t stream);
 
 // Longest-first order (ties by index) within each segment of L consecutive
-// items (L = M: one segment): order[seg*L + rank] = item.
-hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L = 0);
+// items (L = M: one segment): order[seg*L + rank] = item.  With shift > 0 the
+// items are ranked by work >> shift, so that items of nearly equal work keep
+// their index order (for the attention kernel: the query blocks of one
+// document stay together, and the workgroups resident on an XCD share fewer
+// documents' K/V).
+hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L = 0,
+                           int shift = 0);
+
+// Work bucket of the attention kernel's order on the large-problem path:
+// 32 key blocks.  The one-workgroup path (at most kPrepSmallMax query blocks,
+// too few to fill the XCDs several times over) ranks by exact work.
+constexpr int kScheduleBucketShift = 5;
 
 // Preprocessor and scheduler in one launch of one workgroup, for at most
 // kPrepSmallMax query blocks (B * n_q): same meta, work and order outputs.

@@ -9,7 +9,10 @@
 // longest first: the long ones start early and the short ones fill the
 // tail.  The order is a stable sort by decreasing work; each item's rank is
 // counted directly (items ranked ahead of x: larger work, or equal work and
-// smaller index), which is deterministic and needs no atomics.  The order
+// smaller index), which is deterministic and needs no atomics.  On large
+// problems the attention order sorts by work in buckets of 32 key blocks, so
+// that the query blocks of one document that need about the same work run
+// together and share their K/V in the XCD's L2.  The order
 // never changes a result: every query block's output depends only on its
 // own fixed sequence of key blocks.
 
@@ -26,10 +29,10 @@ constexpr int kThreads = 256;
 // its threads' segments (uniform bounds for the barriers) and each thread
 // counts only its own segment.
 __global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __restrict__ work, int M, int L,
-                                                            int32_t* __restrict__ order) {
+                                                            int shift, int32_t* __restrict__ order) {
     __shared__ int s_work[kThreads];
     const int x = blockIdx.x * kThreads + threadIdx.x;
-    const int wx = x < M ? work[x] : INT_MIN;
+    const int wx = x < M ? (work[x] >> shift) : INT_MIN;
     const int x_first = blockIdx.x * kThreads;
     const int x_last = min(M, x_first + kThreads) - 1;
     const int y_begin = (x_first / L) * L;
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __res
     int rank = 0;
     for (int base = y_begin; base < y_end; base += kThreads) {
         const int y = base + threadIdx.x;
-        s_work[threadIdx.x] = y < y_end ? work[y] : INT_MIN;
+        s_work[threadIdx.x] = y < y_end ? (work[y] >> shift) : INT_MIN;
         __syncthreads();
         const int lim = min(kThreads, y_end - base);
         for (int i = 0; i < lim; ++i) {
@@ -164,11 +167,12 @@ hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, i
     });
 }
 
-hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L) {
+hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L,
+                           int shift) {
     if (L <= 0) L = M;
     const int64_t blocks = (M + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, work,
-                       (int)M, (int)L, order);
+                       (int)M, (int)L, shift, order);
     return hipGetLastError();
 }
 

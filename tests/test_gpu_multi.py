@@ -9,7 +9,7 @@ import oracle
 from masked_attention_fm_amd import flashmask as fm
 from masked_attention_fm_amd import inputs
 
-from test_gpu_parity import DEV, LSE_TOL, O_TOL, compare, log, to_dev
+from test_gpu_parity import DEV, LSE_TOL, O_TOL, compare, log, schedule_key, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -104,7 +104,7 @@ def test_schedule_multi_counts_union(B, N, K):
     ref = np.concatenate([(oracle.classes_minmax_multi(s[b], e[b], N, Br, Bc) != oracle.SKIP).sum(1)
                           for b in range(B)])
     assert np.array_equal(work, ref)
-    assert np.array_equal(order, np.argsort(-ref, kind="stable"))
+    assert np.array_equal(order, np.argsort(-schedule_key(ref), kind="stable"))
 
 
 # ---------------------------------------------------------------- attention
