@@ -395,7 +395,7 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     } else {
         FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, nullptr,
                                      stream, (int)n_sets));
-        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q));
+        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q, fm::kScheduleBucketShift));
     }
     // dK, dV: query chunks per key block, long key blocks split into pieces,
     // pieces longest first (within each set)
