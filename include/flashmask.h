@@ -221,10 +221,17 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
  *               nothing get dq = 0).
  *   stream    : HIP stream the work is queued on.
  *
- * Asynchronous on `stream`; deterministic (no atomics: every output element is
- * written once).  Workspace, argument checks and errors as fm_attn_fwd, whose
- * internal workspace per (device, stream) it shares (about 4 B per row and head
- * plus 40 B per query block).  Inputs must not alias the outputs.
+ * Asynchronous on `stream`; deterministic: a key block attended by many query
+ * blocks is split into pieces (see FM_OPT_BWD_SPLIT_CHUNKS) whose partial dK,
+ * dV sums are added into the output in a fixed piece order by a final
+ * reduction, so repeated calls give identical bits (the pieces are found with
+ * integer atomics, which fix only their slots, never a floating-point order).
+ * Argument checks and errors as fm_attn_fwd.  Workspace: it shares
+ * fm_attn_fwd's internal buffer per (device, stream), grown to about 4 B per
+ * row and head plus 40 B per query block and, with one interval set for all
+ * heads, the split pieces' partial sums, 32 * H * 128 * d * 8 bytes (128 MiB
+ * at H = 32, d = 128); the buffer is kept until the process ends.  Inputs must
+ * not alias the outputs.
  */
 FM_API int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                        const float* lse, const int32_t* col_start, const int32_t* col_end,

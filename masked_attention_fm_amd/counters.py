@@ -3,11 +3,14 @@
     python -m masked_attention_fm_amd.counters OUT.json COPY_MIB RUN_DIR [RUN_DIR ...]
 
 Each RUN_DIR is the output directory of one ``rocprofv3 --pmc ... -o run
---output-format csv -- python3 bench.py --config CFG --copy-mib M ...`` pass.
-The record holds, per counter, the mean over the attention kernel's
-dispatches and over the reference copy's dispatches, the HBM byte
-calibration that the copy of known size gives, and a hash of the attention
-kernel source so that a later change of the kernel makes the record stale.
+--output-format csv -- python3 bench.py --config CFG --no-per-config
+--no-backward --no-fp8 --no-cpu-baseline --copy-mib M ...`` pass.  The record
+holds, per counter, the mean over the dispatches of the bf16 attention kernel
+(``attn_fwd_kernel<d, ranges, 0>``; the FP8 instances are other kernels and
+never counted) and over the reference copy's dispatches, the byte calibration
+that the copy of known size gives, and a hash of the code that decides what
+the attention launch does (kernel, preprocessor, scheduler, launch set-up) so
+that a later change makes the record stale.
 """
 from __future__ import annotations
 
@@ -15,12 +18,22 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# The attention kernel and the headers whose device helpers it inlines.
-ATTN_SOURCES = [os.path.join(PKG, "csrc", name) for name in ("fm_attn_fwd.hip", "fm_internal.h", "fm_mfma.h")]
+# The attention kernel, the headers whose device helpers it inlines, and the code that
+# fixes its launch order and grid (the order changes which K/V blocks the L2 still
+# holds, so it changes the traffic).
+ATTN_SOURCES = [os.path.join(PKG, "csrc", name) for name in
+                ("fm_attn_fwd.hip", "fm_internal.h", "fm_mfma.h", "fm_schedule.hip", "fm_intervals.hip",
+                 "fm_api.hip")]
+
+# One bf16 MFMA v_mfma_f32_32x32x16_bf16: 2 * 32 * 32 * 16 FLOPs.
+MFMA_FLOPS = 2 * 32 * 32 * 16
+
+_BF16_ATTN = re.compile(r"attn_fwd_kernel<\s*\d+\s*,\s*\d+\s*,\s*0\s*>")
 
 
 def code_text(text: str) -> str:
@@ -35,8 +48,8 @@ def code_text(text: str) -> str:
 
 
 def attn_source_hash(sources=None) -> str:
-    """sha256 (first 16 hex) over the code of the attention kernel's sources (comments
-    and whitespace ignored).  `sources`: texts to hash instead of the files."""
+    """sha256 (first 16 hex) over the code of the attention launch's sources (comments and
+    whitespace ignored).  `sources`: texts to hash instead of the files."""
     h = hashlib.sha256()
     if sources is None:
         sources = []
@@ -48,8 +61,9 @@ def attn_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def _kind(name: str) -> str:
-    if "attn_fwd_kernel" in name:
+def kind_of(name: str) -> str:
+    """'attention' for the bf16 attention kernel, 'copy' for the runtime's buffer copy."""
+    if _BF16_ATTN.search(name):
         return "attention"
     if "copyBuffer" in name:
         return "copy"
@@ -62,7 +76,7 @@ def summarise(run_dirs, copy_mib: int):
         path = os.path.join(d, "run_counter_collection.csv")
         with open(path, newline="") as f:
             for row in csv.DictReader(f):
-                kind = _kind(row["Kernel_Name"])
+                kind = kind_of(row["Kernel_Name"])
                 if not kind:
                     continue
                 value = float(row["Counter_Value"])
@@ -71,8 +85,9 @@ def summarise(run_dirs, copy_mib: int):
                     continue
                 sums[kind][row["Counter_Name"]].append(value)
     mean = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in sums.items()}
+    dispatches = {k: {c: len(v) for c, v in cs.items()} for k, cs in sums.items()}
     out = {"attention": mean["attention"], "copy": mean["copy"], "copy_mib": copy_mib,
-           "attn_source_sha256_16": attn_source_hash()}
+           "dispatches": dispatches, "attn_source_sha256_16": attn_source_hash()}
     copy_kib = copy_mib * 1024.0
     cal = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -80,15 +95,23 @@ def summarise(run_dirs, copy_mib: int):
             cal[c] = copy_kib / mean["copy"][c]          # true KiB per counted KiB
     out["calibration"] = cal
     att = mean["attention"]
+    # FETCH_SIZE counts L2 misses, which the MALL (Infinity Cache) or HBM serves: the
+    # scaled sum is an upper bound on the HBM bytes of one launch.
     if "FETCH_SIZE" in att and "FETCH_SIZE" in cal and "WRITE_SIZE" in att and "WRITE_SIZE" in cal:
-        out["hbm_bytes_per_launch"] = 1024.0 * (att["FETCH_SIZE"] * cal["FETCH_SIZE"]
-                                                + att["WRITE_SIZE"] * cal["WRITE_SIZE"])
-        out["hbm_read_bytes_per_launch"] = 1024.0 * att["FETCH_SIZE"] * cal["FETCH_SIZE"]
-        out["hbm_write_bytes_per_launch"] = 1024.0 * att["WRITE_SIZE"] * cal["WRITE_SIZE"]
+        out["l2_miss_bytes_per_launch"] = 1024.0 * (att["FETCH_SIZE"] * cal["FETCH_SIZE"]
+                                                    + att["WRITE_SIZE"] * cal["WRITE_SIZE"])
+        out["l2_miss_read_bytes_per_launch"] = 1024.0 * att["FETCH_SIZE"] * cal["FETCH_SIZE"]
+        out["write_bytes_per_launch"] = 1024.0 * att["WRITE_SIZE"] * cal["WRITE_SIZE"]
     if "SQ_LDS_BANK_CONFLICT" in att:
         out["lds_bank_conflict_cycles"] = att["SQ_LDS_BANK_CONFLICT"]
+        if att.get("SQ_LDS_IDX_ACTIVE"):
+            out["lds_bank_conflict_per_lds_active"] = att["SQ_LDS_BANK_CONFLICT"] / att["SQ_LDS_IDX_ACTIVE"]
     if "SQ_VALU_MFMA_BUSY_CYCLES" in att and "SQ_BUSY_CU_CYCLES" in att:
         out["mfma_busy_per_cu_busy"] = att["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * att["SQ_BUSY_CU_CYCLES"])
+    if "SQ_INSTS_MFMA" in att:
+        out["mfma_flops_per_launch"] = att["SQ_INSTS_MFMA"] * MFMA_FLOPS
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in att and "SQ_VALU_MFMA_BUSY_CYCLES" in att:
+        out["mfma_valu_coexec_per_mfma_busy"] = att["SQ_VALU_MFMA_COEXEC_CYCLES"] / att["SQ_VALU_MFMA_BUSY_CYCLES"]
     return out
 
 

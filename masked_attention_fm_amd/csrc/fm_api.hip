@@ -49,37 +49,50 @@ int g_bwd_min_chunks = 32; // smallest piece of a split key block (query chunks)
 // buffer per (device, stream) is kept and grown in stream order, so
 // back-to-back calls on a stream reuse it and calls on different streams
 // never share it.  It lives until the process ends.
+//
+// A call holds its buffer's lock from the moment it takes the buffer until
+// every kernel that uses it is queued.  A second host thread on the same
+// (device, stream) that needs a larger buffer therefore queues its
+// hipFreeAsync of the old one after those kernels, and stream order keeps
+// the old buffer alive until they have run.
 
 struct Workspace {
+    std::mutex mu;            // held while a call queues work that uses ptr
     void* ptr = nullptr;
     size_t bytes = 0;
 };
-std::mutex g_ws_mutex;
+std::mutex g_ws_map_mutex;    // guards the map itself (its nodes never move)
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out) {
+// On success *out is the buffer and `hold` owns its lock; the caller keeps
+// `hold` until its last launch that uses the buffer is queued.
+hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out, std::unique_lock<std::mutex>& hold) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[{dev, stream}];
-    if (w.bytes < bytes) {
-        if (w.ptr != nullptr) {
-            e = hipFreeAsync(w.ptr, stream);
-            w.ptr = nullptr;
-            w.bytes = 0;
+    Workspace* w = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_ws_map_mutex);
+        w = &g_ws[{dev, stream}];
+    }
+    hold = std::unique_lock<std::mutex>(w->mu);
+    if (w->bytes < bytes) {
+        if (w->ptr != nullptr) {
+            e = hipFreeAsync(w->ptr, stream);
+            w->ptr = nullptr;
+            w->bytes = 0;
             if (e != hipSuccess) return e;
         }
         size_t nb = std::max(bytes, size_t(64) << 10);
         nb = (nb + 0xFFFF) & ~size_t(0xFFFF);
-        e = hipMallocAsync(&w.ptr, nb, stream);
+        e = hipMallocAsync(&w->ptr, nb, stream);
         if (e != hipSuccess) {
-            w.ptr = nullptr;
+            w->ptr = nullptr;
             return e;
         }
-        w.bytes = nb;
+        w->bytes = nb;
     }
-    *out = w.ptr;
+    *out = w->ptr;
     return hipSuccess;
 }
 
@@ -251,7 +264,8 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* co
     const size_t meta_bytes = ((size_t)(M * n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
     const size_t int_bytes = ((size_t)M * sizeof(int32_t) + 255) & ~size_t(255);
     void* ws = nullptr;
-    FM_HIP(get_workspace(stream, meta_bytes + 2 * int_bytes, &ws));
+    std::unique_lock<std::mutex> ws_hold;       // held until the last launch below is queued
+    FM_HIP(get_workspace(stream, meta_bytes + 2 * int_bytes, &ws, ws_hold));
     auto* meta = static_cast<fm::TileMeta*>(ws);
     auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes);
     auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes + int_bytes);
@@ -371,7 +385,8 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     const size_t part_floats = n_sets == 1 ? (size_t)fm::kBwdExtraPieces * H * fm::kBwdKeys * d * 2 : 0;
     const size_t total = o_part + al(part_floats * sizeof(float));
     void* ws = nullptr;
-    FM_HIP(get_workspace(stream, total, &ws));
+    std::unique_lock<std::mutex> ws_hold;       // held until the last launch below is queued
+    FM_HIP(get_workspace(stream, total, &ws, ws_hold));
     char* w = static_cast<char*>(ws);
     auto* meta_q = reinterpret_cast<fm::TileMeta*>(w);
     auto* work_q = reinterpret_cast<int32_t*>(w + o_work_q);

@@ -95,6 +95,13 @@ def _stream_handle(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _require_scale(scale):
+    """The score scale is the caller's (typically 1/sqrt(d) as a float32 value): the
+    binding computes none, so every caller passes the exact value the oracle also uses."""
+    if scale is None:
+        raise ValueError("scale is required (the float32 value multiplying q.k, e.g. 1/sqrt(d))")
+
+
 def _dev_tensor(x: torch.Tensor, name: str, dtype: torch.dtype):
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -194,8 +201,7 @@ def fm_tile_schedule_multi(col_start: torch.Tensor, col_end: torch.Tensor, d: in
 
 def _attn(func: str, q, k, v, col_start, col_end, n_ranges: Optional[int], scale, out, lse, stream):
     B, H, N, d = q.shape
-    if scale is None:
-        scale = 1.0 / (d ** 0.5)
+    _require_scale(scale)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -266,8 +272,7 @@ def fm_attn_fwd_per_head(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_
     _intervals(col_start, col_end, (B, H, col_start.shape[2], N), "[B, H, K, N]")
     if not (col_start.is_contiguous() and col_end.is_contiguous()):
         raise ValueError("col_start / col_end must be contiguous")
-    if scale is None:
-        scale = 1.0 / (d ** 0.5)
+    _require_scale(scale)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -315,8 +320,7 @@ def fm_attn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scal
             raise ValueError("col_start / col_end must be [B, N] or [B, K, N]")
         _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
         n_ranges = col_start.shape[1]
-    if scale is None:
-        scale = 1.0 / (d ** 0.5)
+    _require_scale(scale)
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     else:
@@ -347,8 +351,7 @@ def _bwd(func: str, q, k, v, out, dout, lse, col_start, col_end, n_ranges: Optio
     _dev_tensor(lse, "lse", torch.float32)
     if tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be [B, H, N]")
-    if scale is None:
-        scale = 1.0 / (d ** 0.5)
+    _require_scale(scale)
     grads = []
     for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
         if g is None:

@@ -53,6 +53,7 @@ def effective_flops(col_start: np.ndarray, col_end: np.ndarray, N: int, H: int, 
     return 4 * d * H * attended_pairs(col_start, col_end, N)
 
 
-def algorithmic_bytes(B: int, H: int, N: int, d: int) -> int:
-    """Q, K, V read once, O written once (bf16), LSE written once (fp32), intervals read once."""
-    return 4 * B * H * N * d * 2 + B * H * N * 4 + 2 * B * N * 4
+def algorithmic_bytes(B: int, H: int, N: int, d: int, n_ranges: int = 1) -> int:
+    """Q, K, V read once, O written once (bf16), LSE written once (fp32), the intervals
+    (start and end, int32, n_ranges per row) read once."""
+    return 4 * B * H * N * d * 2 + B * H * N * 4 + 2 * B * n_ranges * N * 4

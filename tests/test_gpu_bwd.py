@@ -232,21 +232,46 @@ def test_bwd_split_deterministic_and_equal_to_unsplit_up_to_summation_order():
     assert not (np.array_equal(a[1], c[1]) and np.array_equal(a[2], c[2]))
 
 
+def oracle_bwd_by_head(q, k, v, do, s, e, scale):
+    """oracle.attention_bwd of every head, one head per thread (BLAS at one thread per
+    call; no process is forked from the test process, which holds the GPU)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    B, H = q.shape[:2]
+    arrays = [x.float().numpy() for x in (q, k, v, do)]
+
+    def one(bh):
+        b, h = bh
+        return oracle.attention_bwd(*(x[b:b + 1, h:h + 1] for x in arrays), s[b:b + 1], e[b:b + 1], scale)
+
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    with threadpool_limits(1), ThreadPoolExecutor(min(16, len(heads))) as ex:
+        res = list(ex.map(one, heads))
+    grads = [np.zeros(q.shape, np.float64) for _ in range(3)]
+    for (b, h), r in zip(heads, res):
+        for g, x in zip(grads, r):
+            g[b, h] = x[0, 0]
+    return grads
+
+
+@pytest.mark.timeout(600)
 def test_bwd_split_sinks_window_workload_heads():
-    """The sinks-plus-window workload (B=1, N=32768, d=128), two heads, with the default
-    piece size (its sink key block is split): dK, dV equal the unsplit kernel's up to the
-    order of the fp32 chunk sums, dQ exactly."""
+    """The sinks-plus-window workload (B=1, N=32768, d=128), four whole heads, with the
+    default piece size (its sink key block is split): dQ, dK, dV against the float64
+    oracle's gradients on every row; dK, dV also equal the unsplit kernel's up to the
+    order of the fp32 chunk sums, and dQ exactly."""
     cfg = inputs.CONFIGS["S1"]
     spec = inputs.config_intervals(cfg)
-    H = 2
+    scale = inputs.default_scale(cfg.d)
+    H = 4
     q, k, v = (x[:, :H].contiguous() for x in inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed))
     do = dout_for(q.shape, cfg.seed)
-    log("bwd S1 two heads: split against unsplit")
+    log("bwd S1 four heads: split against unsplit and against the oracle")
     try:
         fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 32)
-        a = run_bwd(q, k, v, do, spec.col_start, spec.col_end, inputs.default_scale(cfg.d), True)
+        a = run_bwd(q, k, v, do, spec.col_start, spec.col_end, scale, True)
         fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 0)
-        c = run_bwd(q, k, v, do, spec.col_start, spec.col_end, inputs.default_scale(cfg.d), True)
+        c = run_bwd(q, k, v, do, spec.col_start, spec.col_end, scale, True)
     finally:
         fm.fm_set_option(fm.FM_OPT_BWD_SPLIT_CHUNKS, 32)
     assert np.array_equal(a[0], c[0])
@@ -255,3 +280,6 @@ def test_bwd_split_sinks_window_workload_heads():
         log(f"S1 {name}: max|split - unsplit| = {err:.3e}")
         assert err <= 1e-4 * max(1.0, float(np.abs(y).max()))
     assert not (np.array_equal(a[1], c[1]) and np.array_equal(a[2], c[2]))
+    ref = oracle_bwd_by_head(q, k, v, do, spec.col_start, spec.col_end, scale)
+    worst = compare_grads(a, ref, "bwd S1 four heads (split) vs oracle")
+    log(f"bwd S1: worst relative error {worst:.3e}")

@@ -9,6 +9,7 @@ import oracle
 from masked_attention_fm_amd import flashmask as fm
 from masked_attention_fm_amd import inputs
 
+import full_parity
 from test_gpu_parity import DEV, LSE_TOL, O_TOL, compare, log, schedule_key, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -205,21 +206,16 @@ def test_multi_q_zero_is_union_mean():
         assert np.abs(L[0, :, i] - np.log(n)).max() <= LSE_TOL
 
 
-def test_sinks_window_workload_sampled():
+@pytest.mark.timeout(900)
+def test_sinks_window_workload_every_row():
     """The sinks-plus-window workload at full size, in the launch configuration the
-    benchmark times, on sampled rows: the first rows, block edges, the rows where
-    the window leaves the sinks, and random rows, for every head."""
+    benchmark times, every row of every head against the float64 oracle."""
     cfg = inputs.CONFIGS["S1"]
     spec = inputs.config_intervals(cfg)
-    w, sinks = cfg.param("window"), cfg.param("sinks")
+    scale = inputs.default_scale(cfg.d)
     q, k, v = inputs.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
-    rng = np.random.default_rng(cfg.seed)
-    join = w + sinks
-    picks = {0, 1, sinks - 1, sinks, sinks + 1, 127, 128, w - 1, w, join - 2, join - 1, join, join + 1,
-             cfg.N // 2, cfg.N - 1}
-    picks.update(int(x) for x in rng.integers(0, cfg.N, 200))
-    rows = np.array(sorted(picks))
     log(f"workload {cfg.describe()}")
-    dO, dL = check_multi(q, k, v, spec.col_start, spec.col_end, inputs.default_scale(cfg.d),
-                         "S1 sinks+window", rows=rows)
-    log(f"S1: worst max|dO|={dO:.3e} max|dLSE|={dL:.3e} ({len(rows)} sampled rows, all {cfg.H} heads)")
+    out, lse = run_multi(*to_dev(q, k, v, spec.col_start, spec.col_end), scale)
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any(), "unwritten output"
+    del q, k, v
+    full_parity.compare_every_row(cfg, spec, out, lse, scale, O_TOL, LSE_TOL, log)

@@ -80,10 +80,10 @@ def test_per_head_equal_sets_match_shared(H, N):
     spec = inputs.make_intervals("doc_uniform", B, N, 9, lo=100, hi=1500)
     q, k, v = to_dev(*inputs.make_qkv(B, H, N, d, seed=9))
     sd, ed = to_dev(spec.col_start, spec.col_end)
-    o1, l1 = fm.fm_attn_fwd(q, k, v, sd, ed)
+    o1, l1 = fm.fm_attn_fwd(q, k, v, sd, ed, inputs.default_scale(d))
     sh = sd[:, None, None].expand(B, H, 1, N).contiguous()
     eh = ed[:, None, None].expand(B, H, 1, N).contiguous()
-    o2, l2 = fm.fm_attn_fwd_per_head(q, k, v, sh, eh)
+    o2, l2 = fm.fm_attn_fwd_per_head(q, k, v, sh, eh, inputs.default_scale(d))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
@@ -97,8 +97,8 @@ def test_per_head_backward(B, H, N, d):
     do = dout_for(q.shape, N)
     qd, kd, vd, dod = to_dev(q, k, v, do)
     sd, ed = to_dev(s, e)
-    out, lse = fm.fm_attn_fwd_per_head(qd, kd, vd, sd, ed)
-    dq, dk, dv = fm.fm_attn_bwd_per_head(qd, kd, vd, out, dod, lse, sd, ed)
+    out, lse = fm.fm_attn_fwd_per_head(qd, kd, vd, sd, ed, inputs.default_scale(d))
+    dq, dk, dv = fm.fm_attn_bwd_per_head(qd, kd, vd, out, dod, lse, sd, ed, inputs.default_scale(d))
     torch.cuda.synchronize()
     got = [g.cpu().numpy().astype(np.float64) for g in (dq, dk, dv)]
     qf, kf, vf, dof = (x.float().numpy() for x in (q, k, v, do))
@@ -115,11 +115,11 @@ def test_per_head_backward_equal_sets_match_shared():
     q, k, v = to_dev(*inputs.make_qkv(B, H, N, d, seed=11))
     do = to_dev(dout_for((B, H, N, d), 11))[0]
     sd, ed = to_dev(spec.col_start, spec.col_end)
-    out, lse = fm.fm_attn_fwd(q, k, v, sd, ed)
-    g1 = fm.fm_attn_bwd(q, k, v, out, do, lse, sd, ed)
+    out, lse = fm.fm_attn_fwd(q, k, v, sd, ed, inputs.default_scale(d))
+    g1 = fm.fm_attn_bwd(q, k, v, out, do, lse, sd, ed, inputs.default_scale(d))
     sh = sd[:, None, None].expand(B, H, 1, N).contiguous()
     eh = ed[:, None, None].expand(B, H, 1, N).contiguous()
-    g2 = fm.fm_attn_bwd_per_head(q, k, v, out, do, lse, sh, eh)
+    g2 = fm.fm_attn_bwd_per_head(q, k, v, out, do, lse, sh, eh, inputs.default_scale(d))
     torch.cuda.synchronize()
     for a, b_ in zip(g1, g2):
         assert torch.equal(a, b_)

@@ -66,20 +66,35 @@ def _write_run(d, rows):
 
 
 def test_counter_summary_calibrates_with_the_copy(tmp_path):
-    attn = "void fm::(anonymous namespace)::attn_fwd_kernel<128>(...)"
+    attn = "void fm::(anonymous namespace)::attn_fwd_kernel<128, 1, 0>(...)"
+    fp8 = "void fm::(anonymous namespace)::attn_fwd_kernel<128, 1, 1>(...)"   # another kernel: never counted
     copy = "__amd_rocclr_copyBuffer"
     _write_run(tmp_path / "fetch", [(attn, "FETCH_SIZE", 1000.0), (attn, "FETCH_SIZE", 1200.0),
-                                    (copy, "FETCH_SIZE", 2.0), (copy, "FETCH_SIZE", 262144.0)])
-    _write_run(tmp_path / "write", [(attn, "WRITE_SIZE", 300.0), (copy, "WRITE_SIZE", 524288.0)])
+                                    (fp8, "FETCH_SIZE", 9e9), (copy, "FETCH_SIZE", 2.0),
+                                    (copy, "FETCH_SIZE", 262144.0)])
+    _write_run(tmp_path / "write", [(attn, "WRITE_SIZE", 300.0), (fp8, "WRITE_SIZE", 9e9),
+                                    (copy, "WRITE_SIZE", 524288.0)])
     _write_run(tmp_path / "mfma", [(attn, "SQ_VALU_MFMA_BUSY_CYCLES", 400.0), (attn, "SQ_BUSY_CU_CYCLES", 200.0),
-                                   (attn, "SQ_LDS_BANK_CONFLICT", 0.0)])
+                                   (attn, "SQ_LDS_BANK_CONFLICT", 5.0), (attn, "SQ_LDS_IDX_ACTIVE", 50.0),
+                                   (attn, "SQ_INSTS_MFMA", 3.0), (fp8, "SQ_INSTS_MFMA", 1e9)])
     rec = counters.summarise([tmp_path / "fetch", tmp_path / "write", tmp_path / "mfma"], copy_mib=512)
     assert rec["calibration"]["FETCH_SIZE"] == pytest.approx(2.0)     # the tiny helper copy is ignored
     assert rec["calibration"]["WRITE_SIZE"] == pytest.approx(1.0)
-    assert rec["hbm_read_bytes_per_launch"] == pytest.approx(1024 * 1100 * 2.0)
-    assert rec["hbm_write_bytes_per_launch"] == pytest.approx(1024 * 300)
+    assert rec["l2_miss_read_bytes_per_launch"] == pytest.approx(1024 * 1100 * 2.0)
+    assert rec["write_bytes_per_launch"] == pytest.approx(1024 * 300)
+    assert rec["l2_miss_bytes_per_launch"] == pytest.approx(1024 * (1100 * 2.0 + 300))
     assert rec["mfma_busy_per_cu_busy"] == pytest.approx(0.5)
+    assert rec["lds_bank_conflict_per_lds_active"] == pytest.approx(0.1)
+    assert rec["mfma_flops_per_launch"] == pytest.approx(3 * 32768)
+    assert rec["dispatches"]["attention"]["FETCH_SIZE"] == 2
     assert rec["attn_source_sha256_16"] == counters.attn_source_hash()
+
+
+def test_counter_kernel_filter():
+    assert counters.kind_of("void fm::(anonymous namespace)::attn_fwd_kernel<64, 4, 0>(int)") == "attention"
+    for name in ("attn_fwd_kernel<128, 1, 1>", "attn_fwd_kernel<128, 2, 2>", "bwd_dq_kernel<128, 1>",
+                 "prep_small_kernel<1>"):
+        assert counters.kind_of(name) == ""
 
 
 def test_code_hash_ignores_comments_and_whitespace():
