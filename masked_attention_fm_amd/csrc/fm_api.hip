@@ -208,9 +208,13 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
     if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
     const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
     if (B * n_q >= (int64_t(1) << 31)) return FM_ERR_INVALID_ARG;
+    const int64_t n_kv = (N + fm::kBc - 1) / fm::kBc;
+    const size_t meta_bytes = ((size_t)(B * n_q * n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
+    const int64_t sched_ints = fm::schedule_scratch_ints(B * n_q, B * n_q, fm::kScheduleBucketShift, (int)n_kv);
     void* buf = nullptr;
-    FM_HIP(hipMalloc(&buf, (size_t)(B * n_q * n_ranges) * sizeof(fm::TileMeta)));
+    FM_HIP(hipMalloc(&buf, meta_bytes + (size_t)sched_ints * sizeof(int32_t)));
     auto* meta = static_cast<fm::TileMeta*>(buf);
+    auto* sched = reinterpret_cast<int32_t*>(static_cast<char*>(buf) + meta_bytes);
     // the same path fm_attn_fwd takes for this size
     hipError_t e;
     if (B * n_q <= fm::kPrepSmallMax) {
@@ -220,7 +224,8 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
         e = fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work_out,
                                   nullptr, 0);
         if (e == hipSuccess)
-            e = fm::launch_schedule(work_out, B * n_q, order_out, 0, 0, fm::kScheduleBucketShift);
+            e = fm::launch_schedule(work_out, B * n_q, order_out, 0, 0, fm::kScheduleBucketShift, (int)n_kv,
+                                    sched);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(0);
     hipError_t ef = hipFree(buf);
@@ -238,49 +243,97 @@ FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, in
 
 namespace {
 
-// The forward pass for bf16 inputs (fp8_scales == nullptr) or e4m3 inputs with
-// their three dequantization scales (and, with fp8_weights, e4m3 weights).
-int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* col_start, const int32_t* col_end,
-                  int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
-                  hipStream_t stream, const float* fp8_scales, bool per_head = false, bool fp8_weights = false) {
-    // ---- host-side checks, before any HIP call
-    if (q == nullptr || k == nullptr || v == nullptr || col_start == nullptr || col_end == nullptr ||
-        out == nullptr || lse == nullptr)
-        return FM_ERR_INVALID_ARG;
-    if (n_ranges < 1 || n_ranges > fm::kMaxRanges) return FM_ERR_INVALID_ARG;
-    if (B < 1 || H < 1 || N < 1 || N > kMaxAttnN) return FM_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
-    if (!(scale > 0.f) || !isfinite(scale)) return FM_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(lse, 4) || !aligned(col_start, 4) || !aligned(col_end, 4))
-        return FM_ERR_INVALID_ARG;
-    const int64_t n_q = (N + fm::kBr - 1) / fm::kBr;
-    const int64_t n_sets = per_head ? H : 1;   // interval sets per batch element
-    if (B * H * n_q >= (int64_t(1) << 31) || B * n_sets * n_ranges * N >= (int64_t(1) << 40))
-        return FM_ERR_INVALID_ARG;
+// ---- the forward pass, in three parts: host-side checks, the workspace plan,
+// and the launches into a given workspace.
 
-    // ---- workspace: meta[M][n_ranges] | work[M] | order[M], M = n_sets * B * n_q
-    const int64_t M = n_sets * B * n_q;
-    const size_t meta_bytes = ((size_t)(M * n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
-    const size_t int_bytes = ((size_t)M * sizeof(int32_t) + 255) & ~size_t(255);
-    void* ws = nullptr;
-    std::unique_lock<std::mutex> ws_hold;       // held until the last launch below is queued
-    FM_HIP(get_workspace(stream, meta_bytes + 2 * int_bytes, &ws, ws_hold));
+struct FwdArgs {
+    const void *q, *k, *v;
+    const int32_t *col_start, *col_end;
+    int32_t n_ranges;
+    int64_t B, H, N, d;
+    float scale;
+    void* out;
+    float* lse;
+    hipStream_t stream;
+    const float* fp8_scales;   // nullptr: bf16 inputs; else the three e4m3 dequantization scales
+    bool per_head;             // one interval set per head
+    bool fp8_weights;          // e4m3 weights and an FP8 PV product
+};
+
+int fwd_check(const FwdArgs& a) {
+    if (a.q == nullptr || a.k == nullptr || a.v == nullptr || a.col_start == nullptr || a.col_end == nullptr ||
+        a.out == nullptr || a.lse == nullptr)
+        return FM_ERR_INVALID_ARG;
+    if (a.n_ranges < 1 || a.n_ranges > fm::kMaxRanges) return FM_ERR_INVALID_ARG;
+    if (a.B < 1 || a.H < 1 || a.N < 1 || a.N > kMaxAttnN) return FM_ERR_INVALID_ARG;
+    if (a.d != 64 && a.d != 128) return FM_ERR_UNSUPPORTED;
+    if (!(a.scale > 0.f) || !isfinite(a.scale)) return FM_ERR_INVALID_ARG;
+    if (!aligned(a.q, 16) || !aligned(a.k, 16) || !aligned(a.v, 16) || !aligned(a.out, 16) || !aligned(a.lse, 4) ||
+        !aligned(a.col_start, 4) || !aligned(a.col_end, 4))
+        return FM_ERR_INVALID_ARG;
+    const int64_t n_q = (a.N + fm::kBr - 1) / fm::kBr;
+    const int64_t n_sets = a.per_head ? a.H : 1;
+    if (a.B * a.H * n_q >= (int64_t(1) << 31) || a.B * n_sets * a.n_ranges * a.N >= (int64_t(1) << 40))
+        return FM_ERR_INVALID_ARG;
+    return FM_OK;
+}
+
+// Workspace layout: meta[M][n_ranges] | work[M] | order[M] | scheduler scratch,
+// M = n_sets * B * n_q, each part 256-byte aligned.
+struct FwdPlan {
+    int64_t n_q, n_kv, n_sets, M;
+    size_t meta_bytes, int_bytes, sched_bytes;
+    size_t total() const { return meta_bytes + 2 * int_bytes + sched_bytes; }
+};
+
+FwdPlan fwd_plan(const FwdArgs& a) {
+    FwdPlan p;
+    p.n_q = (a.N + fm::kBr - 1) / fm::kBr;
+    p.n_kv = (a.N + fm::kBc - 1) / fm::kBc;
+    p.n_sets = a.per_head ? a.H : 1;
+    p.M = p.n_sets * a.B * p.n_q;
+    p.meta_bytes = ((size_t)(p.M * a.n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
+    p.int_bytes = ((size_t)p.M * sizeof(int32_t) + 255) & ~size_t(255);
+    const int64_t sched_ints = fm::schedule_scratch_ints(p.M, a.B * p.n_q, fm::kScheduleBucketShift, (int)p.n_kv);
+    p.sched_bytes = ((size_t)sched_ints * sizeof(int32_t) + 255) & ~size_t(255);
+    return p;
+}
+
+// Queues the preprocessor, the scheduler and the attention kernel on
+// a.stream, with ws (p.total() bytes, device memory) as their workspace.
+// Every byte of ws that a kernel reads was written earlier in the same
+// sequence, so ws needs no clearing.
+int fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, hipEvent_t ev_start, hipEvent_t ev_stop) {
     auto* meta = static_cast<fm::TileMeta*>(ws);
-    auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes);
-    auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + meta_bytes + int_bytes);
-
+    auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes);
+    auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + p.int_bytes);
+    auto* sched = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + 2 * p.int_bytes);
     const bool natural = g_schedule_mode == 1;
-    if (!natural && M <= fm::kPrepSmallMax) {
+    if (!natural && p.M <= fm::kPrepSmallMax) {
         // one launch: metadata and longest-first order together
-        FM_HIP(fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work, order,
-                                     stream, (int)n_sets));
+        FM_HIP(fm::launch_prep_small(a.col_start, a.col_end, a.n_ranges, a.B, a.N, fm::kBr, fm::kBc, meta, work,
+                                     order, a.stream, (int)p.n_sets));
     } else {
-        FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work, nullptr,
-                                     stream, (int)n_sets));
-        if (!natural) FM_HIP(fm::launch_schedule(work, M, order, stream, B * n_q, fm::kScheduleBucketShift));
+        FM_HIP(fm::launch_preprocess(a.col_start, a.col_end, a.n_ranges, a.B, a.N, fm::kBr, fm::kBc, meta, work,
+                                     nullptr, a.stream, (int)p.n_sets));
+        if (!natural)
+            FM_HIP(fm::launch_schedule(work, p.M, order, a.stream, a.B * p.n_q, fm::kScheduleBucketShift,
+                                       (int)p.n_kv, sched));
     }
+    FM_HIP(fm::launch_attention(a.q, a.k, a.v, a.col_start, a.col_end, a.n_ranges, meta, natural ? nullptr : order,
+                                a.B, a.H, a.N, a.d, a.scale, a.out, a.lse, a.stream, ev_start, ev_stop, a.fp8_scales,
+                                (int)p.n_sets, a.fp8_weights));
+    return FM_OK;
+}
 
+// The forward pass with the library's workspace for (device, stream).
+int attn_fwd_impl(const FwdArgs& a) {
+    const int st = fwd_check(a);
+    if (st != FM_OK) return st;
+    const FwdPlan p = fwd_plan(a);
+    void* ws = nullptr;
+    std::unique_lock<std::mutex> ws_hold;       // held until the launches below are queued
+    FM_HIP(get_workspace(a.stream, p.total(), &ws, ws_hold));
     std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
     {
         std::lock_guard<std::mutex> lock(g_timing.mu);
@@ -294,15 +347,23 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* co
             }
         }
     }
-    FM_HIP(fm::launch_attention(q, k, v, col_start, col_end, n_ranges, meta, natural ? nullptr : order, B, H,
-                                N, d, scale, out, lse, stream, ev.first, ev.second, fp8_scales, (int)n_sets,
-                                fp8_weights));
+    const int r = fwd_launch(a, p, ws, ev.first, ev.second);
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
-        g_timing.pending.push_back(ev);
+        if (r == FM_OK) g_timing.pending.push_back(ev);
+        else g_timing.pool.push_back(ev);
     }
-    return FM_OK;
+    return r;
 }
+
+FwdArgs fwd_args(const void* q, const void* k, const void* v, const int32_t* col_start, const int32_t* col_end,
+                 int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
+                 hipStream_t stream, const float* fp8_scales = nullptr, bool per_head = false,
+                 bool fp8_weights = false) {
+    return FwdArgs{q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, fp8_scales, per_head,
+                   fp8_weights};
+}
+
 
 }  // namespace
 
@@ -311,13 +372,14 @@ extern "C" {
 FM_API int fm_attn_fwd_multi(const void* q, const void* k, const void* v, const int32_t* col_start,
                              const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
                              int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
-    return attn_fwd_impl(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, nullptr);
+    return attn_fwd_impl(fwd_args(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream));
 }
 
 FM_API int fm_attn_fwd_per_head(const void* q, const void* k, const void* v, const int32_t* col_start,
                                 const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
                                 int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
-    return attn_fwd_impl(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, nullptr, true);
+    return attn_fwd_impl(
+        fwd_args(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, nullptr, true));
 }
 
 FM_API int fm_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_scale, float k_scale,
@@ -328,8 +390,8 @@ FM_API int fm_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float
     for (float x : scales)
         if (!(x > 0.f) || !isfinite(x)) return FM_ERR_INVALID_ARG;
     if (mode != FM_FP8_SCORES && mode != FM_FP8_ALL) return FM_ERR_INVALID_ARG;
-    return attn_fwd_impl(q8, k8, v8, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, scales,
-                         false, mode == FM_FP8_ALL);
+    return attn_fwd_impl(fwd_args(q8, k8, v8, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream,
+                                  scales, false, mode == FM_FP8_ALL));
 }
 
 FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_t* col_start,
@@ -383,7 +445,12 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     const size_t o_dd = o_splits + al((size_t)(1 + fm::kBwdExtraPieces) * sizeof(int4));
     const size_t o_part = o_dd + al((size_t)(B * H * N) * sizeof(float));
     const size_t part_floats = n_sets == 1 ? (size_t)fm::kBwdExtraPieces * H * fm::kBwdKeys * d * 2 : 0;
-    const size_t total = o_part + al(part_floats * sizeof(float));
+    const int64_t n_kv = (N + fm::kBc - 1) / fm::kBc;
+    // scheduler scratch, used by the two orders one after the other
+    const int64_t sched_ints = std::max(fm::schedule_scratch_ints(Mq, B * n_q, fm::kScheduleBucketShift, (int)n_kv),
+                                        fm::schedule_scratch_ints(Mp, Lp, 0, (int)n_qc));
+    const size_t o_sched = o_part + al(part_floats * sizeof(float));
+    const size_t total = o_sched + al((size_t)sched_ints * sizeof(int32_t));
     void* ws = nullptr;
     std::unique_lock<std::mutex> ws_hold;       // held until the last launch below is queued
     FM_HIP(get_workspace(stream, total, &ws, ws_hold));
@@ -401,6 +468,7 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     auto* splits = reinterpret_cast<int4*>(w + o_splits);
     auto* dd = reinterpret_cast<float*>(w + o_dd);
     auto* part = reinterpret_cast<float*>(w + o_part);
+    auto* sched = reinterpret_cast<int32_t*>(w + o_sched);
 
     FM_HIP(fm::launch_bwd_rowdot(out, dout, B * H * N, d, dd, stream));
     // dQ: the forward's query blocks, key blocks and longest-first order
@@ -410,7 +478,8 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     } else {
         FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, nullptr,
                                      stream, (int)n_sets));
-        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q, fm::kScheduleBucketShift));
+        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q, fm::kScheduleBucketShift, (int)n_kv,
+                                   sched));
     }
     // dK, dV: query chunks per key block, long key blocks split into pieces,
     // pieces longest first (within each set)
@@ -419,7 +488,7 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     FM_HIP(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream, (int)n_sets));
     const int min_chunks = g_bwd_min_chunks > 0 ? g_bwd_min_chunks : (1 << 30);
     FM_HIP(fm::launch_bwd_split(kvr, B * n_kb, (int)n_sets, min_chunks, pieces, pslot, pwork, splits, stream));
-    FM_HIP(fm::launch_schedule(pwork, Mp, order_k, stream, Lp));
+    FM_HIP(fm::launch_schedule(pwork, Mp, order_k, stream, Lp, 0, (int)n_qc, sched));
     FM_HIP(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, pieces, pslot, order_k,
                                B, H, N, d, scale, dk, dv, part, stream, (int)n_sets));
     FM_HIP(fm::launch_bwd_dq(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_q, order_q, B, H, N, d,

@@ -49,13 +49,22 @@ hipError_t launch_class_table(const TileMeta* meta, int n_iv, int64_t n_q, int64
                               hipStream_t stream);
 
 // Longest-first order (ties by index) within each segment of L consecutive
-// items (L = M: one segment): order[seg*L + rank] = item.  With shift > 0 the
-// items are ranked by work >> shift, so that items of nearly equal work keep
-// their index order (for the attention kernel: the query blocks of one
-// document stay together, and the workgroups resident on an XCD share fewer
-// documents' K/V).
-hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L = 0,
-                           int shift = 0);
+// items (L = 0: one segment of all M items; M must be a multiple of L):
+// order[seg*L + rank] = item.  With shift > 0 the items are ranked by
+// work >> shift, so that items of nearly equal work keep their index order
+// (for the attention kernel: the query blocks of one document stay together,
+// and the workgroups resident on an XCD share fewer documents' K/V).  Work
+// values lie in [-1, max_work] (-1 ranks last).  A segment of at most
+// kSortSmall items is sorted by one workgroup in LDS; a longer one takes a
+// counting sort whose int32 scratch (schedule_scratch_ints; 0 when no segment
+// is longer than kSortSmall) the caller provides.
+constexpr int kSortSmall = 16384;       // items per segment sorted by one workgroup
+constexpr int kSortSmallBits = 14;      // index bits of its sort keys (2^14 = kSortSmall)
+constexpr int kSortChunk = 8192;        // items per chunk of the counting sort
+constexpr int kSortChunkBits = 13;
+int64_t schedule_scratch_ints(int64_t M, int64_t L, int shift, int max_work);
+hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L,
+                           int shift, int max_work, int32_t* scratch);
 
 // Work bucket of the attention kernel's order on the large-problem path:
 // 32 key blocks.  The one-workgroup path (at most kPrepSmallMax query blocks,

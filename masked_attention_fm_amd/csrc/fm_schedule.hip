@@ -7,14 +7,26 @@
 // query block at the end of a long document needs many key blocks, one at
 // the start of a short document needs one), so the blocks are issued
 // longest first: the long ones start early and the short ones fill the
-// tail.  The order is a stable sort by decreasing work; each item's rank is
-// counted directly (items ranked ahead of x: larger work, or equal work and
-// smaller index), which is deterministic and needs no atomics.  On large
-// problems the attention order sorts by work in buckets of 32 key blocks, so
-// that the query blocks of one document that need about the same work run
-// together and share their K/V in the XCD's L2.  The order
-// never changes a result: every query block's output depends only on its
-// own fixed sequence of key blocks.
+// tail.  The order is a stable sort by decreasing work: items of equal work
+// keep their index order.  On large problems the attention order sorts by
+// work in buckets of 32 key blocks, so that the query blocks of one document
+// that need about the same work run together and share their K/V in the
+// XCD's L2.  The order never changes a result: every query block's output
+// depends only on its own fixed sequence of key blocks.
+//
+// The sort is deterministic and has no floating point:
+//   * a segment of at most kSortSmall items is sorted by one workgroup: each
+//     item becomes the 32-bit key ((kmax - work') << bits) | index, unique
+//     and ordered exactly as the result must be (work' = bucketed work + 1,
+//     so that the -1 of unused backward entries sorts last), and a bitonic
+//     network sorts the keys in LDS;
+//   * a longer segment is a counting sort over work' (at most max_work + 2
+//     values): chunks of kSortChunk items are sorted in LDS as above, which
+//     gives each item its rank among the equal-work items of its chunk and
+//     each chunk's count per work value; a second launch turns the counts
+//     into each chunk's first position per work value (work values in
+//     decreasing order, chunks in index order); a third places every item.
+//     Work and memory are linear in the items plus chunks x work values.
 
 #include <climits>
 
@@ -23,36 +35,155 @@
 namespace fm {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kSortThreads = 1024;
 
-// Items are ranked within their segment of L; a workgroup walks the union of
-// its threads' segments (uniform bounds for the barriers) and each thread
-// counts only its own segment.
-__global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __restrict__ work, int M, int L,
-                                                            int shift, int32_t* __restrict__ order) {
-    __shared__ int s_work[kThreads];
-    const int x = blockIdx.x * kThreads + threadIdx.x;
-    const int wx = x < M ? (work[x] >> shift) : INT_MIN;
-    const int x_first = blockIdx.x * kThreads;
-    const int x_last = min(M, x_first + kThreads) - 1;
-    const int y_begin = (x_first / L) * L;
-    const int y_end = min(M, (x_last / L + 1) * L);
-    const int my_lo = (x / L) * L;
-    const int my_hi = my_lo + L;
-    int rank = 0;
-    for (int base = y_begin; base < y_end; base += kThreads) {
-        const int y = base + threadIdx.x;
-        s_work[threadIdx.x] = y < y_end ? (work[y] >> shift) : INT_MIN;
-        __syncthreads();
-        const int lim = min(kThreads, y_end - base);
-        for (int i = 0; i < lim; ++i) {
-            const int wy = s_work[i];
-            const int yy = base + i;
-            rank += (yy >= my_lo) & (yy < my_hi) & ((wy > wx) | ((wy == wx) & (yy < x)));
+// Work value of an item: its bucketed work shifted up by one (so -1 becomes
+// 0), clamped to [0, kw_max].  Every pass clamps alike, so the positions the
+// counting sort hands out always form a permutation of the segment.
+__device__ __forceinline__ int work_value(int w, int shift, int kw_max) {
+    const int kw = (w >> shift) + 1;
+    return kw < 0 ? 0 : (kw > kw_max ? kw_max : kw);
+}
+
+// Sort key of an item: the work value, decreasing, then the index inside the
+// sorted run, increasing (kw_max <= kmax = 2^(32 - bits) - 1).
+__device__ __forceinline__ uint32_t sort_key(int kw, int idx, int bits) {
+    const uint32_t kmax = (1u << (32 - bits)) - 1u;
+    return ((kmax - (uint32_t)kw) << bits) | (uint32_t)idx;
+}
+
+// Ascending bitonic sort of s[0, n), n a power of two, by the whole workgroup.
+__device__ __forceinline__ void bitonic_sort_lds(uint32_t* s, int n) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < (n >> 1); i += kSortThreads) {
+                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+                const int hi = lo | j;
+                const uint32_t a = s[lo];
+                const uint32_t b = s[hi];
+                const bool up = (lo & k) == 0;
+                if ((a > b) == up) {
+                    s[lo] = b;
+                    s[hi] = a;
+                }
+            }
+            __syncthreads();
         }
+    }
+}
+
+// One segment of L <= kSortSmall items per workgroup: load, sort, write the
+// order.  Entries past L hold 0xFFFFFFFF, which no item's key reaches (an
+// item key with every bit set would need index 2^bits - 1 >= L).
+__global__ __launch_bounds__(kSortThreads) void order_small_kernel(const int32_t* __restrict__ work, int L,
+                                                                   int n, int shift, int32_t* __restrict__ order) {
+    __shared__ uint32_t s[kSortSmall];
+    const int64_t lo = (int64_t)blockIdx.x * L;
+    for (int i = threadIdx.x; i < n; i += kSortThreads)
+        s[i] = i < L ? sort_key(work_value(work[lo + i], shift, (1 << (32 - kSortSmallBits)) - 1), i, kSortSmallBits)
+                     : 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort_lds(s, n);
+    const uint32_t mask = (1u << kSortSmallBits) - 1u;
+    for (int p = threadIdx.x; p < L; p += kSortThreads) order[lo + p] = (int32_t)(lo + (s[p] & mask));
+}
+
+// Counting sort, pass 1: chunk t (chunk c of segment g) sorts its keys in LDS;
+// item at sorted position p gets its rank among the equal-work items of the
+// chunk (p minus the first position of its work value), and the last item of
+// each run stores the run's length as the chunk's count for that work value.
+// cnt[t][*] is cleared first by the same workgroup.
+__global__ __launch_bounds__(kSortThreads) void order_count_kernel(const int32_t* __restrict__ work, int L,
+                                                                   int n_chunks, int shift, int n_keys,
+                                                                   int32_t* __restrict__ cnt,
+                                                                   int32_t* __restrict__ lrank) {
+    __shared__ uint32_t s[kSortChunk];
+    const int t = blockIdx.x;
+    const int g = t / n_chunks;
+    const int c = t - g * n_chunks;
+    const int64_t base = (int64_t)g * L + (int64_t)c * kSortChunk;
+    const int n_c = min(kSortChunk, L - c * kSortChunk);
+    int32_t* row = cnt + (int64_t)t * n_keys;
+    for (int k = threadIdx.x; k < n_keys; k += kSortThreads) row[k] = 0;
+    for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads)
+        s[i] = i < n_c ? sort_key(work_value(work[base + i], shift, n_keys - 1), i, kSortChunkBits) : 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort_lds(s, kSortChunk);
+    const uint32_t kmax = (1u << (32 - kSortChunkBits)) - 1u;
+    const uint32_t mask = (1u << kSortChunkBits) - 1u;
+    for (int p = threadIdx.x; p < n_c; p += kSortThreads) {
+        const uint32_t hi = s[p] >> kSortChunkBits;
+        int a = 0, b = p;                                  // first position whose key part is hi
+        while (a < b) {
+            const int m = (a + b) >> 1;
+            if ((s[m] >> kSortChunkBits) < hi) a = m + 1; else b = m;
+        }
+        lrank[base + (s[p] & mask)] = p - a;
+        const bool last = p + 1 == n_c || (s[p + 1] >> kSortChunkBits) != hi;
+        const int kw = (int)(kmax - hi);                   // work value of the run (< n_keys)
+        if (last) row[kw] = p - a + 1;
+    }
+}
+
+// Counting sort, pass 2 (one workgroup per segment): for every work value w'
+// (thread i takes the values at descending positions [i per, (i+1) per)),
+// cnt[(g, c)][w'] becomes the number of items of value w' in the segment's
+// earlier chunks, and start[g][w'] the number of items of larger value.
+__global__ __launch_bounds__(kSortThreads) void order_offsets_kernel(int n_chunks, int n_keys,
+                                                                     int32_t* __restrict__ cnt,
+                                                                     int32_t* __restrict__ start) {
+    __shared__ int s_sum[kSortThreads];
+    const int g = blockIdx.x;
+    const int per = (n_keys + kSortThreads - 1) / kSortThreads;
+    const int q0 = threadIdx.x * per;
+    const int q1 = min(n_keys, q0 + per);
+    int32_t* st = start + (int64_t)g * n_keys;
+    int mine = 0;
+    for (int q = q0; q < q1; ++q) {
+        const int kw = n_keys - 1 - q;
+        int run = 0;
+        for (int c = 0; c < n_chunks; ++c) {
+            int32_t* e = cnt + ((int64_t)g * n_chunks + c) * n_keys + kw;
+            const int v = *e;
+            *e = run;
+            run += v;
+        }
+        st[kw] = run;                                      // the value's total, for now
+        mine += run;
+    }
+    s_sum[threadIdx.x] = mine;
+    __syncthreads();
+    // exclusive scan of the per-thread sums (Hillis-Steele, in place)
+    for (int off = 1; off < kSortThreads; off <<= 1) {
+        const int v = threadIdx.x >= off ? s_sum[threadIdx.x - off] : 0;
+        __syncthreads();
+        s_sum[threadIdx.x] += v;
         __syncthreads();
     }
-    if (x < M) order[my_lo + rank] = x;
+    int acc = s_sum[threadIdx.x] - mine;
+    for (int q = q0; q < q1; ++q) {
+        const int kw = n_keys - 1 - q;
+        const int tot = st[kw];
+        st[kw] = acc;
+        acc += tot;
+    }
+}
+
+// Counting sort, pass 3: every item's place.
+__global__ __launch_bounds__(256) void order_place_kernel(const int32_t* __restrict__ work, int64_t M, int L,
+                                                          int n_chunks, int shift, int n_keys,
+                                                          const int32_t* __restrict__ cnt,
+                                                          const int32_t* __restrict__ start,
+                                                          const int32_t* __restrict__ lrank,
+                                                          int32_t* __restrict__ order) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= M) return;
+    const int64_t g = x / L;
+    const int in_seg = (int)(x - g * L);
+    const int c = in_seg / kSortChunk;
+    const int kw = work_value(work[x], shift, n_keys - 1);
+    const int pos = start[g * n_keys + kw] + cnt[(g * n_chunks + c) * n_keys + kw] + lrank[x];
+    order[g * L + pos] = (int32_t)x;
 }
 
 constexpr int kPrepThreads = 1024;
@@ -167,12 +298,44 @@ hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, i
     });
 }
 
-hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L,
-                           int shift) {
+int64_t schedule_scratch_ints(int64_t M, int64_t L, int shift, int max_work) {
     if (L <= 0) L = M;
-    const int64_t blocks = (M + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, work,
-                       (int)M, (int)L, shift, order);
+    if (L <= kSortSmall) return 0;
+    const int64_t S = M / L;
+    const int64_t chunks = (L + kSortChunk - 1) / kSortChunk;
+    const int64_t n_keys = (int64_t)(max_work >> shift) + 2;
+    return S * chunks * n_keys + S * n_keys + M;
+}
+
+hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L,
+                           int shift, int max_work, int32_t* scratch) {
+    if (L <= 0) L = M;
+    if (M <= 0 || M % L != 0 || max_work < 0) return hipErrorInvalidValue;
+    const int64_t S = M / L;
+    if (L <= kSortSmall) {
+        int n = 1;
+        while (n < L) n <<= 1;
+        hipLaunchKernelGGL(order_small_kernel, dim3((unsigned)S), dim3(kSortThreads), 0, stream, work, (int)L, n,
+                           shift, order);
+        return hipGetLastError();
+    }
+    // counting sort: keys are work' = (work >> shift) + 1 in [0, n_keys)
+    const int64_t n_keys = (int64_t)(max_work >> shift) + 2;
+    if (scratch == nullptr || n_keys > (int64_t(1) << (32 - kSortChunkBits))) return hipErrorInvalidValue;
+    const int64_t chunks = (L + kSortChunk - 1) / kSortChunk;
+    int32_t* cnt = scratch;
+    int32_t* start = cnt + S * chunks * n_keys;
+    int32_t* lrank = start + S * n_keys;
+    hipLaunchKernelGGL(order_count_kernel, dim3((unsigned)(S * chunks)), dim3(kSortThreads), 0, stream, work,
+                       (int)L, (int)chunks, shift, (int)n_keys, cnt, lrank);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(order_offsets_kernel, dim3((unsigned)S), dim3(kSortThreads), 0, stream, (int)chunks,
+                       (int)n_keys, cnt, start);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(order_place_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, work, M, (int)L,
+                       (int)chunks, shift, (int)n_keys, cnt, start, lrank, order);
     return hipGetLastError();
 }
 

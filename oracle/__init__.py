@@ -31,8 +31,8 @@ routines); none is "parity unpinned".
 from .attention import attention, attention_weights, dense_mask, bf16_round
 from .backward import attention_bwd
 from .tiles import (SKIP, FULL, PARTIAL, classes_minmax, classes_minmax_multi, classes_dense,
-                    unmasked_count)
+                    nonskip_counts, unmasked_count)
 
 __all__ = ["attention", "attention_weights", "attention_bwd", "dense_mask", "bf16_round",
            "SKIP", "FULL", "PARTIAL", "classes_minmax", "classes_minmax_multi", "classes_dense",
-           "unmasked_count"]
+           "nonskip_counts", "unmasked_count"]

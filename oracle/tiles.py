@@ -57,6 +57,29 @@ def classes_minmax(col_start, col_end, N: int, Br: int, Bc: int) -> np.ndarray:
     return out
 
 
+def nonskip_counts(col_start, col_end, N: int, Br: int, Bc: int, blocks_per_pass: int = 64) -> np.ndarray:
+    """Non-SKIP key blocks of every query block of one sequence (the row sums of the
+    min/max rule's table, without building the table): for query block t, the number
+    of key blocks j that are not SKIP, i.e. not (khi < min col_start or klo > max
+    col_end) over the block's rows.  Valid intervals (0 <= s <= e <= N-1).  The rule
+    is evaluated for every key block, a pass of `blocks_per_pass` query blocks at a
+    time, so that long sequences (millions of rows) fit in memory."""
+    s = np.asarray(col_start, dtype=np.int64)
+    e = np.asarray(col_end, dtype=np.int64)
+    n_q = -(-N // Br)
+    n_kv = -(-N // Bc)
+    klo = np.arange(n_kv, dtype=np.int64) * Bc
+    khi = np.minimum(klo + Bc, N) - 1
+    out = np.empty(n_q, dtype=np.int64)
+    for t0 in range(0, n_q, blocks_per_pass):
+        t1 = min(t0 + blocks_per_pass, n_q)
+        min_s = np.array([s[t * Br:min(t * Br + Br, N)].min() for t in range(t0, t1)])
+        max_e = np.array([e[t * Br:min(t * Br + Br, N)].max() for t in range(t0, t1)])
+        skip = (khi[None, :] < min_s[:, None]) | (klo[None, :] > max_e[:, None])
+        out[t0:t1] = (~skip).sum(axis=1)
+    return out
+
+
 def classes_dense(col_start, col_end, N: int, Br: int, Bc: int) -> np.ndarray:
     """Dense-exact rule: classify each tile by counting its attended entries."""
     n_q = -(-N // Br)

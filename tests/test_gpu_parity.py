@@ -163,6 +163,26 @@ def test_schedule_large_path_is_stable_longest_first():
     assert np.array_equal(order, np.argsort(-schedule_key(ref_work), kind="stable"))
 
 
+def test_schedule_counting_sort_over_1e5_query_blocks():
+    """131072 query blocks in one segment (B = 64, N = 2^18, documents of log-normal
+    length): the scheduler's counting-sort path.  The work counts equal the oracle's
+    non-skip counts (the min/max rule evaluated per key block) and the order is the
+    stable longest-first order of the bucketed work, bit for bit."""
+    B, N, d = 64, 1 << 18, 128
+    Br, Bc = fm.fm_attn_tile_shape(d)
+    spec = inputs.make_intervals("doc_lognormal", B, N, 31, median=4096, sigma=1.0, lo=16, hi=65536)
+    assert B * (N // Br) >= 10 ** 5
+    sd, ed = to_dev(spec.col_start, spec.col_end)
+    work, order = fm.fm_tile_schedule(sd, ed, d)
+    work, order = work.cpu().numpy(), order.cpu().numpy()
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(16, B)) as ex:
+        ref_work = np.concatenate(list(ex.map(
+            lambda b: oracle.nonskip_counts(spec.col_start[b], spec.col_end[b], N, Br, Bc), range(B))))
+    assert np.array_equal(work, ref_work)
+    assert np.array_equal(order, np.argsort(-schedule_key(ref_work), kind="stable"))
+
+
 # ---------------------------------------------------------------- attention, small cases
 
 

@@ -123,3 +123,22 @@ def test_per_head_backward_equal_sets_match_shared():
     torch.cuda.synchronize()
     for a, b_ in zip(g1, g2):
         assert torch.equal(a, b_)
+
+
+def test_per_head_segments_longer_than_one_sort_workgroup():
+    """Two interval sets (one per head) of 20480 query blocks each (B = 5, N = 2^19): each
+    segment of the launch order is longer than one workgroup sorts, so the order comes
+    from the counting sort, segment by segment.  Sampled rows of both heads against the
+    oracle (the order changes no result)."""
+    B, H, N, d = 5, 2, 1 << 19, 64
+    s = np.empty((B, H, 1, N), np.int32)
+    e = np.empty((B, H, 1, N), np.int32)
+    s[:, 0, 0], e[:, 0, 0] = inputs.sliding_window_intervals(N, 64)
+    spec = inputs.make_intervals("doc_lognormal", B, N, 41, median=128, sigma=1.0, lo=1, hi=2048)
+    s[:, 1, 0], e[:, 1, 0] = spec.col_start, spec.col_end
+    assert B * (N // 128) > 16384
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=41)
+    rng = np.random.default_rng(41)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 1], rng.integers(0, N, 60)]))
+    log("per-head, two long segments")
+    check_per_head(q, k, v, s, e, inputs.default_scale(d), "per-head long segments", rows=rows)

@@ -119,3 +119,22 @@ def test_backward_mutant_is_caught(name):
     old, new = BWD_MUTANTS[name]
     mod = _mutant("backward.py", old, new)
     assert _caught(test_oracle_bwd.ALL_BWD_PINS, mod.attention_bwd), f"mutant {name} survived every pin"
+
+
+NONSKIP_MUTANTS = {
+    "skip_left_inclusive": ("(khi[None, :] < min_s[:, None])", "(khi[None, :] <= min_s[:, None])"),
+    "skip_right_inclusive": ("(klo[None, :] > max_e[:, None])", "(klo[None, :] >= max_e[:, None])"),
+    "no_right_skip": ("skip = (khi[None, :] < min_s[:, None]) | (klo[None, :] > max_e[:, None])",
+                      "skip = (khi[None, :] < min_s[:, None])"),
+    "khi_exclusive": ("khi = np.minimum(klo + Bc, N) - 1", "khi = np.minimum(klo + Bc, N)"),
+    "largest_start": ("s[t * Br:min(t * Br + Br, N)].min()", "s[t * Br:min(t * Br + Br, N)].max()"),
+    "rows_not_clipped": ("e[t * Br:min(t * Br + Br, N)].max()", "e[t * Br:min(t * Br + Br - 1, N)].max()"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NONSKIP_MUTANTS))
+def test_nonskip_mutant_is_caught(name):
+    import oracle
+    old, new = NONSKIP_MUTANTS[name]
+    mod = _mutant("tiles.py", old, new, {"dense_mask": oracle.dense_mask})
+    assert _caught(test_oracle_tiles.NONSKIP_PINS, mod.nonskip_counts), f"mutant {name} survived every pin"

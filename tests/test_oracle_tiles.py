@@ -156,6 +156,45 @@ def test_rules_agree_on_lognormal_docs():
     assert np.array_equal(a, d)
 
 
+# ---------------------------------------------------------------- non-skip counts per query block
+
+
+def pin_nonskip_row_sums(fn):
+    """Pinned to the scalar-loop class table (a separate evaluation of the same rule)."""
+    for N, Br, Bc in ((1, 1, 1), (7, 3, 2), (300, 128, 64), (1000, 33, 17), (4097, 128, 64)):
+        rng = np.random.default_rng(N + Br)
+        for width in (None, 3, 200):
+            s, e = inputs.random_intervals(rng, 1, N, max_width=width)
+            table = oracle.classes_minmax(s[0], e[0], N, Br, Bc)
+            for bpp in (1, 5, 64):
+                got = fn(s[0], e[0], N, Br, Bc, blocks_per_pass=bpp)
+                assert np.array_equal(got, (table != SKIP).sum(axis=1))
+
+
+def pin_nonskip_causal(fn):
+    """Causal, Br = 2 Bc: query block t reaches key block 2t + 1, so 2t + 2 blocks are kept."""
+    N, Br, Bc = 1 << 15, 128, 64
+    s, e = inputs.causal_intervals(N)
+    assert np.array_equal(fn(s, e, N, Br, Bc), 2 * np.arange(N // Br) + 2)
+
+
+def pin_nonskip_window(fn):
+    """Sliding window w = 1024, Br = 128, Bc = 64: from query block 8 on, every block keeps
+    its 16 window blocks plus the partly covered block on each side: 18."""
+    N, Br, Bc = 1 << 14, 128, 64
+    s, e = inputs.sliding_window_intervals(N, 1024)
+    got = fn(s, e, N, Br, Bc)
+    assert np.all(got[8:] == 18) and np.array_equal(got[:8], 2 * np.arange(8) + 2)
+
+
+NONSKIP_PINS = [pin_nonskip_row_sums, pin_nonskip_causal, pin_nonskip_window]
+
+
+@pytest.mark.parametrize("pin", NONSKIP_PINS, ids=lambda f: f.__name__)
+def test_nonskip_pin(pin):
+    pin(oracle.nonskip_counts)
+
+
 # ---------------------------------------------------------------- unmasked entries
 
 
