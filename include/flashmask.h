@@ -42,7 +42,8 @@ typedef enum fm_status {
     FM_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer, bad scale   */
     FM_ERR_UNSUPPORTED = 2,   /* head dimension other than 64 or 128                      */
     FM_ERR_BAD_INTERVAL = 3,  /* fm_classify_tiles: some row violates 0 <= s <= e <= N-1  */
-    FM_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed               */
+    FM_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed               */
+    FM_ERR_TOO_LARGE = 5      /* fm_attn_fwd_noalloc: the problem exceeds its scratch     */
 } fm_status;
 
 /* Tile classes, in the order the FlashMask article §2.2 lists the cases. */
@@ -99,6 +100,32 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v,
                        const int32_t* col_start, const int32_t* col_end,
                        int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                        void* out, float* lse, hipStream_t stream);
+
+/*
+ * fm_attn_fwd_noalloc -- fm_attn_fwd_multi (bf16, [B][n_ranges][N] intervals
+ * shared by all heads) that allocates nothing: for callers that cannot call
+ * hipMalloc, such as code under HIP graph capture, tight serving loops, or
+ * harnesses that forbid allocation.  The caller still provides the inputs and
+ * outputs.  Its workspace (per query block: 16 B of tile metadata per range,
+ * a work count and a place in the order, plus the order's sort scratch on
+ * very long problems) lives in a static device array of
+ * FM_NOALLOC_SCRATCH_BYTES (4 MiB) that each GPU holds until the process ends;
+ * one range per row fits up to about 170,000 query blocks of 128 rows
+ * (B * ceil(N/128)), four ranges about 58,000.
+ *   Arguments, results (bit-identical to fm_attn_fwd_multi's), asynchrony and
+ * errors as fm_attn_fwd_multi; FM_ERR_TOO_LARGE (nothing queued) when the
+ * problem needs more scratch than that.  No kernel timing is recorded.
+ *   Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents (nothing in it needs clearing: each call writes what it
+ * reads).  Calls in order on one stream are safe; calls that can overlap on
+ * one GPU (other streams, other host threads) race on the array and give
+ * undefined results.
+ */
+#define FM_NOALLOC_SCRATCH_BYTES (4u << 20)
+FM_API int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                               const int32_t* col_start, const int32_t* col_end, int32_t n_ranges,
+                               int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                               void* out, float* lse, hipStream_t stream);
 
 /*
  * Rows with several key ranges.  The FlashMask article lists, as an

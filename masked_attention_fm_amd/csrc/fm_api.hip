@@ -116,6 +116,7 @@ FM_API const char* fm_status_string(int status) {
         case FM_ERR_UNSUPPORTED: return "unsupported head dimension";
         case FM_ERR_BAD_INTERVAL: return "interval outside 0 <= col_start <= col_end <= N-1";
         case FM_ERR_HIP: return "HIP runtime error";
+        case FM_ERR_TOO_LARGE: return "problem needs more than the no-allocation scratch holds";
         default: return "unknown status";
     }
 }
@@ -364,6 +365,39 @@ FwdArgs fwd_args(const void* q, const void* k, const void* v, const int32_t* col
                    fp8_weights};
 }
 
+}  // namespace
+
+// ---- the no-allocation forward: a static device scratch array.
+//
+// In host code `scratch` is only a host-side stand-in: its device address
+// comes from hipGetSymbolAddress, taken once per device (with that device
+// current) and kept; only that address is ever handed to a kernel.  Each
+// device holds its own copy of the array until the process ends.
+static __device__ __align__(256) unsigned char scratch[FM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;   // device -> address of its copy of scratch
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_addr.find(dev);
+    if (it != g_scratch_addr.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = ptr;
+    *out = ptr;
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -398,6 +432,19 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
                        const int32_t* col_end, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                        void* out, float* lse, hipStream_t stream) {
     return fm_attn_fwd_multi(q, k, v, col_start, col_end, 1, B, H, N, d, scale, out, lse, stream);
+}
+
+FM_API int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* col_start,
+                               const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
+                               int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
+    const FwdArgs a = fwd_args(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream);
+    const int st = fwd_check(a);
+    if (st != FM_OK) return st;
+    const FwdPlan p = fwd_plan(a);
+    if (p.total() > (size_t)FM_NOALLOC_SCRATCH_BYTES) return FM_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    FM_HIP(scratch_address(&ws));
+    return fwd_launch(a, p, ws, nullptr, nullptr);
 }
 
 }  // extern "C"

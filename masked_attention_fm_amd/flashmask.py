@@ -15,7 +15,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libflashmask.so")
 
-FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_BAD_INTERVAL, FM_ERR_HIP = range(5)
+FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_BAD_INTERVAL, FM_ERR_HIP, FM_ERR_TOO_LARGE = range(6)
+FM_NOALLOC_SCRATCH_BYTES = 4 << 20
 FM_TILE_SKIP, FM_TILE_FULL, FM_TILE_PARTIAL = 0, 1, 2
 FM_OPT_SCHEDULE = 1
 FM_OPT_BWD_SPLIT_CHUNKS = 2
@@ -35,6 +36,8 @@ SIGNATURES = {
     "fm_tile_schedule": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P]),
     "fm_attn_fwd_multi": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
                                          _P, _P, _P]),
+    "fm_attn_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                           _P, _P, _P]),
     "fm_classify_tiles_multi": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P]),
     "fm_attn_fwd_per_head": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
                                             _P, _P, _P]),
@@ -257,6 +260,31 @@ def fm_attn_fwd_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_sta
     _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
     return _attn("fm_attn_fwd_multi", q, k, v, col_start, col_end, col_start.shape[1], scale, out, lse,
                  stream)
+
+
+def fm_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: torch.Tensor,
+                        col_end: torch.Tensor, scale: float, out: torch.Tensor, lse: torch.Tensor,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fm_attn_fwd_multi into the caller's out and lse with the library's static scratch: the
+    library allocates nothing.  Intervals [B, N] or [B, K, N].  Raises FlashMaskError with
+    FM_ERR_TOO_LARGE when the problem needs more than FM_NOALLOC_SCRATCH_BYTES.  Calls that
+    can overlap on one GPU share that scratch and race.  Asynchronous."""
+    B, H, N, d = _qkv(q, k, v)
+    if col_start.dim() == 2:
+        col_start, col_end = col_start.unsqueeze(1), col_end.unsqueeze(1)
+    if col_start.dim() != 3:
+        raise ValueError("col_start / col_end must be [B, N] or [B, K, N]")
+    _intervals(col_start, col_end, (B, col_start.shape[1], N), "[B, K, N]")
+    _require_scale(scale)
+    _dev_tensor(out, "out", torch.bfloat16)
+    _dev_tensor(lse, "lse", torch.float32)
+    if out.shape != q.shape or tuple(lse.shape) != (B, H, N):
+        raise ValueError("out must match q's shape and lse must be [B, H, N]")
+    status = lib().fm_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), col_start.data_ptr(),
+                                       col_end.data_ptr(), col_start.shape[1], B, H, N, d, float(scale),
+                                       out.data_ptr(), lse.data_ptr(), _stream_handle(stream))
+    _check("fm_attn_fwd_noalloc", status)
+    return out, lse
 
 
 def fm_attn_fwd_per_head(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, col_start: torch.Tensor,

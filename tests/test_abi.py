@@ -267,3 +267,39 @@ def test_attn_bwd_per_head_rejects_bad_arguments(L):
     assert L.fm_attn_bwd_per_head(None, *head[1:], 1, *tail) == fmb.FM_ERR_INVALID_ARG
     bad_d = [1, 2, 128, 80, 0.125, FAKE, FAKE, FAKE, None]
     assert L.fm_attn_bwd_per_head(*head, 1, *bad_d) == fmb.FM_ERR_UNSUPPORTED
+
+
+def noalloc(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cs=FAKE, ce=FAKE, K=1, B=1, H=1, N=128, d=128, scale=0.125,
+             out=FAKE, lse=FAKE)
+    a.update(kw)
+    return L.fm_attn_fwd_noalloc(a["q"], a["k"], a["v"], a["cs"], a["ce"], a["K"], a["B"], a["H"], a["N"],
+                                 a["d"], a["scale"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fmb.FM_ERR_INVALID_ARG),
+    (dict(K=0), fmb.FM_ERR_INVALID_ARG),
+    (dict(K=5), fmb.FM_ERR_INVALID_ARG),
+    (dict(d=96), fmb.FM_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fmb.FM_ERR_INVALID_ARG),
+    (dict(out=FAKE + 8), fmb.FM_ERR_INVALID_ARG),
+    # 64 x 2^22 rows: 2^21 query blocks, far beyond the 4 MiB scratch
+    (dict(B=64, N=1 << 22), fmb.FM_ERR_TOO_LARGE),
+    # 180,224 query blocks of one range (about 4.3 MB of records): just too large
+    (dict(B=44, N=1 << 19), fmb.FM_ERR_TOO_LARGE),
+    # four ranges per row: 65,536 query blocks need 6.3 MB
+    (dict(B=2, N=1 << 22, K=4), fmb.FM_ERR_TOO_LARGE),
+])
+def test_noalloc_rejects_on_the_host(L, kw, status):
+    """Every rejection happens before any HIP call (the pointers are never touched)."""
+    assert noalloc(L, **kw) == status
+
+
+def test_noalloc_limit_matches_the_workspace_plan():
+    """The largest single-range problems that fit: 4 MiB holds 16 B of records plus two
+    4-byte entries per query block (each part rounded to 256 B), plus the sort scratch
+    above 16,384 query blocks in one segment."""
+    per_block = 16 + 4 + 4
+    assert (4 << 20) // per_block > 170_000
+    assert fmb.FM_NOALLOC_SCRATCH_BYTES == 4 << 20
