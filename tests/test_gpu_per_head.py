@@ -142,3 +142,18 @@ def test_per_head_segments_longer_than_one_sort_workgroup():
     rows = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 1], rng.integers(0, N, 60)]))
     log("per-head, two long segments")
     check_per_head(q, k, v, s, e, inputs.default_scale(d), "per-head long segments", rows=rows)
+
+
+def test_per_head_masks_from_specifications():
+    """Heads with different mask kinds built by masks.head_intervals (padded to the sinks
+    head's two ranges): causal, a window, sinks + window, packed documents, prefix-LM and
+    full attention, each head against the oracle with its own intervals."""
+    from masked_attention_fm_amd import masks as mk
+    B, N, d = 2, 1500, 128
+    specs = [mk.Causal(), mk.SlidingWindow(200), mk.SinksWindow(300, 4), mk.Documents([[700, 800], [1, 1499]]),
+             mk.PrefixLM([400, 1100]), mk.Full()]
+    s, e = mk.head_intervals(specs, B, N)
+    assert s.shape == (B, len(specs), 2, N)
+    q, k, v = inputs.make_qkv(B, len(specs), N, d, seed=61)
+    log("per-head masks from specifications")
+    check_per_head(q, k, v, s, e, inputs.default_scale(d), "per-head specs")
