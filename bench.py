@@ -170,6 +170,8 @@ def time_config(cfg, steps, warmup, warm_s=0.0):
         "attended_pairs": U,
         "effective_flops": flops,
         "algorithmic_bytes": metrics.algorithmic_bytes(cfg.B, cfg.H, cfg.N, cfg.d, n_ranges),
+        # matrix instructions the kernel issues (every wavefront's computed key blocks)
+        "mfma_instructions": metrics.wave_mfma_instructions(spec.col_start, spec.col_end, cfg.N, cfg.H, cfg.d),
         "ms_per_step": ms_step,
         "ms_median": ms_median,
         "effective_tflops": flops / (ms_step * 1e-3) / 1e12,
@@ -298,7 +300,11 @@ def roofline_of(res):
         "traffic_over_algorithmic": traffic / alg if traffic else None,
         "hbm_peak_GBps": metrics.MI355X_HBM_TBPS * 1e3,
         "mfma_busy": rec.get("mfma_busy_per_cu_busy") if rec else None,
-        "mfma_flops_counted_per_launch": rec.get("mfma_flops_per_launch") if rec else None,
+        "executed_flops_per_launch": res["mfma_instructions"] * 32768,
+        "executed_TFLOPs": res["mfma_instructions"] * 32768 / (kms * 1e-3) / 1e12 if kms else None,
+        "mfma_instructions_per_launch": res["mfma_instructions"],
+        "mfma_instructions_counted_per_launch": rec["attention"].get("SQ_INSTS_MFMA") if rec else None,
+        "mfma_valu_coexec_per_mfma_busy": rec.get("mfma_valu_coexec_per_mfma_busy") if rec else None,
         "lds_bank_conflict_cycles": rec.get("lds_bank_conflict_cycles") if rec else None,
         "lds_bank_conflict_per_lds_active": rec.get("lds_bank_conflict_per_lds_active") if rec else None,
         "counter_record": rec.get("file") if rec else None,

@@ -28,7 +28,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # holds, so it changes the traffic).
 ATTN_SOURCES = [os.path.join(PKG, "csrc", name) for name in
                 ("fm_attn_fwd.hip", "fm_internal.h", "fm_mfma.h", "fm_schedule.hip", "fm_intervals.hip",
-                 "fm_api.hip")]
+                 "fm_forward.hip")]
 
 # One bf16 MFMA v_mfma_f32_32x32x16_bf16: 2 * 32 * 32 * 16 FLOPs.
 MFMA_FLOPS = 2 * 32 * 32 * 16

@@ -211,7 +211,7 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
     if (B * n_q >= (int64_t(1) << 31)) return FM_ERR_INVALID_ARG;
     const int64_t n_kv = (N + fm::kBc - 1) / fm::kBc;
     const size_t meta_bytes = ((size_t)(B * n_q * n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
-    const int64_t sched_ints = fm::schedule_scratch_ints(B * n_q, B * n_q, fm::kScheduleBucketShift, (int)n_kv);
+    const int64_t sched_ints = fm::schedule_scratch_ints(B * n_q, B * n_q, fm::schedule_shift(B * n_q), (int)n_kv);
     void* buf = nullptr;
     FM_HIP(hipMalloc(&buf, meta_bytes + (size_t)sched_ints * sizeof(int32_t)));
     auto* meta = static_cast<fm::TileMeta*>(buf);
@@ -225,7 +225,7 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
         e = fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta, work_out,
                                   nullptr, 0);
         if (e == hipSuccess)
-            e = fm::launch_schedule(work_out, B * n_q, order_out, 0, 0, fm::kScheduleBucketShift, (int)n_kv,
+            e = fm::launch_schedule(work_out, B * n_q, order_out, 0, 0, fm::schedule_shift(B * n_q), (int)n_kv,
                                     sched);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(0);
@@ -244,24 +244,10 @@ FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end, in
 
 namespace {
 
-// ---- the forward pass, in three parts: host-side checks, the workspace plan,
-// and the launches into a given workspace.
+// ---- the forward pass: host-side checks here; the workspace plan and the
+// launches into a given workspace are fm::fwd_plan / fm::fwd_launch.
 
-struct FwdArgs {
-    const void *q, *k, *v;
-    const int32_t *col_start, *col_end;
-    int32_t n_ranges;
-    int64_t B, H, N, d;
-    float scale;
-    void* out;
-    float* lse;
-    hipStream_t stream;
-    const float* fp8_scales;   // nullptr: bf16 inputs; else the three e4m3 dequantization scales
-    bool per_head;             // one interval set per head
-    bool fp8_weights;          // e4m3 weights and an FP8 PV product
-};
-
-int fwd_check(const FwdArgs& a) {
+int fwd_check(const fm::FwdArgs& a) {
     if (a.q == nullptr || a.k == nullptr || a.v == nullptr || a.col_start == nullptr || a.col_end == nullptr ||
         a.out == nullptr || a.lse == nullptr)
         return FM_ERR_INVALID_ARG;
@@ -279,59 +265,11 @@ int fwd_check(const FwdArgs& a) {
     return FM_OK;
 }
 
-// Workspace layout: meta[M][n_ranges] | work[M] | order[M] | scheduler scratch,
-// M = n_sets * B * n_q, each part 256-byte aligned.
-struct FwdPlan {
-    int64_t n_q, n_kv, n_sets, M;
-    size_t meta_bytes, int_bytes, sched_bytes;
-    size_t total() const { return meta_bytes + 2 * int_bytes + sched_bytes; }
-};
-
-FwdPlan fwd_plan(const FwdArgs& a) {
-    FwdPlan p;
-    p.n_q = (a.N + fm::kBr - 1) / fm::kBr;
-    p.n_kv = (a.N + fm::kBc - 1) / fm::kBc;
-    p.n_sets = a.per_head ? a.H : 1;
-    p.M = p.n_sets * a.B * p.n_q;
-    p.meta_bytes = ((size_t)(p.M * a.n_ranges) * sizeof(fm::TileMeta) + 255) & ~size_t(255);
-    p.int_bytes = ((size_t)p.M * sizeof(int32_t) + 255) & ~size_t(255);
-    const int64_t sched_ints = fm::schedule_scratch_ints(p.M, a.B * p.n_q, fm::kScheduleBucketShift, (int)p.n_kv);
-    p.sched_bytes = ((size_t)sched_ints * sizeof(int32_t) + 255) & ~size_t(255);
-    return p;
-}
-
-// Queues the preprocessor, the scheduler and the attention kernel on
-// a.stream, with ws (p.total() bytes, device memory) as their workspace.
-// Every byte of ws that a kernel reads was written earlier in the same
-// sequence, so ws needs no clearing.
-int fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, hipEvent_t ev_start, hipEvent_t ev_stop) {
-    auto* meta = static_cast<fm::TileMeta*>(ws);
-    auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes);
-    auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + p.int_bytes);
-    auto* sched = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + 2 * p.int_bytes);
-    const bool natural = g_schedule_mode == 1;
-    if (!natural && p.M <= fm::kPrepSmallMax) {
-        // one launch: metadata and longest-first order together
-        FM_HIP(fm::launch_prep_small(a.col_start, a.col_end, a.n_ranges, a.B, a.N, fm::kBr, fm::kBc, meta, work,
-                                     order, a.stream, (int)p.n_sets));
-    } else {
-        FM_HIP(fm::launch_preprocess(a.col_start, a.col_end, a.n_ranges, a.B, a.N, fm::kBr, fm::kBc, meta, work,
-                                     nullptr, a.stream, (int)p.n_sets));
-        if (!natural)
-            FM_HIP(fm::launch_schedule(work, p.M, order, a.stream, a.B * p.n_q, fm::kScheduleBucketShift,
-                                       (int)p.n_kv, sched));
-    }
-    FM_HIP(fm::launch_attention(a.q, a.k, a.v, a.col_start, a.col_end, a.n_ranges, meta, natural ? nullptr : order,
-                                a.B, a.H, a.N, a.d, a.scale, a.out, a.lse, a.stream, ev_start, ev_stop, a.fp8_scales,
-                                (int)p.n_sets, a.fp8_weights));
-    return FM_OK;
-}
-
 // The forward pass with the library's workspace for (device, stream).
-int attn_fwd_impl(const FwdArgs& a) {
+int attn_fwd_impl(const fm::FwdArgs& a) {
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
-    const FwdPlan p = fwd_plan(a);
+    const fm::FwdPlan p = fm::fwd_plan(a);
     void* ws = nullptr;
     std::unique_lock<std::mutex> ws_hold;       // held until the launches below are queued
     FM_HIP(get_workspace(a.stream, p.total(), &ws, ws_hold));
@@ -348,7 +286,8 @@ int attn_fwd_impl(const FwdArgs& a) {
             }
         }
     }
-    const int r = fwd_launch(a, p, ws, ev.first, ev.second);
+    const hipError_t e = fm::fwd_launch(a, p, ws, g_schedule_mode == 1, ev.first, ev.second);
+    const int r = e == hipSuccess ? FM_OK : hip_fail(e);
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
         if (r == FM_OK) g_timing.pending.push_back(ev);
@@ -357,11 +296,11 @@ int attn_fwd_impl(const FwdArgs& a) {
     return r;
 }
 
-FwdArgs fwd_args(const void* q, const void* k, const void* v, const int32_t* col_start, const int32_t* col_end,
+fm::FwdArgs fwd_args(const void* q, const void* k, const void* v, const int32_t* col_start, const int32_t* col_end,
                  int32_t n_ranges, int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out, float* lse,
                  hipStream_t stream, const float* fp8_scales = nullptr, bool per_head = false,
                  bool fp8_weights = false) {
-    return FwdArgs{q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, fp8_scales, per_head,
+    return fm::FwdArgs{q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream, fp8_scales, per_head,
                    fp8_weights};
 }
 
@@ -437,14 +376,15 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v, const int32_
 FM_API int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* col_start,
                                const int32_t* col_end, int32_t n_ranges, int64_t B, int64_t H, int64_t N,
                                int64_t d, float scale, void* out, float* lse, hipStream_t stream) {
-    const FwdArgs a = fwd_args(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream);
+    const fm::FwdArgs a = fwd_args(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream);
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
-    const FwdPlan p = fwd_plan(a);
+    const fm::FwdPlan p = fm::fwd_plan(a);
     if (p.total() > (size_t)FM_NOALLOC_SCRATCH_BYTES) return FM_ERR_TOO_LARGE;
     void* ws = nullptr;
     FM_HIP(scratch_address(&ws));
-    return fwd_launch(a, p, ws, nullptr, nullptr);
+    FM_HIP(fm::fwd_launch(a, p, ws, g_schedule_mode == 1, nullptr, nullptr));
+    return FM_OK;
 }
 
 }  // extern "C"
@@ -494,7 +434,7 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     const size_t part_floats = n_sets == 1 ? (size_t)fm::kBwdExtraPieces * H * fm::kBwdKeys * d * 2 : 0;
     const int64_t n_kv = (N + fm::kBc - 1) / fm::kBc;
     // scheduler scratch, used by the two orders one after the other
-    const int64_t sched_ints = std::max(fm::schedule_scratch_ints(Mq, B * n_q, fm::kScheduleBucketShift, (int)n_kv),
+    const int64_t sched_ints = std::max(fm::schedule_scratch_ints(Mq, B * n_q, fm::schedule_shift(Mq), (int)n_kv),
                                         fm::schedule_scratch_ints(Mp, Lp, 0, (int)n_qc));
     const size_t o_sched = o_part + al(part_floats * sizeof(float));
     const size_t total = o_sched + al((size_t)sched_ints * sizeof(int32_t));
@@ -525,8 +465,7 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     } else {
         FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, nullptr,
                                      stream, (int)n_sets));
-        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q, fm::kScheduleBucketShift, (int)n_kv,
-                                   sched));
+        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q, fm::schedule_shift(Mq), (int)n_kv, sched));
     }
     // dK, dV: query chunks per key block, long key blocks split into pieces,
     // pieces longest first (within each set)

@@ -1,0 +1,52 @@
+// The forward pass's launch sequence: workspace plan, then the interval
+// preprocessor, the work ordering and the attention kernel, queued on the
+// caller's stream.  The C ABI (fm_api.hip) checks the arguments and supplies
+// the workspace: the library's per-(device, stream) buffer, or the static
+// scratch array of the no-allocation entry point.  Everything that decides
+// what the attention launch does (its grid, its order, its tile records) is
+// here or in the kernels' own sources.
+
+#include "fm_internal.h"
+
+namespace fm {
+
+FwdPlan fwd_plan(const FwdArgs& a) {
+    FwdPlan p;
+    p.n_q = (a.N + kBr - 1) / kBr;
+    p.n_kv = (a.N + kBc - 1) / kBc;
+    p.n_sets = a.per_head ? a.H : 1;
+    p.M = p.n_sets * a.B * p.n_q;
+    p.meta_bytes = ((size_t)(p.M * a.n_ranges) * sizeof(TileMeta) + 255) & ~size_t(255);
+    p.int_bytes = ((size_t)p.M * sizeof(int32_t) + 255) & ~size_t(255);
+    const int64_t sched_ints = schedule_scratch_ints(p.M, a.B * p.n_q, schedule_shift(p.M), (int)p.n_kv);
+    p.sched_bytes = ((size_t)sched_ints * sizeof(int32_t) + 255) & ~size_t(255);
+    return p;
+}
+
+hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, bool natural, hipEvent_t ev_start,
+                      hipEvent_t ev_stop) {
+    auto* meta = static_cast<TileMeta*>(ws);
+    auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes);
+    auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + p.int_bytes);
+    auto* sched = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + 2 * p.int_bytes);
+    hipError_t e;
+    if (!natural && p.M <= kPrepSmallMax) {
+        // one launch: metadata and longest-first order together
+        e = launch_prep_small(a.col_start, a.col_end, a.n_ranges, a.B, a.N, kBr, kBc, meta, work, order, a.stream,
+                              (int)p.n_sets);
+        if (e != hipSuccess) return e;
+    } else {
+        e = launch_preprocess(a.col_start, a.col_end, a.n_ranges, a.B, a.N, kBr, kBc, meta, work, nullptr, a.stream,
+                              (int)p.n_sets);
+        if (e != hipSuccess) return e;
+        if (!natural) {
+            e = launch_schedule(work, p.M, order, a.stream, a.B * p.n_q, schedule_shift(p.M), (int)p.n_kv, sched);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return launch_attention(a.q, a.k, a.v, a.col_start, a.col_end, a.n_ranges, meta, natural ? nullptr : order, a.B,
+                            a.H, a.N, a.d, a.scale, a.out, a.lse, a.stream, ev_start, ev_stop, a.fp8_scales,
+                            (int)p.n_sets, a.fp8_weights);
+}
+
+}  // namespace fm

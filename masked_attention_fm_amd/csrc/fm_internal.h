@@ -66,14 +66,19 @@ int64_t schedule_scratch_ints(int64_t M, int64_t L, int shift, int max_work);
 hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipStream_t stream, int64_t L,
                            int shift, int max_work, int32_t* scratch);
 
-// Work bucket of the attention kernel's order on the large-problem path:
-// 32 key blocks.  The one-workgroup path (at most kPrepSmallMax query blocks,
-// too few to fill the XCDs several times over) ranks by exact work.
+// Work bucket of the attention kernel's order above kScheduleExactMax query
+// blocks: 32 key blocks.  Up to kScheduleExactMax query blocks (too few to fill
+// the XCDs several times over) the order ranks by exact work.
 constexpr int kScheduleBucketShift = 5;
+constexpr int kScheduleExactMax = 256;
+inline int schedule_shift(int64_t M) { return M <= kScheduleExactMax ? 0 : kScheduleBucketShift; }
 
 // Preprocessor and scheduler in one launch of one workgroup, for at most
 // kPrepSmallMax query blocks (B * n_q): same meta, work and order outputs.
-constexpr int kPrepSmallMax = 256;
+// Above that the intervals are reduced by many workgroups (one wavefront per
+// query block) and the order is a separate launch: one CU reading every row's
+// intervals takes longer than the second launch costs.
+constexpr int kPrepSmallMax = 64;
 hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B,
                              int64_t N, int Br, int Bc, TileMeta* meta, int32_t* work, int32_t* order,
                              hipStream_t stream, int n_sets = 1);
@@ -88,6 +93,37 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
                             const float* fp8_scales = nullptr, int n_sets = 1, bool fp8_weights = false);
+
+// The forward pass's launch sequence (fm_forward.hip).
+struct FwdArgs {
+    const void *q, *k, *v;
+    const int32_t *col_start, *col_end;
+    int32_t n_ranges;
+    int64_t B, H, N, d;
+    float scale;
+    void* out;
+    float* lse;
+    hipStream_t stream;
+    const float* fp8_scales;   // nullptr: bf16 inputs; else the three e4m3 dequantization scales
+    bool per_head;             // one interval set per head
+    bool fp8_weights;          // e4m3 weights and an FP8 PV product
+};
+
+// Workspace layout: meta[M][n_ranges] | work[M] | order[M] | scheduler scratch,
+// M = n_sets * B * n_q, each part 256-byte aligned.
+struct FwdPlan {
+    int64_t n_q, n_kv, n_sets, M;
+    size_t meta_bytes, int_bytes, sched_bytes;
+    size_t total() const { return meta_bytes + 2 * int_bytes + sched_bytes; }
+};
+FwdPlan fwd_plan(const FwdArgs& a);
+
+// Queues the preprocessor, the scheduler (unless natural order) and the
+// attention kernel on a.stream, with ws (p.total() bytes of device memory) as
+// their workspace.  Every byte of ws that a kernel reads was written earlier
+// in the same sequence, so ws needs no clearing.
+hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, bool natural, hipEvent_t ev_start,
+                      hipEvent_t ev_stop);
 
 // Backward pass (gradients of Q, K, V).  Shapes: the key-block kernel runs
 // kBwdKeys keys per workgroup against query chunks of kBwdRows rows; the

@@ -52,38 +52,102 @@ __device__ __forceinline__ uint32_t sort_key(int kw, int idx, int bits) {
     return ((kmax - (uint32_t)kw) << bits) | (uint32_t)idx;
 }
 
-// Ascending bitonic sort of s[0, n), n a power of two, by the whole workgroup.
-__device__ __forceinline__ void bitonic_sort_lds(uint32_t* s, int n) {
+// Ascending bitonic sort of n = E * kSortThreads 32-bit keys (E a power of two,
+// at most kMaxPerThread) held E per thread in registers, thread t holding
+// elements t E .. t E + E - 1.  A compare-exchange of elements x and x ^ j
+// keeps the smaller value in the lower element when (x & k) == 0 (ascending
+// run), the larger otherwise.  Partners inside one thread (j < E) exchange in
+// registers, partners inside one wavefront (j < 64 E) with lane shuffles, and
+// only the stages whose partners lie in other wavefronts go through LDS
+// (buffer s, n entries), two barriers each.
+constexpr int kMaxPerThread = kSortSmall / kSortThreads;   // 16
+
+template <int E>
+__device__ __forceinline__ void bitonic_sort_regs(uint32_t (&v)[E], uint32_t* s) {
+    constexpr int n = E * kSortThreads;
+    const int t = threadIdx.x;
     for (int k = 2; k <= n; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < (n >> 1); i += kSortThreads) {
-                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-                const int hi = lo | j;
-                const uint32_t a = s[lo];
-                const uint32_t b = s[hi];
-                const bool up = (lo & k) == 0;
-                if ((a > b) == up) {
-                    s[lo] = b;
-                    s[hi] = a;
+            if (j < E) {
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const int pr = r ^ j;
+                    if (pr > r) {
+                        const int x = t * E + r;
+                        const bool up = (x & k) == 0;
+                        const uint32_t a = v[r], b = v[pr];
+                        v[r] = up ? min(a, b) : max(a, b);
+                        v[pr] = up ? max(a, b) : min(a, b);
+                    }
                 }
+            } else if (j < 64 * E) {
+                const int lane_mask = j / E;
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const int x = t * E + r;
+                    const uint32_t other = (uint32_t)__shfl_xor((int)v[r], lane_mask);
+                    const bool keep_min = ((x & j) == 0) == ((x & k) == 0);
+                    v[r] = keep_min ? min(v[r], other) : max(v[r], other);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < E; ++r) s[t * E + r] = v[r];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const int x = t * E + r;
+                    const uint32_t other = s[x ^ j];
+                    const bool keep_min = ((x & j) == 0) == ((x & k) == 0);
+                    v[r] = keep_min ? min(v[r], other) : max(v[r], other);
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 }
 
-// One segment of L <= kSortSmall items per workgroup: load, sort, write the
-// order.  Entries past L hold 0xFFFFFFFF, which no item's key reaches (an
-// item key with every bit set would need index 2^bits - 1 >= L).
-__global__ __launch_bounds__(kSortThreads) void order_small_kernel(const int32_t* __restrict__ work, int L,
-                                                                   int n, int shift, int32_t* __restrict__ order) {
+// Sorts the keys key(i) for i < count (entries up to n hold 0xFFFFFFFF) and
+// leaves them sorted in s[0, n); n = E * kSortThreads.
+template <int E, typename KeyOf>
+__device__ __forceinline__ void sort_into_lds(uint32_t* s, int count, KeyOf key) {
+    uint32_t v[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int x = threadIdx.x * E + r;
+        v[r] = x < count ? key(x) : 0xFFFFFFFFu;
+    }
+    bitonic_sort_regs<E>(v, s);
+#pragma unroll
+    for (int r = 0; r < E; ++r) s[threadIdx.x * E + r] = v[r];
+    __syncthreads();
+}
+
+// Dispatch on the per-thread count for n = max(kSortThreads, next power of two >= count).
+template <typename KeyOf>
+__device__ __forceinline__ int sort_keys(uint32_t* s, int count, KeyOf key) {
+    int e = 1;
+    while (e * kSortThreads < count) e <<= 1;
+    switch (e) {
+        case 1: sort_into_lds<1>(s, count, key); break;
+        case 2: sort_into_lds<2>(s, count, key); break;
+        case 4: sort_into_lds<4>(s, count, key); break;
+        case 8: sort_into_lds<8>(s, count, key); break;
+        default: sort_into_lds<16>(s, count, key); break;
+    }
+    return e * kSortThreads;
+}
+
+// One segment of L <= kSortSmall items per workgroup: keys into registers,
+// sort, write the order.  Padding entries hold 0xFFFFFFFF, which no item's
+// key reaches (an item key with every bit set would need index
+// 2^bits - 1 >= L).
+__global__ __launch_bounds__(kSortThreads) void order_small_kernel(const int32_t* __restrict__ work, int L, int shift,
+                                                                   int32_t* __restrict__ order) {
     __shared__ uint32_t s[kSortSmall];
     const int64_t lo = (int64_t)blockIdx.x * L;
-    for (int i = threadIdx.x; i < n; i += kSortThreads)
-        s[i] = i < L ? sort_key(work_value(work[lo + i], shift, (1 << (32 - kSortSmallBits)) - 1), i, kSortSmallBits)
-                     : 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_sort_lds(s, n);
+    sort_keys(s, L, [&](int i) {
+        return sort_key(work_value(work[lo + i], shift, (1 << (32 - kSortSmallBits)) - 1), i, kSortSmallBits);
+    });
     const uint32_t mask = (1u << kSortSmallBits) - 1u;
     for (int p = threadIdx.x; p < L; p += kSortThreads) order[lo + p] = (int32_t)(lo + (s[p] & mask));
 }
@@ -105,10 +169,11 @@ __global__ __launch_bounds__(kSortThreads) void order_count_kernel(const int32_t
     const int n_c = min(kSortChunk, L - c * kSortChunk);
     int32_t* row = cnt + (int64_t)t * n_keys;
     for (int k = threadIdx.x; k < n_keys; k += kSortThreads) row[k] = 0;
-    for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads)
-        s[i] = i < n_c ? sort_key(work_value(work[base + i], shift, n_keys - 1), i, kSortChunkBits) : 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_sort_lds(s, kSortChunk);
+    __syncthreads();                                       // the row is cleared before any count is stored
+    static_assert(kSortChunk == 8 * kSortThreads, "eight keys per thread");
+    sort_into_lds<8>(s, n_c, [&](int i) {
+        return sort_key(work_value(work[base + i], shift, n_keys - 1), i, kSortChunkBits);
+    });
     const uint32_t kmax = (1u << (32 - kSortChunkBits)) - 1u;
     const uint32_t mask = (1u << kSortChunkBits) - 1u;
     for (int p = threadIdx.x; p < n_c; p += kSortThreads) {
@@ -187,6 +252,10 @@ __global__ __launch_bounds__(256) void order_place_kernel(const int32_t* __restr
 }
 
 constexpr int kPrepThreads = 1024;
+// LDS slots of the one-launch prep's rank: G lanes per item (G <= 64) each
+// take SL entries, SL = (ceil(M / G) + 3) rounded down to a multiple of 4,
+// so G * SL <= G * ceil(M / G) + 3 G <= M + 4 G <= kPrepSmallMax + 256.
+constexpr int kPrepWorkSlots = kPrepSmallMax + 4 * 64;
 
 // Small problems: one workgroup computes every query block's metadata and
 // then ranks the blocks from LDS, saving a launch.  Each query block gets a
@@ -200,8 +269,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_small_kernel(
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int n_q, int n_kv,
     int Br, int Bc, int M, int G, bool vec4, int n_sets, int L, TileMeta* __restrict__ meta,
     int32_t* __restrict__ work, int32_t* __restrict__ order) {
-    // work of each item, padded with INT_MIN up to G * SL <= M + 4 G <= 2 * kPrepSmallMax entries
-    __shared__ __attribute__((aligned(16))) int s_work[2 * kPrepSmallMax];
+    // work of each item, padded with INT_MIN up to G * SL <= kPrepWorkSlots entries
+    __shared__ __attribute__((aligned(16))) int s_work[kPrepWorkSlots];
     const int item = threadIdx.x / G;          // G divides 64: a group never straddles wavefronts
     const int g = threadIdx.x % G;
     if (item < M) {
@@ -313,10 +382,8 @@ hipError_t launch_schedule(const int32_t* work, int64_t M, int32_t* order, hipSt
     if (M <= 0 || M % L != 0 || max_work < 0) return hipErrorInvalidValue;
     const int64_t S = M / L;
     if (L <= kSortSmall) {
-        int n = 1;
-        while (n < L) n <<= 1;
-        hipLaunchKernelGGL(order_small_kernel, dim3((unsigned)S), dim3(kSortThreads), 0, stream, work, (int)L, n,
-                           shift, order);
+        hipLaunchKernelGGL(order_small_kernel, dim3((unsigned)S), dim3(kSortThreads), 0, stream, work, (int)L, shift,
+                           order);
         return hipGetLastError();
     }
     // counting sort: keys are work' = (work >> shift) + 1 in [0, n_keys)

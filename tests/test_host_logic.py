@@ -103,3 +103,35 @@ def test_code_hash_ignores_comments_and_whitespace():
     c = "int f(int x) {\n    return 3 * x;\n}\n"
     assert counters.attn_source_hash([a]) == counters.attn_source_hash([b])
     assert counters.attn_source_hash([a]) != counters.attn_source_hash([c])
+
+
+def _wave_mfma_brute(s, e, N, H, d, Br=128, Bc=64, R=32):
+    """Wavefront by wavefront, key block by key block: computed when some row of the
+    wavefront attends some key of the block through any of its ranges."""
+    s = np.asarray(s); e = np.asarray(e)
+    if s.ndim == 2:
+        s, e = s[:, None], e[:, None]
+    per_block = (d // 16) * (Bc // 32) + (Bc // 16) * (d // 32)
+    n = 0
+    for b in range(s.shape[0]):
+        for w0 in range(0, N, R):
+            rows = range(w0, min(w0 + R, N))
+            for j in range(-(-N // Bc)):
+                klo, khi = j * Bc, min(j * Bc + Bc, N) - 1
+                if any(max(s[b, k, r], 0) <= min(e[b, k, r], N - 1) and max(s[b, k, r], 0) <= khi
+                       and min(e[b, k, r], N - 1) >= klo
+                       for r in rows for k in range(s.shape[1])):
+                    n += per_block
+    return n * H
+
+
+@pytest.mark.parametrize("K,N,d", [(1, 300, 128), (1, 129, 64), (2, 500, 128), (3, 200, 64)])
+def test_wave_mfma_count_matches_brute_force(K, N, d):
+    """A wavefront computes a key block when one of its rows attends a key in it through
+    one range: the count per wavefront is then the union of the ranges' block spans,
+    which the vectorised count uses (valid and empty ranges, several per row)."""
+    rng = np.random.default_rng(K * N + d)
+    s, e = inputs.random_multi_intervals(rng, 2, K, N, empty_frac=0.2, max_width=N // 3)
+    if K == 1:
+        s, e = s[:, 0], e[:, 0]
+    assert metrics.wave_mfma_instructions(s, e, N, 3, d) == _wave_mfma_brute(s, e, N, 3, d)
