@@ -304,10 +304,15 @@ FM_API int fm_tile_schedule(const int32_t* col_start, const int32_t* col_end,
 /* Process-wide options (not synchronized with calls in flight on other threads). */
 enum {
     FM_OPT_SCHEDULE = 1,      /* 0: longest-first order (default), 1: natural (b, t) order */
-    FM_OPT_BWD_SPLIT_CHUNKS = 2 /* backward: a key block attended by more than max(this, twice the
+    FM_OPT_BWD_SPLIT_CHUNKS = 2, /* backward: a key block attended by more than max(this, twice the
                                    mean) query chunks of 64 rows is split into pieces of about that
                                    many chunks, whose partial dK/dV are summed in a fixed order
                                    (deterministic); default 32, 0: never split */
+    FM_OPT_SINGLE_LAUNCH = 3    /* forward, bf16 inputs: 1 (default) runs problems of at most 256
+                                   workgroups (B * H * ceil(N/128)) as the attention kernel alone, each
+                                   workgroup reducing its own query block's key range; 0 always
+                                   queues the interval preprocessor and the work ordering first.
+                                   Results are identical either way. */
 };
 FM_API int fm_set_option(int option, int64_t value);
 

@@ -39,6 +39,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // ---------------------------------------------------------------- options
 
 int g_schedule_mode = 0;   // 0 longest first, 1 natural order
+int g_single_launch = 1;   // 1: small problems run the attention kernel alone
 int g_bwd_min_chunks = 32; // smallest piece of a split key block (query chunks); 0: never split
 
 // ---------------------------------------------------------------- workspace
@@ -135,6 +136,11 @@ FM_API int fm_set_option(int option, int64_t value) {
     if (option == FM_OPT_SCHEDULE) {
         if (value != 0 && value != 1) return FM_ERR_INVALID_ARG;
         g_schedule_mode = (int)value;
+        return FM_OK;
+    }
+    if (option == FM_OPT_SINGLE_LAUNCH) {
+        if (value != 0 && value != 1) return FM_ERR_INVALID_ARG;
+        g_single_launch = (int)value;
         return FM_OK;
     }
     if (option == FM_OPT_BWD_SPLIT_CHUNKS) {
@@ -286,7 +292,7 @@ int attn_fwd_impl(const fm::FwdArgs& a) {
             }
         }
     }
-    const hipError_t e = fm::fwd_launch(a, p, ws, g_schedule_mode == 1, ev.first, ev.second);
+    const hipError_t e = fm::fwd_launch(a, p, ws, g_schedule_mode == 1, g_single_launch == 1, ev.first, ev.second);
     const int r = e == hipSuccess ? FM_OK : hip_fail(e);
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
@@ -383,7 +389,7 @@ FM_API int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, cons
     if (p.total() > (size_t)FM_NOALLOC_SCRATCH_BYTES) return FM_ERR_TOO_LARGE;
     void* ws = nullptr;
     FM_HIP(scratch_address(&ws));
-    FM_HIP(fm::fwd_launch(a, p, ws, g_schedule_mode == 1, nullptr, nullptr));
+    FM_HIP(fm::fwd_launch(a, p, ws, g_schedule_mode == 1, g_single_launch == 1, nullptr, nullptr));
     return FM_OK;
 }
 

@@ -581,9 +581,15 @@ void attn_fwd_kernel(
     const int local = bt - set * L;
     const int b = local / n_q;
     const int t = local - b * n_q;
+    // The query block's key-block records (only the non-skip range x..y of
+    // each range is used here), from the preprocessor; without one (meta ==
+    // nullptr, small problems launched alone) they are reduced below from the
+    // block's own staged intervals.
     TileMeta tm[NIV];
+    if (meta != nullptr) {
 #pragma unroll
-    for (int k = 0; k < NIV; ++k) tm[k] = meta[(int64_t)bt * NIV + k];
+        for (int k = 0; k < NIV; ++k) tm[k] = meta[(int64_t)bt * NIV + k];
+    }
 
     const int64_t bh = (int64_t)b * H + h;
     const typename T::In* Qbh = Q + bh * N * D;
@@ -611,6 +617,31 @@ void attn_fwd_kernel(
             sm.start[k][tid] = s;
             sm.width[k][tid] = w;
         }
+    }
+
+    if constexpr (!F8) {
+      if (meta == nullptr) {
+        // Every wavefront reduces the smallest start and largest end over all
+        // kBr rows of the block (two rows per lane), the preprocessor's rule,
+        // before any Q row occupies registers.  (bf16 inputs only: the host
+        // never launches the e4m3 kernels without records.)
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            int lo = INT_MAX, hi = INT_MIN;
+#pragma unroll
+            for (int r = lane; r < kBr; r += 64) {
+                const int st = sm.start[k][r];
+                if (st != kEmptyStart) {
+                    lo = min(lo, st);
+                    hi = max(hi, st + sm.width[k][r]);
+                }
+            }
+            lo = wave_min(lo);
+            hi = wave_max(hi);
+            tm[k] = hi >= lo ? make_int4(lo / kBc, hi / kBc, 0, -1) : make_int4(0, -1, 0, -1);
+        }
+      }
     }
 
     // Q rows of this lane as MFMA B operands: Q[row][16 cs + 8 half .. +7]

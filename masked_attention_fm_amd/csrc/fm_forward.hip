@@ -23,8 +23,12 @@ FwdPlan fwd_plan(const FwdArgs& a) {
     return p;
 }
 
-hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, bool natural, hipEvent_t ev_start,
-                      hipEvent_t ev_stop) {
+hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, bool natural, bool single_launch,
+                      hipEvent_t ev_start, hipEvent_t ev_stop) {
+    if (single_launch && a.fp8_scales == nullptr && p.M * a.H / p.n_sets <= kSingleLaunchGrid)
+        return launch_attention(a.q, a.k, a.v, a.col_start, a.col_end, a.n_ranges, nullptr, nullptr, a.B, a.H, a.N,
+                                a.d, a.scale, a.out, a.lse, a.stream, ev_start, ev_stop, a.fp8_scales, (int)p.n_sets,
+                                a.fp8_weights);
     auto* meta = static_cast<TileMeta*>(ws);
     auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes);
     auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + p.int_bytes);

@@ -121,9 +121,13 @@ FwdPlan fwd_plan(const FwdArgs& a);
 // Queues the preprocessor, the scheduler (unless natural order) and the
 // attention kernel on a.stream, with ws (p.total() bytes of device memory) as
 // their workspace.  Every byte of ws that a kernel reads was written earlier
-// in the same sequence, so ws needs no clearing.
-hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, bool natural, hipEvent_t ev_start,
-                      hipEvent_t ev_stop);
+// in the same sequence, so ws needs no clearing.  With single_launch, a bf16
+// grid of at most kSingleLaunchGrid workgroups (all resident at once, so their
+// order cannot matter) runs the attention kernel alone: each workgroup
+// reduces its own query block's key range from the intervals it stages.
+constexpr int64_t kSingleLaunchGrid = 256;
+hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, bool natural, bool single_launch,
+                      hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Backward pass (gradients of Q, K, V).  Shapes: the key-block kernel runs
 // kBwdKeys keys per workgroup against query chunks of kBwdRows rows; the

@@ -113,6 +113,8 @@ def test_options_and_strings(L):
     assert L.fm_set_option(fmb.FM_OPT_SCHEDULE, 0) == fmb.FM_OK
     assert L.fm_set_option(fmb.FM_OPT_BWD_SPLIT_CHUNKS, -1) == fmb.FM_ERR_INVALID_ARG
     assert L.fm_set_option(fmb.FM_OPT_BWD_SPLIT_CHUNKS, 32) == fmb.FM_OK
+    assert L.fm_set_option(fmb.FM_OPT_SINGLE_LAUNCH, 2) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_set_option(fmb.FM_OPT_SINGLE_LAUNCH, 1) == fmb.FM_OK
     for s in range(5):
         assert L.fm_status_string(s)
     assert b"unknown" in L.fm_status_string(42)
@@ -244,6 +246,7 @@ def test_header_options_match_binding():
     text = open(HEADER, encoding="utf-8").read()
     assert re.search(r"FM_OPT_SCHEDULE = (\d+)", text).group(1) == str(fmb.FM_OPT_SCHEDULE)
     assert re.search(r"FM_OPT_BWD_SPLIT_CHUNKS = (\d+)", text).group(1) == str(fmb.FM_OPT_BWD_SPLIT_CHUNKS)
+    assert re.search(r"FM_OPT_SINGLE_LAUNCH = (\d+)", text).group(1) == str(fmb.FM_OPT_SINGLE_LAUNCH)
 
 
 def test_header_fp8_modes_match_binding():

@@ -384,3 +384,35 @@ def test_maximum_sequence_length():
                                      rng.integers(0, N, 200)]))
     log("maximum length N=2^22")
     check_case(q, k, v, s, e, inputs.default_scale(d), "N=2^22", rows=rows)
+
+
+@pytest.mark.parametrize("kind", ["single", "multi", "per_head"])
+def test_single_launch_equals_preprocessed_launch(kind):
+    """Small bf16 problems (at most 256 workgroups) run the attention kernel alone, each
+    workgroup reducing its own key range from its staged intervals; with
+    FM_OPT_SINGLE_LAUNCH = 0 the preprocessor and the work ordering run first.  Both give
+    the same bits."""
+    rng = np.random.default_rng(91)
+    B, H, N, d = 2, 3, 1000, 128
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=91)
+    scale = inputs.default_scale(d)
+    if kind == "single":
+        s, e = inputs.random_intervals(rng, B, N, empty_frac=0.1, max_width=300)
+        call = lambda qd, kd, vd, sd, ed: fm.fm_attn_fwd(qd, kd, vd, sd, ed, scale)
+    elif kind == "multi":
+        s, e = inputs.random_multi_intervals(rng, B, 3, N, empty_frac=0.2, max_width=200)
+        call = lambda qd, kd, vd, sd, ed: fm.fm_attn_fwd_multi(qd, kd, vd, sd, ed, scale)
+    else:
+        s, e = inputs.random_multi_intervals(rng, B * H, 2, N, max_width=400)
+        s, e = s.reshape(B, H, 2, N), e.reshape(B, H, 2, N)
+        call = lambda qd, kd, vd, sd, ed: fm.fm_attn_fwd_per_head(qd, kd, vd, sd, ed, scale)
+    args = to_dev(q, k, v, np.ascontiguousarray(s), np.ascontiguousarray(e))
+    log(f"single launch vs preprocessed launch: {kind}")
+    o1, l1 = call(*args)
+    try:
+        fm.fm_set_option(fm.FM_OPT_SINGLE_LAUNCH, 0)
+        o2, l2 = call(*args)
+    finally:
+        fm.fm_set_option(fm.FM_OPT_SINGLE_LAUNCH, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
