@@ -1,16 +1,23 @@
-"""Summarise rocprofv3 hardware-counter runs of bench.py into a small JSON record.
+"""Summarise rocprofv3 hardware-counter runs into a small JSON record.
 
-    python -m masked_attention_fm_amd.counters OUT.json COPY_MIB RUN_DIR [RUN_DIR ...]
+    python -m masked_attention_fm_amd.counters [--kernel KIND] OUT.json COPY_MIB RUN_DIR [RUN_DIR ...]
 
 Each RUN_DIR is the output directory of one ``rocprofv3 --pmc ... -o run
---output-format csv -- python3 bench.py --config CFG --no-per-config
---no-backward --no-fp8 --no-cpu-baseline --copy-mib M ...`` pass.  The record
-holds, per counter, the mean over the dispatches of the bf16 attention kernel
-(``attn_fwd_kernel<d, ranges, 0>``; the FP8 instances are other kernels and
-never counted) and over the reference copy's dispatches, the byte calibration
-that the copy of known size gives, and a hash of the code that decides what
-the attention launch does (kernel, preprocessor, scheduler, launch set-up) so
-that a later change makes the record stale.
+--output-format csv -- python3 ...`` pass over a program that runs the kernel
+and, at its end, a plain device copy of COPY_MIB MiB (bench.py --copy-mib M with
+--no-backward --no-fp8, or masked_attention_fm_amd.profile_steps --copy-mib M).
+KIND picks the kernel (default ``attention``):
+
+* ``attention``: the bf16 forward kernel ``attn_fwd_kernel<d, ranges, 0>`` (the
+  FP8 instances are other kernels and never counted);
+* ``bwd_dkdv`` / ``bwd_dq``: the backward's dK/dV and dQ kernels.
+
+The record holds, per counter, the mean over that kernel's dispatches and over
+the reference copy's dispatches, the byte calibration that the copy of known
+size gives, and a hash of the code that decides what the kernel's launch does
+(kernel, preprocessing, ordering, launch set-up) so that a later change makes
+the record stale.  The per-kernel means sit under "attention" for every KIND
+(the name the forward's readers use); "kernel" names the KIND.
 """
 from __future__ import annotations
 
@@ -34,6 +41,15 @@ ATTN_SOURCES = [os.path.join(PKG, "csrc", name) for name in
 MFMA_FLOPS = 2 * 32 * 32 * 16
 
 _BF16_ATTN = re.compile(r"attn_fwd_kernel<\s*\d+\s*,\s*\d+\s*,\s*0\s*>")
+# The backward's kernels and the sources of their launch sequence.
+BWD_SOURCES = [os.path.join(PKG, "csrc", name) for name in
+               ("fm_attn_bwd.hip", "fm_internal.h", "fm_mfma.h", "fm_schedule.hip", "fm_intervals.hip",
+                "fm_api.hip")]
+KINDS = {
+    "attention": (_BF16_ATTN, ATTN_SOURCES),
+    "bwd_dkdv": (re.compile(r"bwd_dkdv_kernel<"), BWD_SOURCES),
+    "bwd_dq": (re.compile(r"bwd_dq_kernel<"), BWD_SOURCES),
+}
 
 
 def code_text(text: str) -> str:
@@ -61,22 +77,32 @@ def attn_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def kind_of(name: str) -> str:
-    """'attention' for the bf16 attention kernel, 'copy' for the runtime's buffer copy."""
-    if _BF16_ATTN.search(name):
+def source_hash(kind: str = "attention") -> str:
+    """attn_source_hash over the sources of KIND's launch."""
+    texts = []
+    for path in KINDS[kind][1]:
+        with open(path, encoding="utf-8") as f:
+            texts.append(f.read())
+    return attn_source_hash(texts)
+
+
+def kind_of(name: str, kernel: str = "attention") -> str:
+    """'attention' for the counted kernel (KIND `kernel`), 'copy' for the runtime's buffer
+    copy, '' for anything else."""
+    if KINDS[kernel][0].search(name):
         return "attention"
     if "copyBuffer" in name:
         return "copy"
     return ""
 
 
-def summarise(run_dirs, copy_mib: int):
+def summarise(run_dirs, copy_mib: int, kernel: str = "attention"):
     sums = {"attention": defaultdict(list), "copy": defaultdict(list)}
     for d in run_dirs:
         path = os.path.join(d, "run_counter_collection.csv")
         with open(path, newline="") as f:
             for row in csv.DictReader(f):
-                kind = kind_of(row["Kernel_Name"])
+                kind = kind_of(row["Kernel_Name"], kernel)
                 if not kind:
                     continue
                 value = float(row["Counter_Value"])
@@ -86,8 +112,8 @@ def summarise(run_dirs, copy_mib: int):
                 sums[kind][row["Counter_Name"]].append(value)
     mean = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in sums.items()}
     dispatches = {k: {c: len(v) for c, v in cs.items()} for k, cs in sums.items()}
-    out = {"attention": mean["attention"], "copy": mean["copy"], "copy_mib": copy_mib,
-           "dispatches": dispatches, "attn_source_sha256_16": attn_source_hash()}
+    out = {"attention": mean["attention"], "copy": mean["copy"], "copy_mib": copy_mib, "kernel": kernel,
+           "dispatches": dispatches, "attn_source_sha256_16": source_hash(kernel)}
     copy_kib = copy_mib * 1024.0
     cal = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -116,11 +142,14 @@ def summarise(run_dirs, copy_mib: int):
 
 
 def main(argv):
-    if len(argv) < 3:
+    kernel = "attention"
+    if len(argv) >= 2 and argv[0] == "--kernel":
+        kernel, argv = argv[1], argv[2:]
+    if len(argv) < 3 or kernel not in KINDS:
         print(__doc__)
         return 2
     out_path, copy_mib, dirs = argv[0], int(argv[1]), argv[2:]
-    rec = summarise(dirs, copy_mib)
+    rec = summarise(dirs, copy_mib, kernel)
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps(rec, indent=1, sort_keys=True))

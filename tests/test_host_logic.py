@@ -97,6 +97,24 @@ def test_counter_kernel_filter():
         assert counters.kind_of(name) == ""
 
 
+def test_counter_kernel_filter_backward(tmp_path):
+    """--kernel bwd_dkdv / bwd_dq count only that backward kernel, hashed over the backward's
+    launch sources."""
+    dkdv = "void fm::(anonymous namespace)::bwd_dkdv_kernel<128, 1>(...)"
+    dq = "void fm::(anonymous namespace)::bwd_dq_kernel<128, 1>(...)"
+    fwd = "void fm::(anonymous namespace)::attn_fwd_kernel<128, 1, 0>(...)"
+    assert counters.kind_of(dkdv, "bwd_dkdv") == "attention"
+    assert counters.kind_of(dq, "bwd_dkdv") == ""
+    assert counters.kind_of(fwd, "bwd_dkdv") == ""
+    assert counters.kind_of(dq, "bwd_dq") == "attention"
+    assert counters.kind_of(dkdv, "bwd_dq") == ""
+    _write_run(tmp_path / "a", [(dkdv, "SQ_INSTS_MFMA", 10.0), (dq, "SQ_INSTS_MFMA", 99.0),
+                                (fwd, "SQ_INSTS_MFMA", 7.0)])
+    rec = counters.summarise([tmp_path / "a"], copy_mib=0, kernel="bwd_dkdv")
+    assert rec["attention"]["SQ_INSTS_MFMA"] == 10.0 and rec["kernel"] == "bwd_dkdv"
+    assert rec["attn_source_sha256_16"] == counters.source_hash("bwd_dkdv") != counters.attn_source_hash()
+
+
 def test_code_hash_ignores_comments_and_whitespace():
     a = "int f(int x) {  // doubles\n    return 2 * x;\n}\n"
     b = "// f: twice x\nint f(int x) {\n\n  return 2 * x;   // twice\n}\n"
