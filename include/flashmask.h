@@ -308,11 +308,17 @@ enum {
                                    mean) query chunks of 64 rows is split into pieces of about that
                                    many chunks, whose partial dK/dV are summed in a fixed order
                                    (deterministic); default 32, 0: never split */
-    FM_OPT_SINGLE_LAUNCH = 3    /* forward, bf16 inputs: 1 (default) runs problems of at most 256
+    FM_OPT_SINGLE_LAUNCH = 3,   /* forward, bf16 inputs: 1 (default) runs problems of at most 256
                                    workgroups (B * H * ceil(N/128)) as the attention kernel alone, each
                                    workgroup reducing its own query block's key range; 0 always
                                    queues the interval preprocessor and the work ordering first.
-                                   Results are identical either way. */
+                                   Results are identical either way when FM_OPT_SPLIT_KEYS is 0. */
+    FM_OPT_SPLIT_KEYS = 4       /* forward, bf16 single launches (above): 1 (default) cuts each query
+                                   block's key range into up to 8 pieces of at least two key blocks,
+                                   run by separate workgroups (at most 256 in all) whose partial
+                                   softmax states the last one to finish combines; 0 never.  The
+                                   results differ from the unsplit ones only by the order of fp32
+                                   additions.  fm_attn_fwd_noalloc never splits. */
 };
 FM_API int fm_set_option(int option, int64_t value);
 

@@ -40,6 +40,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int g_schedule_mode = 0;   // 0 longest first, 1 natural order
 int g_single_launch = 1;   // 1: small problems run the attention kernel alone
+int g_split_keys = 1;      // 1: single launches split long key ranges over several workgroups
 int g_bwd_min_chunks = 32; // smallest piece of a split key block (query chunks); 0: never split
 
 // ---------------------------------------------------------------- workspace
@@ -58,16 +59,20 @@ int g_bwd_min_chunks = 32; // smallest piece of a split key block (query chunks)
 // the old buffer alive until they have run.
 
 struct Workspace {
-    std::mutex mu;            // held while a call queues work that uses ptr
+    std::mutex mu;            // held while a call queues work that uses ptr or counters
     void* ptr = nullptr;
     size_t bytes = 0;
+    unsigned* counters = nullptr;   // fm::kSplitCounters arrival counters, zero between calls
 };
 std::mutex g_ws_map_mutex;    // guards the map itself (its nodes never move)
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 // On success *out is the buffer and `hold` owns its lock; the caller keeps
 // `hold` until its last launch that uses the buffer is queued.
-hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out, std::unique_lock<std::mutex>& hold) {
+// With `counters`, also the stream's split-arrival counters, allocated and
+// zero-filled on first use (the kernels that use them leave them zero).
+hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out, std::unique_lock<std::mutex>& hold,
+                         unsigned** counters = nullptr) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -92,6 +97,18 @@ hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out, std::uniq
             return e;
         }
         w->bytes = nb;
+    }
+    if (counters != nullptr) {
+        if (w->counters == nullptr) {
+            e = hipMallocAsync(reinterpret_cast<void**>(&w->counters), fm::kSplitCounters * sizeof(unsigned), stream);
+            if (e != hipSuccess) {
+                w->counters = nullptr;
+                return e;
+            }
+            e = fm::launch_zero_u32(w->counters, fm::kSplitCounters, stream);
+            if (e != hipSuccess) return e;
+        }
+        *counters = w->counters;
     }
     *out = w->ptr;
     return hipSuccess;
@@ -141,6 +158,11 @@ FM_API int fm_set_option(int option, int64_t value) {
     if (option == FM_OPT_SINGLE_LAUNCH) {
         if (value != 0 && value != 1) return FM_ERR_INVALID_ARG;
         g_single_launch = (int)value;
+        return FM_OK;
+    }
+    if (option == FM_OPT_SPLIT_KEYS) {
+        if (value != 0 && value != 1) return FM_ERR_INVALID_ARG;
+        g_split_keys = (int)value;
         return FM_OK;
     }
     if (option == FM_OPT_BWD_SPLIT_CHUNKS) {
@@ -275,10 +297,11 @@ int fwd_check(const fm::FwdArgs& a) {
 int attn_fwd_impl(const fm::FwdArgs& a) {
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
-    const fm::FwdPlan p = fm::fwd_plan(a);
+    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1);
     void* ws = nullptr;
+    unsigned* counters = nullptr;
     std::unique_lock<std::mutex> ws_hold;       // held until the launches below are queued
-    FM_HIP(get_workspace(a.stream, p.total(), &ws, ws_hold));
+    FM_HIP(get_workspace(a.stream, p.total(), &ws, ws_hold, p.split > 1 ? &counters : nullptr));
     std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
     {
         std::lock_guard<std::mutex> lock(g_timing.mu);
@@ -292,7 +315,7 @@ int attn_fwd_impl(const fm::FwdArgs& a) {
             }
         }
     }
-    const hipError_t e = fm::fwd_launch(a, p, ws, g_schedule_mode == 1, g_single_launch == 1, ev.first, ev.second);
+    const hipError_t e = fm::fwd_launch(a, p, ws, counters, g_schedule_mode == 1, ev.first, ev.second);
     const int r = e == hipSuccess ? FM_OK : hip_fail(e);
     if (ev.first != nullptr) {
         std::lock_guard<std::mutex> lock(g_timing.mu);
@@ -385,11 +408,12 @@ FM_API int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, cons
     const fm::FwdArgs a = fwd_args(q, k, v, col_start, col_end, n_ranges, B, H, N, d, scale, out, lse, stream);
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
-    const fm::FwdPlan p = fm::fwd_plan(a);
+    // (no split key ranges here: they need arrival counters that start at zero)
+    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, false);
     if (p.total() > (size_t)FM_NOALLOC_SCRATCH_BYTES) return FM_ERR_TOO_LARGE;
     void* ws = nullptr;
     FM_HIP(scratch_address(&ws));
-    FM_HIP(fm::fwd_launch(a, p, ws, g_schedule_mode == 1, g_single_launch == 1, nullptr, nullptr));
+    FM_HIP(fm::fwd_launch(a, p, ws, nullptr, g_schedule_mode == 1, nullptr, nullptr));
     return FM_OK;
 }
 

@@ -507,7 +507,8 @@ __device__ __forceinline__ void score8_direct(floatx16 (&st)[kBc / 32], const v8
 }
 
 // Types of one instantiation: PREC 0 bf16 inputs; 1 e4m3 inputs (V widened to
-// bf16, bf16 weights); 2 e4m3 inputs and e4m3 weights.
+// bf16, bf16 weights); 2 e4m3 inputs and e4m3 weights; 3 bf16 inputs of a
+// single launch, whose key ranges may be split over several workgroups.
 template <int D, int NIV, int PREC>
 struct FwdTypes {
     using In = uint16_t;
@@ -524,6 +525,9 @@ struct FwdTypes8 {
 };
 template <int D, int NIV>
 struct FwdTypes<D, NIV, 1> : FwdTypes8<D, NIV> {};
+// bf16 inputs launched alone (no records), key ranges possibly split.
+template <int D, int NIV>
+struct FwdTypes<D, NIV, 3> : FwdTypes<D, NIV, 0> {};
 template <int D, int NIV>
 struct FwdTypes<D, NIV, 2> : FwdTypes8<D, NIV> {};
 
@@ -534,17 +538,20 @@ struct FwdTypes<D, NIV, 2> : FwdTypes8<D, NIV> {};
 // Two workgroups per CU in bf16; the e4m3 kernels' smaller K/V buffers and
 // register sets leave room for three, which the register limit keeps.
 template <int D, int NIV, int PREC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PREC != 0 ? 3 : 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PREC == 1 || PREC == 2 ? 3 : 2)))
 void attn_fwd_kernel(
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ Q,
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ K,
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ V, const int32_t* __restrict__ col_start,
     const int32_t* __restrict__ col_end, const TileMeta* __restrict__ meta, const int32_t* __restrict__ order,
     int H, int N, int n_q, float c, float v_scale, int xcd_heads, int per_head, uint16_t* __restrict__ O,
-    float* __restrict__ LSE) {
+    float* __restrict__ LSE, int split_arg, float* __restrict__ part, unsigned* __restrict__ counters) {
     using T = FwdTypes<D, NIV, PREC>;
-    constexpr bool F8 = PREC != 0;       // e4m3 inputs
-    constexpr bool W8 = PREC == 2;       // e4m3 weights
+    constexpr bool F8 = PREC == 1 || PREC == 2;   // e4m3 inputs
+    constexpr bool W8 = PREC == 2;                // e4m3 weights
+    // Only the single-launch instance (PREC 3) splits key ranges; in the
+    // others split is the constant 1 and its code folds away.
+    const int split = PREC == 3 ? split_arg : 1;
     constexpr float kW8Shift = W8 ? 8.f : 0.f;   // log2 of the weights' scale
     constexpr int kElt = (int)sizeof(typename T::In);   // bytes per Q/K/V element
     __shared__ typename T::Shared sm;
@@ -562,19 +569,25 @@ void attn_fwd_kernel(
     // and so on: the workgroups resident on one XCD stream one head's K/V
     // nearly in lockstep and share it through that XCD's L2.  Otherwise the
     // heads of one query block are adjacent in launch order.
+    // With the key ranges split (split > 1: small bf16 problems launched
+    // alone), workgroup blockIdx.x takes piece `piece` of the key blocks of
+    // work item `item`; the last of an item's pieces to finish combines them.
+    const unsigned n_items = split == 1 ? gridDim.x : gridDim.x / (unsigned)split;
+    const int piece = split == 1 ? 0 : (int)(blockIdx.x / n_items);
+    const unsigned item = blockIdx.x - (unsigned)piece * n_items;
     int h, q_item;
     if (xcd_heads) {
-        const int s = blockIdx.x >> 3;
-        const int M = gridDim.x / H;            // query blocks per head
-        h = (blockIdx.x & 7) + 8 * (s / M);
+        const int s = item >> 3;
+        const int M = n_items / H;              // query blocks per head
+        h = (item & 7) + 8 * (s / M);
         q_item = s % M;
     } else {
-        h = blockIdx.x % H;
-        q_item = blockIdx.x / H;
+        h = item % H;
+        q_item = item / H;
     }
     // With one interval set per head, head h reads set h: its items are the
     // segment [h L, h L + L) of the preprocessor's records and of the order.
-    const int L = gridDim.x / H;                 // query blocks per head (B n_q)
+    const int L = n_items / H;                   // query blocks per head (B n_q)
     const int set = per_head ? h : 0;
     const int n_sets = per_head ? H : 1;
     const int bt = order != nullptr ? order[set * L + q_item] : set * L + q_item;
@@ -711,8 +724,18 @@ void attn_fwd_kernel(
     }
 
     // Key blocks in increasing order over the union of the ranges' non-skip
-    // blocks (one contiguous run for a single range).
+    // blocks (one contiguous run for a single range).  A piece of a split
+    // item takes the union's blocks [lo, hi) by position, lo = piece * n / split.
     int j = union_next<NIV>(tm, -1);
+    int left = INT_MAX;                           // blocks this workgroup still computes
+    if (split > 1) {
+        int n = 0;
+        for (int x = j; x != INT_MAX; x = union_next<NIV>(tm, x)) ++n;
+        const int lo = piece * n / split, hi = (piece + 1) * n / split;
+        for (int s = 0; s < lo; ++s) j = union_next<NIV>(tm, j);
+        left = hi - lo;
+        if (left == 0) j = INT_MAX;
+    }
     if (j != INT_MAX) {
         if constexpr (F8) {
             load_block8_direct<D>(sm, 0, krs, vrs, dvoff8, j * kBc, wave_u);
@@ -725,7 +748,7 @@ void attn_fwd_kernel(
 
         for (int buf = 0;; buf ^= 1) {
             const int j_next = union_next<NIV>(tm, j);
-            const bool has_next = j_next != INT_MAX;
+            const bool has_next = j_next != INT_MAX && (split == 1 || --left > 0);
             if (has_next) {
                 if constexpr (F8)
                     load_block8_direct<D>(sm, buf ^ 1, krs, vrs, dvoff8, j_next * kBc, wave_u);
@@ -882,6 +905,63 @@ void attn_fwd_kernel(
         }
     }
 
+    // ---- split key ranges: every piece stores its running state (the
+    // unnormalised accumulators, the reference maximum and both sums, per
+    // lane); the last piece of the item to arrive reads them all back and
+    // combines them against the largest reference,
+    //     O_acc = sum_p 2^(m_p - m) O_acc,p,  l = sum_p 2^(m_p - m) l_p,
+    // which is the state one workgroup would have reached over all the
+    // blocks (up to the order of the fp32 additions).  The arrival count is
+    // reset by that last piece, so it is zero again for the next call.
+    if constexpr (!F8) {
+        if (split > 1) {
+            constexpr int kAcc = D / 32 * 16;                 // accumulator floats per lane
+            constexpr int kChunks = kAcc / 4 + 1;             // float4 chunks per lane (last: m, l, l16)
+            float4* const mine = reinterpret_cast<float4*>(part) + ((int64_t)item * split + piece) * kChunks * kThreads;
+#pragma unroll
+            for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    mine[(nb * 4 + g) * kThreads + tid] =
+                        make_float4(oacc[nb][4 * g], oacc[nb][4 * g + 1], oacc[nb][4 * g + 2], oacc[nb][4 * g + 3]);
+            mine[(kChunks - 1) * kThreads + tid] = make_float4(m_run, l_run, l16_run, 0.f);
+            __threadfence();                                  // the state is visible before the arrival counts
+            __syncthreads();
+            int* const arrived = &sm.start[0][0];             // the intervals are in registers by now
+            if (tid == 0) *arrived = (int)atomicAdd(&counters[item], 1u);
+            __syncthreads();
+            if (*arrived != split - 1) return;                // another piece finishes the item
+            __threadfence();                                  // every piece's state is visible
+            if (tid == 0) counters[item] = 0u;
+            const float4* const all = reinterpret_cast<const float4*>(part) + (int64_t)item * split * kChunks * kThreads;
+            // Two passes: the largest reference, then the weighted sums (the
+            // pieces' loads are independent of one another, so they overlap).
+            float m = -INFINITY;
+            for (int pc = 0; pc < split; ++pc) m = fmaxf(m, all[(pc * kChunks + kChunks - 1) * kThreads + tid].x);
+#pragma unroll
+            for (int nb = 0; nb < D / 32; ++nb) oacc[nb] = floatx16{};
+            l_run = 0.f;
+            l16_run = 0.f;
+            for (int pc = 0; pc < split; ++pc) {
+                const float4 st = all[(pc * kChunks + kChunks - 1) * kThreads + tid];
+                const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.x - m);
+                l_run = fmaf(w, st.y, l_run);
+                l16_run = fmaf(w, st.z, l16_run);
+#pragma unroll
+                for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 x = all[(pc * kChunks + nb * 4 + g) * kThreads + tid];
+                        oacc[nb][4 * g] = fmaf(w, x.x, oacc[nb][4 * g]);
+                        oacc[nb][4 * g + 1] = fmaf(w, x.y, oacc[nb][4 * g + 1]);
+                        oacc[nb][4 * g + 2] = fmaf(w, x.z, oacc[nb][4 * g + 2]);
+                        oacc[nb][4 * g + 3] = fmaf(w, x.w, oacc[nb][4 * g + 3]);
+                    }
+            }
+            m_run = m;
+        }
+    }
+
     // ---- epilogue: O = O_acc / l16 (bf16, nearest even), LSE = ln(sum) in natural log.
     // O goes out through LDS so that every store writes whole rows: each
     // wavefront stages its rows in its own part of the K/V buffers, idle now
@@ -933,7 +1013,9 @@ void attn_fwd_kernel(
             if (grow < N) *reinterpret_cast<u32x4*>(obh + (int64_t)grow * (2 * D) + cb) = v;
         }
     }
-    if (qrow < N && half == 0) LSE[bh * N + qrow] = l > 0.f ? (m_run - kW8Shift) * kLn2 + logf(l) : -INFINITY;
+    // (one fused multiply-add, written out: left to the compiler, the
+    // contraction differs between instances and so would the last bit)
+    if (qrow < N && half == 0) LSE[bh * N + qrow] = l > 0.f ? fmaf(m_run - kW8Shift, kLn2, logf(l)) : -INFINITY;
 }
 
 }  // namespace
@@ -942,10 +1024,15 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                            const float* fp8_scales, int n_sets, bool fp8_weights) {
+                            const float* fp8_scales, int n_sets, bool fp8_weights, int split, float* part,
+                            unsigned* counters) {
     const int64_t n_q = (N + kBr - 1) / kBr;
-    const int64_t grid = B * H * n_q;
     const bool f8 = fp8_scales != nullptr;
+    // Split key ranges only for bf16 launches without records.
+    if (split < 1 || (split & (split - 1)) != 0 ||
+        (split > 1 && (f8 || meta != nullptr || part == nullptr || counters == nullptr)))
+        return hipErrorInvalidValue;
+    const int64_t grid = B * H * n_q * split;
     const float c = (f8 ? scale * fp8_scales[0] * fp8_scales[1] : scale) * kLog2e;
     const float v_scale = f8 ? fp8_scales[2] : 1.f;
     auto* Op = static_cast<uint16_t*>(out);
@@ -964,15 +1051,16 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                                       : (d == 128 ? attn_fwd_kernel<128, NIV, 1> : attn_fwd_kernel<64, NIV, 1>);
             hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
-                                  xcd_heads, n_sets > 1 ? 1 : 0, Op, lse);
+                                  xcd_heads, n_sets > 1 ? 1 : 0, Op, lse, 1, nullptr, nullptr);
         } else {
             const auto* Qp = static_cast<const uint16_t*>(q);
             const auto* Kp = static_cast<const uint16_t*>(k);
             const auto* Vp = static_cast<const uint16_t*>(v);
-            auto kernel = d == 128 ? attn_fwd_kernel<128, NIV, 0> : attn_fwd_kernel<64, NIV, 0>;
+            auto kernel = meta == nullptr ? (d == 128 ? attn_fwd_kernel<128, NIV, 3> : attn_fwd_kernel<64, NIV, 3>)
+                                          : (d == 128 ? attn_fwd_kernel<128, NIV, 0> : attn_fwd_kernel<64, NIV, 0>);
             hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
-                                  xcd_heads, n_sets > 1 ? 1 : 0, Op, lse);
+                                  xcd_heads, n_sets > 1 ? 1 : 0, Op, lse, split, part, counters);
         }
         return hipGetLastError();
     });

@@ -92,7 +92,8 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                            const float* fp8_scales = nullptr, int n_sets = 1, bool fp8_weights = false);
+                            const float* fp8_scales = nullptr, int n_sets = 1, bool fp8_weights = false,
+                            int split = 1, float* part = nullptr, unsigned* counters = nullptr);
 
 // The forward pass's launch sequence (fm_forward.hip).
 struct FwdArgs {
@@ -114,20 +115,44 @@ struct FwdArgs {
 struct FwdPlan {
     int64_t n_q, n_kv, n_sets, M;
     size_t meta_bytes, int_bytes, sched_bytes;
-    size_t total() const { return meta_bytes + 2 * int_bytes + sched_bytes; }
+    bool single;               // the attention kernel alone (no records, no order)
+    int split;                 // pieces per work item's key range (single launches only; 1: none)
+    size_t part_bytes;         // the pieces' partial states
+    size_t total() const { return single ? part_bytes : meta_bytes + 2 * int_bytes + sched_bytes; }
 };
-FwdPlan fwd_plan(const FwdArgs& a);
+
+// Splitting the key ranges of small single launches: a power of two of pieces
+// per work item, at most kMaxSplit, at most kSingleLaunchGrid workgroups in
+// all, and at least kSplitMinBlocks key blocks per piece of the longest
+// possible range (cross-workgroup combining costs a few block times, so short
+// ranges are not split); the partial states take kFwdThreads lanes of d/2 + 4
+// floats per piece.
+constexpr int kMaxSplit = 8;
+constexpr int kSplitMinBlocks = 8;
+constexpr int kFwdThreads = 256;
+// Arrival counters of split items: one per work item of a single launch,
+// zero between calls.
+constexpr int kSplitCounters = 256;
+inline size_t split_part_bytes(int64_t items, int64_t split, int64_t d) {
+    return (size_t)(items * split * kFwdThreads) * (size_t)(d / 2 + 4) * sizeof(float);
+}
+FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys);
 
 // Queues the preprocessor, the scheduler (unless natural order) and the
 // attention kernel on a.stream, with ws (p.total() bytes of device memory) as
 // their workspace.  Every byte of ws that a kernel reads was written earlier
-// in the same sequence, so ws needs no clearing.  With single_launch, a bf16
-// grid of at most kSingleLaunchGrid workgroups (all resident at once, so their
+// in the same sequence, so ws needs no clearing.  With p.single, a bf16 grid
+// of at most kSingleLaunchGrid workgroups (all resident at once, so their
 // order cannot matter) runs the attention kernel alone: each workgroup
-// reduces its own query block's key range from the intervals it stages.
+// reduces its own query block's key range from the intervals it stages; with
+// p.split > 1 each range is cut into p.split pieces whose partial states go
+// to ws, and `counters` (kSplitCounters zeros, left zero again) counts their
+// arrivals.
 constexpr int64_t kSingleLaunchGrid = 256;
-hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, bool natural, bool single_launch,
+hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, unsigned* counters, bool natural,
                       hipEvent_t ev_start, hipEvent_t ev_stop);
+// Fills n counters with zeros on stream (a kernel: no memset node in a graph).
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream);
 
 // Backward pass (gradients of Q, K, V).  Shapes: the key-block kernel runs
 // kBwdKeys keys per workgroup against query chunks of kBwdRows rows; the

@@ -21,6 +21,7 @@ FM_TILE_SKIP, FM_TILE_FULL, FM_TILE_PARTIAL = 0, 1, 2
 FM_OPT_SCHEDULE = 1
 FM_OPT_BWD_SPLIT_CHUNKS = 2
 FM_OPT_SINGLE_LAUNCH = 3
+FM_OPT_SPLIT_KEYS = 4
 FM_MAX_RANGES = 4
 FM_FP8_SCORES, FM_FP8_ALL = 0, 1
 

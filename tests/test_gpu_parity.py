@@ -408,11 +408,58 @@ def test_single_launch_equals_preprocessed_launch(kind):
         call = lambda qd, kd, vd, sd, ed: fm.fm_attn_fwd_per_head(qd, kd, vd, sd, ed, scale)
     args = to_dev(q, k, v, np.ascontiguousarray(s), np.ascontiguousarray(e))
     log(f"single launch vs preprocessed launch: {kind}")
-    o1, l1 = call(*args)
     try:
+        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 0)       # one workgroup per query block
+        o1, l1 = call(*args)
         fm.fm_set_option(fm.FM_OPT_SINGLE_LAUNCH, 0)
         o2, l2 = call(*args)
     finally:
         fm.fm_set_option(fm.FM_OPT_SINGLE_LAUNCH, 1)
+        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+SPLIT_CASES = [
+    # (B, H, N, d, kind): single launches (at most 256 workgroups) whose key ranges are cut
+    # into a power of two of pieces, at most 8 and at most 256 workgroups in all, each of
+    # at least 8 key blocks of the longest possible range.  Pieces per query block:
+    (1, 2, 1024, 64, "causal"),         # 2 (16 key blocks)
+    (1, 1, 1000, 128, "random_empty"),  # 2; ragged tail, empty rows, pieces with no key block
+    (2, 3, 1777, 64, "docs"),           # 2; 84 query blocks
+    (1, 4, 2048, 128, "prefix"),        # 4
+    (1, 1, 4096, 128, "causal"),        # 8
+    (1, 1, 1100, 64, "sliding"),        # 2; most pieces of a window hold no key block
+    (1, 2, 512, 64, "causal"),          # C1's shape: 8 key blocks, not split
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_split_key_ranges(case):
+    """Split single launches: against the oracle to the usual bars, against the unsplit launch
+    to fp32 rounding (the pieces' states are combined exactly up to the order of additions),
+    and the same bits on a repeated call (the arrival counters are left at zero)."""
+    B, H, N, d, kind = case
+    rng = np.random.default_rng(N + d + H)
+    s, e = small_intervals(kind, B, N, rng)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=N + 3)
+    scale = inputs.default_scale(d)
+    log(f"split key ranges {case}")
+    check_case(q, k, v, s, e, scale, f"split {case}")
+    args = to_dev(q, k, v, np.ascontiguousarray(s), np.ascontiguousarray(e))
+    o1, l1 = fm.fm_attn_fwd(*args, scale)
+    o2, l2 = fm.fm_attn_fwd(*args, scale)
+    try:
+        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 0)
+        o3, l3 = fm.fm_attn_fwd(*args, scale)
+    finally:
+        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "a repeated split call changed its result"
+    dO = (o1.float() - o3.float()).abs().max().item()
+    fin = torch.isfinite(l3)
+    assert torch.equal(fin, torch.isfinite(l1)), "split and unsplit disagree on empty rows"
+    dL = (l1[fin] - l3[fin]).abs().max().item() if fin.any() else 0.0
+    log(f"  split vs unsplit: max|dO| {dO:.3e} (bf16 output), max|dLSE| {dL:.3e}")
+    # at most one bf16 ulp of the output (a different fp32 sum can round the other way)
+    assert dO <= 2 ** -7 * max(1.0, o3.float().abs().max().item()) and dL <= 1e-5
