@@ -269,6 +269,29 @@ __device__ __forceinline__ int4 wave_row_bounds(int s, int w, bool in_seq) {
                      wave_min(any ? s + w : (in_seq ? INT_MIN : INT_MAX)));
 }
 
+// Minimum or maximum over the wavefront with DPP moves (VALU latency, where
+// the swizzle butterfly makes five LDS round trips): the quad permutations
+// [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors, reduce each row
+// of 16 lanes; the four rows are combined from lanes 0, 16, 32 and 48.
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_dpp(int v) {
+    auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
+    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
+    return op(op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+              op(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// wave_row_bounds for the per-chunk test of the dK/dV kernels.
+__device__ __forceinline__ int4 wave_row_bounds_dpp(int s, int w, bool in_seq) {
+    const bool any = s != kEmptyStart;
+    return make_int4(wave_reduce_dpp<false>(any ? s : INT_MAX), wave_reduce_dpp<true>(any ? s + w : INT_MIN),
+                     wave_reduce_dpp<true>(any ? s : (in_seq ? INT_MAX : INT_MIN)),
+                     wave_reduce_dpp<false>(any ? s + w : (in_seq ? INT_MIN : INT_MAX)));
+}
+
 // Blocks of 64 rows (keys for dQ, query rows for dK/dV) loaded straight from
 // global memory into LDS (buffer loads with an LDS destination: one
 // instruction writes lane l's 16 bytes to M0 + 16 l, a 1 KB segment per
@@ -571,11 +594,13 @@ struct alignas(16) DkvSmem {
 };
 
 // Per-row values of a chunk staged through registers (Q and dO go straight
-// into LDS).
+// into LDS), as loaded: they are scaled and clamped only when stored, at the
+// end of the step, so that no wait for them (which would also wait for the
+// chunk's LDS loads issued before them) falls inside the step.
 template <int D, int NIV>
 struct DkvStage {
-    float lse2, dd;
-    int s[NIV], w[NIV];
+    float lse, dd;
+    int cs[NIV], ce[NIV];
 };
 
 // Chunk starting at row0 into buffer buf: Q and dO straight into LDS (loff:
@@ -590,49 +615,136 @@ __device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, DkvSmem<D, NIV>& 
     dma_rows<D, true>(&sm.go[buf][0], grs, loff, row0, wave_u);
     if (tid < kBwdRows) {
         const int row = row0 + tid;
+        st.lse = 0.f;
+        st.dd = 0.f;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) st.cs[k] = st.ce[k] = 0;
         if (row < N) {
-            st.lse2 = lse_bh[row] * kLog2e;
+            st.lse = lse_bh[row];
             st.dd = dd_bh[row];
 #pragma unroll
             for (int k = 0; k < NIV; ++k) {
-                const int2 iv = clamp_interval(cs_b[(int64_t)k * N + row], ce_b[(int64_t)k * N + row], N);
-                st.s[k] = iv.x;
-                st.w[k] = iv.y;
-            }
-        } else {
-            st.lse2 = INFINITY;                // P = 0 for rows past N
-            st.dd = 0.f;
-#pragma unroll
-            for (int k = 0; k < NIV; ++k) {
-                st.s[k] = kEmptyStart;
-                st.w[k] = 0;
+                st.cs[k] = cs_b[(int64_t)k * N + row];
+                st.ce[k] = ce_b[(int64_t)k * N + row];
             }
         }
     }
 }
 
 template <int D, int NIV>
-__device__ __forceinline__ void dkv_store(const DkvStage<D, NIV>& st, DkvSmem<D, NIV>& sm, int buf, int tid) {
+__device__ __forceinline__ void dkv_store(const DkvStage<D, NIV>& st, DkvSmem<D, NIV>& sm, int buf, int row0, int N,
+                                          int tid) {
     if (tid < kBwdRows) {
-        sm.lse2[buf][tid] = st.lse2;
-        sm.dd[buf][tid] = st.dd;
+        const bool in = row0 + tid < N;
+        sm.lse2[buf][tid] = in ? st.lse * kLog2e : INFINITY;   // P = 0 for rows past N
+        sm.dd[buf][tid] = in ? st.dd : 0.f;
 #pragma unroll
         for (int k = 0; k < NIV; ++k) {
-            sm.start[buf][k][tid] = st.s[k];
-            sm.width[buf][k][tid] = st.w[k];
+            const int2 iv = in ? clamp_interval(st.cs[k], st.ce[k], N) : make_int2(kEmptyStart, 0);
+            sm.start[buf][k][tid] = iv.x;
+            sm.width[buf][k][tid] = iv.y;
         }
     }
 }
 
+// Records of chunk c (one per range) for key block J: live if some range's
+// non-skip blocks [x, y] hold J, full if some range covers J for every row of
+// the chunk (its blocks [z, w]).
 template <int NIV>
-__device__ __forceinline__ bool chunk_live(const TileMeta* __restrict__ meta_c, int64_t base, int J) {
-    bool live = false;
+__device__ __forceinline__ void chunk_state(const TileMeta (&m)[NIV], int J, bool& live, bool& full) {
+    live = full = false;
 #pragma unroll
     for (int k = 0; k < NIV; ++k) {
-        const TileMeta m = meta_c[base * NIV + k];
-        live |= m.x <= J && J <= m.y;
+        live |= m[k].x <= J && J <= m[k].y;
+        full |= m[k].z <= J && J <= m[k].w;
     }
-    return live;
+}
+
+// First live chunk >= c (INT_MAX if none up to last), searched synchronously;
+// full: its full flag.
+template <int NIV>
+__device__ __forceinline__ int next_live_chunk(const TileMeta* __restrict__ meta_c, int64_t meta_row, int J, int c,
+                                               int last, bool& full) {
+    full = false;
+    for (; c <= last; ++c) {
+        TileMeta m[NIV];
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) m[k] = meta_c[(meta_row + c) * NIV + k];
+        bool live, f;
+        chunk_state<NIV>(m, J, live, f);
+        if (live) {
+            full = f;
+            return c;
+        }
+    }
+    return INT_MAX;
+}
+
+// The records of one candidate chunk, loaded a step ahead: issued at the top
+// of a step and tested at its end, where the wait for that step's own loads
+// already is, so that finding the chunk after next costs no exposed load.
+template <int NIV>
+struct ChunkProbe {
+    TileMeta m[NIV];
+    int cand;
+};
+template <int NIV>
+__device__ __forceinline__ void probe_issue(ChunkProbe<NIV>& pr, const TileMeta* __restrict__ meta_c,
+                                            int64_t meta_row, int cand, int last) {
+    pr.cand = cand;
+    if (cand <= last) {
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) pr.m[k] = meta_c[(meta_row + cand) * NIV + k];
+    }
+}
+template <int NIV>
+__device__ __forceinline__ int probe_resolve(const ChunkProbe<NIV>& pr, const TileMeta* __restrict__ meta_c,
+                                             int64_t meta_row, int J, int last, bool& full) {
+    full = false;
+    if (pr.cand > last) return INT_MAX;
+    bool live, f;
+    chunk_state<NIV>(pr.m, J, live, f);
+    if (live) {
+        full = f;
+        return pr.cand;
+    }
+    return next_live_chunk<NIV>(meta_c, meta_row, J, pr.cand + 1, last, full);
+}
+
+// Per-row values of the weights, read as inline assembly like the operands:
+// ordinary LDS reads here would make the compiler first wait for the next
+// chunk's loads into LDS, which are meant to run until the end of the step.
+// LSE and D of queries 32 QB + 8 g + 4 half .. +3 (bases: this lane's element
+// 4 half of the row arrays), issued LSE g, D g in order of g.
+template <int QB, int G = 0>
+__device__ __forceinline__ void row_vals_issue(u32x4 (&lr)[4], u32x4 (&dr)[4], uint32_t lbase, uint32_t dbase) {
+    if constexpr (G < 4) {
+        lr[G] = lds_read_b128<(QB * 32 + 8 * G) * 4>(lbase);
+        dr[G] = lds_read_b128<(QB * 32 + 8 * G) * 4>(dbase);
+        row_vals_issue<QB, G + 1>(lr, dr, lbase, dbase);
+    }
+}
+__device__ __forceinline__ void row_vals_wait(u32x4 (&lr)[4], u32x4 (&dr)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(lr[0]), "+v"(lr[1]), "+v"(lr[2]), "+v"(lr[3]), "+v"(dr[0]), "+v"(dr[1]), "+v"(dr[2]),
+                   "+v"(dr[3]));
+}
+// Start and width of the same four queries in every range (range k at
+// k kBwdRows entries), waited for at once.
+template <int NIV, int OFF, int K = 0>
+__device__ __forceinline__ void range_rows_read(u32x4 (&sr)[NIV], u32x4 (&wr)[NIV], uint32_t sbase,
+                                                uint32_t wbase) {
+    if constexpr (K < NIV) {
+        sr[K] = lds_read_b128<OFF + K * kBwdRows * 4>(sbase);
+        wr[K] = lds_read_b128<OFF + K * kBwdRows * 4>(wbase);
+        range_rows_read<NIV, OFF, K + 1>(sr, wr, sbase, wbase);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            wait_lds_one<0>(sr[k]);
+            wait_lds_one<0>(wr[k]);
+        }
+    }
 }
 
 template <int D, int NIV>
@@ -712,36 +824,44 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                        8 * (lane & 3);
 
     // The first live chunk of the piece's range.
-    int t = piece.y;
-    while (t <= piece.z && !chunk_live<NIV>(meta_c, meta_row + t, J)) ++t;
-    if (t > piece.z) t = INT_MAX;
+    bool full_t, full_next;
+    int t = next_live_chunk<NIV>(meta_c, meta_row, J, piece.y, piece.z, full_t);
     if (t != INT_MAX) {
+        int t_next = next_live_chunk<NIV>(meta_c, meta_row, J, t + 1, piece.z, full_next);
         DkvStage<D, NIV> stage;
         dkv_load<D, NIV>(stage, sm, 0, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b, t * kBwdRows, N, tid);
-        dkv_store<D, NIV>(stage, sm, 0, tid);
+        dkv_store<D, NIV>(stage, sm, 0, t * kBwdRows, N, tid);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int buf = 0;; buf ^= 1) {
-            int t_next = t + 1;
-            while (t_next <= piece.z && !chunk_live<NIV>(meta_c, meta_row + t_next, J)) ++t_next;
-            const bool has_next = t_next <= piece.z;
-            if (has_next)
+            const bool has_next = t_next != INT_MAX;
+            ChunkProbe<NIV> probe;
+            if (has_next) {
                 dkv_load<D, NIV>(stage, sm, buf ^ 1, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b,
                                  t_next * kBwdRows, N, tid);
+                probe_issue<NIV>(probe, meta_c, meta_row, t_next + 1, piece.z);
+            }
 
             // Does some row of the chunk attend the wavefront's keys, and does
-            // one range cover them for every row?  Lane l looks at row l.
-            const int row0 = t * kBwdRows;
+            // one range cover them for every row?  Where one range covers the
+            // whole key block for every row (the chunk's records), every
+            // wavefront is FULL; otherwise lane l looks at row l.
             const int klo = kw0;
-            const int khi = min(kw0 + 31, N - 1);
-            bool wave_skip = true, wave_full = false;
+            bool wave_skip = klo >= N, wave_full = true;   // every key of the wavefront past N: skip
+            if (!full_t) {
+                const int row0 = t * kBwdRows;
+                const int khi = min(kw0 + 31, N - 1);
+                bool skip = true, full = false;
 #pragma unroll
-            for (int k = 0; k < NIV; ++k) {
-                const int4 rb = wave_row_bounds(sm.start[buf][k][lane], sm.width[buf][k][lane], row0 + lane < N);
-                wave_skip &= khi < rb.x || klo > rb.y;
-                wave_full |= klo >= rb.z && khi <= rb.w;
+                for (int k = 0; k < NIV; ++k) {
+                    const int4 rb =
+                        wave_row_bounds_dpp(sm.start[buf][k][lane], sm.width[buf][k][lane], row0 + lane < N);
+                    skip &= khi < rb.x || klo > rb.y;
+                    full |= klo >= rb.z && khi <= rb.w;
+                }
+                wave_skip |= skip;
+                wave_full = full;
             }
-            wave_skip |= klo >= N;               // every key of the wavefront lies past N
             if (!wave_skip) {
                 // The chunk in two halves of 32 queries, each taken through S, dP,
                 // the weights and its share of the dV / dK products before the
@@ -752,6 +872,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     constexpr int qb = decltype(qbc)::value;
                     constexpr bool kFull = decltype(fullc)::value;   // one range covers every row's keys
                     // ---- S = Q K^T, dP = dO V^T: lane holds [query 32 qb + 8 (v/4) + 4 half + v%4][key]
+                    // the half's LSE and D, issued first: the operand reads'
+                    // waits below also see them complete
+                    u32x4 lr[4], dr[4];
+                    row_vals_issue<qb>(lr, dr, lds_address(&sm.lse2[buf][4 * half]),
+                                       lds_address(&sm.dd[buf][4 * half]));
                     floatx16 s1 = {}, dp1 = {};
                     {
                         const uint32_t qrow = lds_address(&sm.q[buf][0]) + q_lane;
@@ -760,27 +885,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                         sdp_issue<D, qb>(ring, qrow, grow);
                         sdp_products<D, qb>(s1, dp1, kreg, vreg, qrow, grow, ring);
                     }
+                    row_vals_wait(lr, dr);
                     // transposing reads of the half's first product step, issued
                     // now so that their latency overlaps the weights
                     v4s gpart[2 * D / 32], qpart[2 * D / 32];
                     issue_kt_reads<D, 2 * qb>(gpart, gaddr);
                     issue_kt_reads<D, 2 * qb>(qpart, qaddr);
                     // ---- P = exp(scale s - LSE) inside the ranges, dS = P (dP - D)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int qi = qb * 32 + 8 * g + 4 * half;     // four consecutive queries
-                        const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[buf][qi]);
-                        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[buf][qi]);
+                    const uint32_t sbase = lds_address(&sm.start[buf][0][4 * half]);
+                    const uint32_t wbase = lds_address(&sm.width[buf][0][4 * half]);
+                    auto weights = [&](auto gc) {
+                        constexpr int g = decltype(gc)::value;
+                        const float4 l4 = __builtin_bit_cast(float4, lr[g]);
+                        const float4 d4 = __builtin_bit_cast(float4, dr[g]);
                         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
                         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
                         bool ok[4] = {true, true, true, true};
                         if constexpr (!kFull) {
 #pragma unroll
                             for (int q = 0; q < 4; ++q) ok[q] = false;
+                            u32x4 sr[NIV], wr[NIV];
+                            range_rows_read<NIV, (qb * 32 + 8 * g) * 4>(sr, wr, sbase, wbase);
 #pragma unroll
                             for (int k = 0; k < NIV; ++k) {
-                                const int4 s4 = *reinterpret_cast<const int4*>(&sm.start[buf][k][qi]);
-                                const int4 w4 = *reinterpret_cast<const int4*>(&sm.width[buf][k][qi]);
+                                const int4 s4 = __builtin_bit_cast(int4, sr[k]);
+                                const int4 w4 = __builtin_bit_cast(int4, wr[k]);
                                 ok[0] |= (uint32_t)(key - s4.x) <= (uint32_t)w4.x;
                                 ok[1] |= (uint32_t)(key - s4.y) <= (uint32_t)w4.y;
                                 ok[2] |= (uint32_t)(key - s4.z) <= (uint32_t)w4.z;
@@ -795,7 +924,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                             s1[v] = pm;
                             dp1[v] = pm * (dp1[v] - dv4[q]);
                         }
-                    }
+                    };
+                    weights(std::integral_constant<int, 0>{});
+                    weights(std::integral_constant<int, 1>{});
+                    weights(std::integral_constant<int, 2>{});
+                    weights(std::integral_constant<int, 3>{});
                     // ---- dV^T += dO^T P, dK^T += Q^T dS over the half's 32 queries
                     dkv_products_half<D, 2 * qb, 2 * qb + 2>(s1, dp1, dvacc, dkacc, gaddr, qaddr, gpart, qpart);
                 };
@@ -808,13 +941,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     chunk_half(std::integral_constant<int, 1>{}, std::false_type{});
                 }
             }
+            int t_after = INT_MAX;
+            bool full_after = false;
             if (has_next) {
-                dkv_store<D, NIV>(stage, sm, buf ^ 1, tid);
+                dkv_store<D, NIV>(stage, sm, buf ^ 1, t_next * kBwdRows, N, tid);
                 __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
+                t_after = probe_resolve<NIV>(probe, meta_c, meta_row, J, piece.z, full_after);
             }
             __syncthreads();
             if (!has_next) break;
             t = t_next;
+            full_t = full_next;
+            t_next = t_after;
+            full_next = full_after;
         }
     }
 
