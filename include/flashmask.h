@@ -112,8 +112,11 @@ FM_API int fm_attn_fwd(const void* q, const void* k, const void* v,
  * FM_NOALLOC_SCRATCH_BYTES (4 MiB) that each GPU holds until the process ends;
  * one range per row fits up to about 170,000 query blocks of 128 rows
  * (B * ceil(N/128)), four ranges about 58,000.
- *   Arguments, results (bit-identical to fm_attn_fwd_multi's), asynchrony and
- * errors as fm_attn_fwd_multi; FM_ERR_TOO_LARGE (nothing queued) when the
+ *   Arguments, results, asynchrony and errors as fm_attn_fwd_multi.  The
+ * results are bit-identical to fm_attn_fwd_multi's except where that call
+ * splits a small problem's key ranges over several workgroups
+ * (FM_OPT_SPLIT_KEYS), which this one never does: there they differ only by
+ * the order of fp32 additions.  FM_ERR_TOO_LARGE (nothing queued) when the
  * problem needs more scratch than that.  No kernel timing is recorded.
  *   Every call on one GPU uses that GPU's one array, which keeps the last
  * call's contents (nothing in it needs clearing: each call writes what it
@@ -314,11 +317,14 @@ enum {
                                    queues the interval preprocessor and the work ordering first.
                                    Results are identical either way when FM_OPT_SPLIT_KEYS is 0. */
     FM_OPT_SPLIT_KEYS = 4       /* forward, bf16 single launches (above): 1 (default) cuts each query
-                                   block's key range into up to 8 pieces of at least two key blocks,
-                                   run by separate workgroups (at most 256 in all) whose partial
-                                   softmax states the last one to finish combines; 0 never.  The
-                                   results differ from the unsplit ones only by the order of fp32
-                                   additions.  fm_attn_fwd_noalloc never splits. */
+                                   block's long key ranges into pieces.  At d = 128, ranges of at
+                                   least 32 key blocks go first to two groups of four wavefronts in
+                                   each workgroup, combined through LDS; then, up to 8 pieces of at
+                                   least 8 key blocks run in separate workgroups (at most 256 in all)
+                                   whose partial softmax states the last one to finish combines.
+                                   0: neither.  The results differ from the unsplit ones only by the
+                                   order of fp32 additions.  fm_attn_fwd_noalloc uses the groups
+                                   but never splits over workgroups. */
 };
 FM_API int fm_set_option(int option, int64_t value);
 

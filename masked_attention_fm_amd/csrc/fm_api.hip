@@ -297,7 +297,7 @@ int fwd_check(const fm::FwdArgs& a) {
 int attn_fwd_impl(const fm::FwdArgs& a) {
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
-    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1);
+    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1, true);
     void* ws = nullptr;
     unsigned* counters = nullptr;
     std::unique_lock<std::mutex> ws_hold;       // held until the launches below are queued
@@ -409,7 +409,7 @@ FM_API int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, cons
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
     // (no split key ranges here: they need arrival counters that start at zero)
-    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, false);
+    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1, false);
     if (p.total() > (size_t)FM_NOALLOC_SCRATCH_BYTES) return FM_ERR_TOO_LARGE;
     void* ws = nullptr;
     FM_HIP(scratch_address(&ws));

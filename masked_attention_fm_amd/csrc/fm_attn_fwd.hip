@@ -57,6 +57,8 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <type_traits>
+
 #include "fm_internal.h"
 #include "fm_mfma.h"
 
@@ -528,6 +530,29 @@ struct FwdTypes<D, NIV, 1> : FwdTypes8<D, NIV> {};
 // bf16 inputs launched alone (no records), key ranges possibly split.
 template <int D, int NIV>
 struct FwdTypes<D, NIV, 3> : FwdTypes<D, NIV, 0> {};
+// The same with a query block's key blocks shared by two groups of four
+// wavefronts in one workgroup (PREC 4).
+template <int D, int NIV>
+struct FwdTypes<D, NIV, 4> : FwdTypes<D, NIV, 0> {};
+template <int PREC>
+constexpr int kGroups = PREC == 4 ? 2 : 1;
+
+// One group's shared memory: its K/V buffers and staged intervals during the
+// key loop, its running state (d/2 accumulators, the reference maximum and
+// both sums per lane, as float4 chunks) afterwards.
+template <int D, int NIV>
+union alignas(16) GroupShared {
+    Smem<D, NIV> s;
+    float4 state[(D / 8 + 1) * kThreads];
+};
+template <class S>
+__device__ __forceinline__ S& group_smem(S& s) {
+    return s;
+}
+template <int D, int NIV>
+__device__ __forceinline__ Smem<D, NIV>& group_smem(GroupShared<D, NIV>& g) {
+    return g.s;
+}
 template <int D, int NIV>
 struct FwdTypes<D, NIV, 2> : FwdTypes8<D, NIV> {};
 
@@ -538,7 +563,8 @@ struct FwdTypes<D, NIV, 2> : FwdTypes8<D, NIV> {};
 // Two workgroups per CU in bf16; the e4m3 kernels' smaller K/V buffers and
 // register sets leave room for three, which the register limit keeps.
 template <int D, int NIV, int PREC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PREC == 1 || PREC == 2 ? 3 : 2)))
+__global__ __launch_bounds__(kThreads * kGroups<PREC>)
+__attribute__((amdgpu_waves_per_eu(PREC == 1 || PREC == 2 ? 3 : 2)))
 void attn_fwd_kernel(
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ Q,
     const typename FwdTypes<D, NIV, PREC>::In* __restrict__ K,
@@ -549,14 +575,20 @@ void attn_fwd_kernel(
     using T = FwdTypes<D, NIV, PREC>;
     constexpr bool F8 = PREC == 1 || PREC == 2;   // e4m3 inputs
     constexpr bool W8 = PREC == 2;                // e4m3 weights
-    // Only the single-launch instance (PREC 3) splits key ranges; in the
+    // Only the single-launch instances (PREC 3, 4) split key ranges; in the
     // others split is the constant 1 and its code folds away.
-    const int split = PREC == 3 ? split_arg : 1;
+    constexpr int GRP = kGroups<PREC>;
+    const int split = PREC >= 3 ? split_arg : 1;
     constexpr float kW8Shift = W8 ? 8.f : 0.f;   // log2 of the weights' scale
     constexpr int kElt = (int)sizeof(typename T::In);   // bytes per Q/K/V element
-    __shared__ typename T::Shared sm;
+    // With GRP groups, group g (threads 256 g ..) works as a workgroup of its
+    // own on the shared memory smg[g].
+    using Shared = std::conditional_t<(GRP > 1), GroupShared<D, NIV>, typename T::Shared>;
+    __shared__ Shared smg[GRP];
+    const int group = GRP == 1 ? 0 : (int)(threadIdx.x / kThreads);
+    typename T::Shared& sm = group_smem(smg[group]);
 
-    const int tid = threadIdx.x;
+    const int tid = GRP == 1 ? (int)threadIdx.x : (int)(threadIdx.x % kThreads);
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int half = lane >> 5;      // which 32-lane half of the wavefront
@@ -725,30 +757,39 @@ void attn_fwd_kernel(
 
     // Key blocks in increasing order over the union of the ranges' non-skip
     // blocks (one contiguous run for a single range).  A piece of a split
-    // item takes the union's blocks [lo, hi) by position, lo = piece * n / split.
+    // item takes the union's blocks [lo, hi) by position, lo = piece * n /
+    // pieces; the pieces are the workgroups' (split) times their groups'.
+    // Every group of a workgroup takes the same number of steps (a group
+    // past its last block idles through the rest), so that all of them meet
+    // the same barriers.
+    const int pieces = split * GRP;
     int j = union_next<NIV>(tm, -1);
-    int left = INT_MAX;                           // blocks this workgroup still computes
-    if (split > 1) {
+    int left = INT_MAX;                           // blocks this group still computes
+    int steps = 0;                                // GRP > 1: steps every group takes
+    if (pieces > 1) {
         int n = 0;
         for (int x = j; x != INT_MAX; x = union_next<NIV>(tm, x)) ++n;
-        const int lo = piece * n / split, hi = (piece + 1) * n / split;
+        const int my_piece = piece * GRP + group;
+        const int lo = my_piece * n / pieces, hi = (my_piece + 1) * n / pieces;
         for (int s = 0; s < lo; ++s) j = union_next<NIV>(tm, j);
         left = hi - lo;
         if (left == 0) j = INT_MAX;
+        steps = (n + pieces - 1) / pieces;
     }
-    if (j != INT_MAX) {
-        if constexpr (F8) {
-            load_block8_direct<D>(sm, 0, krs, vrs, dvoff8, j * kBc, wave_u);
-            __builtin_amdgcn_s_waitcnt(0);
-        } else {
-            load_block_direct<D>(sm, 0, krs, vrs, dvoff, j * kBc, wave_u);
-            __builtin_amdgcn_s_waitcnt(0);
+    if (GRP > 1 ? steps > 0 : j != INT_MAX) {
+        if (GRP == 1 || j != INT_MAX) {
+            if constexpr (F8)
+                load_block8_direct<D>(sm, 0, krs, vrs, dvoff8, j * kBc, wave_u);
+            else
+                load_block_direct<D>(sm, 0, krs, vrs, dvoff, j * kBc, wave_u);
         }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        for (int buf = 0;; buf ^= 1) {
-            const int j_next = union_next<NIV>(tm, j);
-            const bool has_next = j_next != INT_MAX && (split == 1 || --left > 0);
+        for (int buf = 0, it = 0;; buf ^= 1, ++it) {
+            const bool active = GRP == 1 || j != INT_MAX;
+            const int j_next = active ? union_next<NIV>(tm, j) : INT_MAX;
+            const bool has_next = j_next != INT_MAX && (pieces == 1 || --left > 0);
             if (has_next) {
                 if constexpr (F8)
                     load_block8_direct<D>(sm, buf ^ 1, krs, vrs, dvoff8, j_next * kBc, wave_u);
@@ -756,7 +797,7 @@ void attn_fwd_kernel(
                     load_block_direct<D>(sm, buf ^ 1, krs, vrs, dvoff, j_next * kBc, wave_u);
             }
 
-            const int klo = j * kBc;
+            const int klo = (active ? j : 0) * kBc;
             const int khi = min(klo + kBc, N) - 1;
             // The wavefront skips the block when each range of each of its
             // rows misses it, and computes it without the compare when one
@@ -767,6 +808,7 @@ void attn_fwd_kernel(
                 wave_skip &= khi < w_min_s[k] || klo > w_max_e[k];
                 wave_full |= klo >= w_max_s[k] && khi <= w_min_e[k];
             }
+            wave_skip |= !active;                // a group past its last block
             if (!wave_skip) {
                 // ---- S^T = K Q^T: lane holds S[q = r32][key = 32 jb + 8 (v/4) + 4 half + v%4]
                 floatx16 st[kBc / 32];
@@ -900,9 +942,54 @@ void attn_fwd_kernel(
 
             if (has_next) __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
             __syncthreads();
-            if (!has_next) break;
-            j = j_next;
+            if (GRP == 1 ? !has_next : it + 1 >= steps) break;
+            j = has_next ? j_next : INT_MAX;
         }
+    }
+
+    // ---- groups: groups 1.. leave their running state in their own shared
+    // memory and finish; group 0 combines it with its own against the largest
+    // reference (the combination of the split pieces below, in LDS).
+    if constexpr (GRP > 1) {
+        constexpr int kAcc = D / 32 * 16;
+        constexpr int kChunks = kAcc / 4 + 1;
+        if (group > 0) {
+            float4* const st = smg[group].state;
+#pragma unroll
+            for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    st[(nb * 4 + g) * kThreads + tid] =
+                        make_float4(oacc[nb][4 * g], oacc[nb][4 * g + 1], oacc[nb][4 * g + 2], oacc[nb][4 * g + 3]);
+            st[(kChunks - 1) * kThreads + tid] = make_float4(m_run, l_run, l16_run, 0.f);
+        }
+        __syncthreads();
+        if (group > 0) return;
+        float m = m_run;
+        for (int gp = 1; gp < GRP; ++gp) m = fmaxf(m, smg[gp].state[(kChunks - 1) * kThreads + tid].x);
+        const float w0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+        l_run *= w0;
+        l16_run *= w0;
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) oacc[nb] *= w0;
+#pragma unroll 1
+        for (int gp = 1; gp < GRP; ++gp) {
+            const float4 s4 = smg[gp].state[(kChunks - 1) * kThreads + tid];
+            const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s4.x - m);
+            l_run = fmaf(w, s4.y, l_run);
+            l16_run = fmaf(w, s4.z, l16_run);
+#pragma unroll
+            for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 x = smg[gp].state[(nb * 4 + g) * kThreads + tid];
+                    oacc[nb][4 * g] = fmaf(w, x.x, oacc[nb][4 * g]);
+                    oacc[nb][4 * g + 1] = fmaf(w, x.y, oacc[nb][4 * g + 1]);
+                    oacc[nb][4 * g + 2] = fmaf(w, x.z, oacc[nb][4 * g + 2]);
+                    oacc[nb][4 * g + 3] = fmaf(w, x.w, oacc[nb][4 * g + 3]);
+                }
+        }
+        m_run = m;
     }
 
     // ---- split key ranges: every piece stores its running state (the
@@ -1025,12 +1112,13 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
                             const float* fp8_scales, int n_sets, bool fp8_weights, int split, float* part,
-                            unsigned* counters) {
+                            unsigned* counters, int groups) {
     const int64_t n_q = (N + kBr - 1) / kBr;
     const bool f8 = fp8_scales != nullptr;
     // Split key ranges only for bf16 launches without records.
     if (split < 1 || (split & (split - 1)) != 0 ||
-        (split > 1 && (f8 || meta != nullptr || part == nullptr || counters == nullptr)))
+        (split > 1 && (f8 || meta != nullptr || part == nullptr || counters == nullptr)) ||
+        (groups != 1 && groups != 2) || (groups > 1 && (f8 || meta != nullptr)))
         return hipErrorInvalidValue;
     const int64_t grid = B * H * n_q * split;
     const float c = (f8 ? scale * fp8_scales[0] * fp8_scales[1] : scale) * kLog2e;
@@ -1056,9 +1144,11 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
             const auto* Qp = static_cast<const uint16_t*>(q);
             const auto* Kp = static_cast<const uint16_t*>(k);
             const auto* Vp = static_cast<const uint16_t*>(v);
-            auto kernel = meta == nullptr ? (d == 128 ? attn_fwd_kernel<128, NIV, 3> : attn_fwd_kernel<64, NIV, 3>)
-                                          : (d == 128 ? attn_fwd_kernel<128, NIV, 0> : attn_fwd_kernel<64, NIV, 0>);
-            hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0, Qp, Kp,
+            auto kernel = meta != nullptr ? (d == 128 ? attn_fwd_kernel<128, NIV, 0> : attn_fwd_kernel<64, NIV, 0>)
+                          : groups == 2   ? (d == 128 ? attn_fwd_kernel<128, NIV, 4> : attn_fwd_kernel<64, NIV, 4>)
+                                          : (d == 128 ? attn_fwd_kernel<128, NIV, 3> : attn_fwd_kernel<64, NIV, 3>);
+            hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads * groups), 0, stream, start, stop, 0,
+                                  Qp, Kp,
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
                                   xcd_heads, n_sets > 1 ? 1 : 0, Op, lse, split, part, counters);
         }

@@ -12,7 +12,7 @@
 
 namespace fm {
 
-FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys) {
+FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys, bool across_workgroups) {
     FwdPlan p;
     p.n_q = (a.N + kBr - 1) / kBr;
     p.n_kv = (a.N + kBc - 1) / kBc;
@@ -25,16 +25,21 @@ FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys) {
     const int64_t items = p.M * a.H / p.n_sets;          // B H n_q workgroups
     p.single = single_launch && a.fp8_scales == nullptr && items <= kSingleLaunchGrid;
     p.split = 1;
+    p.groups = 1;
     p.part_bytes = 0;
     if (p.single && split_keys) {
         // Small problems: a query block's key blocks run one after another
         // in one workgroup while most CUs idle, so long ranges are cut into
-        // pieces that run side by side.
+        // pieces that run side by side: at d = 128 first over two wavefront
+        // groups of the workgroup, then over workgroups.  (At d = 64 a key
+        // block's work is mostly the softmax's vector instructions, which two
+        // wavefronts on one SIMD cannot overlap: groups were slower there.)
+        if (a.d == 128 && p.n_kv >= 2 * kGroupMinBlocks) p.groups = 2;
         const int64_t cap = std::min<int64_t>(std::min<int64_t>(kMaxSplit, kSingleLaunchGrid / items),
-                                              p.n_kv / kSplitMinBlocks);
+                                              p.n_kv / (p.groups * kSplitMinBlocks));
         int64_t s = 1;
         while (2 * s <= cap) s *= 2;
-        if (s > 1 && items <= kSplitCounters) {
+        if (s > 1 && items <= kSplitCounters && across_workgroups) {
             p.split = (int)s;
             p.part_bytes = split_part_bytes(items, s, a.d);
         }
@@ -61,7 +66,7 @@ hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, unsigned* co
         return launch_attention(a.q, a.k, a.v, a.col_start, a.col_end, a.n_ranges, nullptr, nullptr, a.B, a.H, a.N,
                                 a.d, a.scale, a.out, a.lse, a.stream, ev_start, ev_stop, a.fp8_scales, (int)p.n_sets,
                                 a.fp8_weights, p.split, p.split > 1 ? static_cast<float*>(ws) : nullptr,
-                                p.split > 1 ? counters : nullptr);
+                                p.split > 1 ? counters : nullptr, p.groups);
     auto* meta = static_cast<TileMeta*>(ws);
     auto* work = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes);
     auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.meta_bytes + p.int_bytes);

@@ -88,12 +88,16 @@ hipError_t launch_prep_small(const int32_t* col_start, const int32_t* col_end, i
 // fp8_scales == nullptr: q, k, v are bf16.  Otherwise they are e4m3,
 // fp8_scales points to their three dequantization scales (host memory), and
 // fp8_weights also rounds the weights to e4m3 for an FP8 PV product.
+// Without records (meta == nullptr, bf16): split > 1 cuts each query block's
+// key range into split pieces over as many workgroups (their states in part,
+// their arrivals counted in counters), groups = 2 each workgroup's share over
+// two groups of four wavefronts inside it.
 hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
                             const int32_t* col_end, int n_iv, const TileMeta* meta, const int32_t* order,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, void* out,
                             float* lse, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
                             const float* fp8_scales = nullptr, int n_sets = 1, bool fp8_weights = false,
-                            int split = 1, float* part = nullptr, unsigned* counters = nullptr);
+                            int split = 1, float* part = nullptr, unsigned* counters = nullptr, int groups = 1);
 
 // The forward pass's launch sequence (fm_forward.hip).
 struct FwdArgs {
@@ -117,6 +121,7 @@ struct FwdPlan {
     size_t meta_bytes, int_bytes, sched_bytes;
     bool single;               // the attention kernel alone (no records, no order)
     int split;                 // pieces per work item's key range (single launches only; 1: none)
+    int groups;                // wavefront groups sharing each workgroup's range (single launches; 1: none)
     size_t part_bytes;         // the pieces' partial states
     size_t total() const { return single ? part_bytes : meta_bytes + 2 * int_bytes + sched_bytes; }
 };
@@ -129,6 +134,10 @@ struct FwdPlan {
 // floats per piece.
 constexpr int kMaxSplit = 8;
 constexpr int kSplitMinBlocks = 8;
+// Before that (d = 128), a workgroup's range is shared by two groups of four
+// wavefronts combining through LDS, which costs far less, with at least
+// kGroupMinBlocks key blocks per group of the longest range.
+constexpr int kGroupMinBlocks = 16;
 constexpr int kFwdThreads = 256;
 // Arrival counters of split items: one per work item of a single launch,
 // zero between calls.
@@ -136,7 +145,9 @@ constexpr int kSplitCounters = 256;
 inline size_t split_part_bytes(int64_t items, int64_t split, int64_t d) {
     return (size_t)(items * split * kFwdThreads) * (size_t)(d / 2 + 4) * sizeof(float);
 }
-FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys);
+// split_keys: cut small single launches' key ranges (groups, and with
+// across_workgroups also workgroups, which need the workspace and counters).
+FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys, bool across_workgroups);
 
 // Queues the preprocessor, the scheduler (unless natural order) and the
 // attention kernel on a.stream, with ws (p.total() bytes of device memory) as

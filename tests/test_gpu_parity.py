@@ -422,15 +422,18 @@ def test_single_launch_equals_preprocessed_launch(kind):
 
 SPLIT_CASES = [
     # (B, H, N, d, kind): single launches (at most 256 workgroups) whose key ranges are cut
-    # into a power of two of pieces, at most 8 and at most 256 workgroups in all, each of
-    # at least 8 key blocks of the longest possible range.  Pieces per query block:
-    (1, 2, 1024, 64, "causal"),         # 2 (16 key blocks)
-    (1, 1, 1000, 128, "random_empty"),  # 2; ragged tail, empty rows, pieces with no key block
-    (2, 3, 1777, 64, "docs"),           # 2; 84 query blocks
-    (1, 4, 2048, 128, "prefix"),        # 4
-    (1, 1, 4096, 128, "causal"),        # 8
-    (1, 1, 1100, 64, "sliding"),        # 2; most pieces of a window hold no key block
+    # into pieces.  At d = 128 with at least 32 key blocks, two wavefront groups of each
+    # workgroup share its range (combined in LDS); then a power of two of workgroups, at
+    # most 8 and at most 256 workgroups in all, with at least 8 key blocks per piece of the
+    # longest possible range (combined through memory).  Groups x workgroups per query block:
+    (1, 2, 1024, 64, "causal"),         # 1 x 2 (16 key blocks)
+    (1, 1, 1000, 128, "random_empty"),  # 1 x 2; ragged tail, empty rows, pieces with no key block
+    (2, 3, 1777, 64, "docs"),           # 1 x 2; 84 query blocks
+    (1, 4, 2048, 128, "prefix"),        # 2 x 2
+    (1, 1, 4096, 128, "causal"),        # 2 x 4
+    (1, 1, 1100, 64, "sliding"),        # 1 x 2; most pieces of a window hold no key block
     (1, 2, 512, 64, "causal"),          # C1's shape: 8 key blocks, not split
+    (1, 9, 2000, 128, "random_empty"),  # 2 x 1 (144 query blocks); ragged tail, empty rows
 ]
 
 
