@@ -272,6 +272,17 @@ def load_counters(key):
     return rec
 
 
+def attn_kernel_name(res):
+    """The bf16 attention kernel instance the default options launch: <d, ranges per row, 0>
+    after the preprocessor; a problem of at most 256 query-block workgroups runs alone as
+    <.., 3>, or <.., 4> (two wavefront groups) at d = 128 with at least 32 key blocks."""
+    items = res["B"] * res["H"] * -(-res["N"] // 128)
+    prec = 0
+    if items <= 256:
+        prec = 4 if res["d"] == 128 and -(-res["N"] // 64) >= 32 else 3
+    return f"attn_fwd_kernel<{res['d']}, {res['ranges_per_row']}, {prec}>"
+
+
 def roofline_of(res):
     """The attention kernel's roofline figures on one workload.  achieved = algorithmic
     FLOPs (4 d per attended pair) over the kernel's own average duration; traffic = the
@@ -291,7 +302,7 @@ def roofline_of(res):
         "unit": "TFLOP/s",
         "frac": achieved / metrics.MI355X_BF16_DENSE_TFLOPS if achieved else None,
         "traffic": traffic,
-        "kernel": f"attn_fwd_kernel<{res['d']}, {res['ranges_per_row']}, 0>",   # <d, ranges per row, bf16>
+        "kernel": attn_kernel_name(res),
         "kernel_ms": kms,
         "algorithmic_flops_per_launch": res["effective_flops"],
         "algorithmic_bytes_per_launch": alg,

@@ -8,8 +8,9 @@ and, at its end, a plain device copy of COPY_MIB MiB (bench.py --copy-mib M with
 --no-backward --no-fp8, or masked_attention_fm_amd.profile_steps --copy-mib M).
 KIND picks the kernel (default ``attention``):
 
-* ``attention``: the bf16 forward kernel ``attn_fwd_kernel<d, ranges, 0>`` (the
-  FP8 instances are other kernels and never counted);
+* ``attention``: the bf16 forward kernel ``attn_fwd_kernel<d, ranges, P>``, P = 0
+  after the preprocessor, 3 or 4 for small problems launched alone (the FP8
+  instances, P = 1 and 2, are other kernels and never counted);
 * ``bwd_dkdv`` / ``bwd_dq``: the backward's dK/dV and dQ kernels.
 
 The record holds, per counter, the mean over that kernel's dispatches and over
@@ -40,7 +41,10 @@ ATTN_SOURCES = [os.path.join(PKG, "csrc", name) for name in
 # One bf16 MFMA v_mfma_f32_32x32x16_bf16: 2 * 32 * 32 * 16 FLOPs.
 MFMA_FLOPS = 2 * 32 * 32 * 16
 
-_BF16_ATTN = re.compile(r"attn_fwd_kernel<\s*\d+\s*,\s*\d+\s*,\s*0\s*>")
+# The bf16 attention kernel: attn_fwd_kernel<d, ranges, P> with P = 0 (launched
+# after the preprocessor) or 3, 4 (small problems launched alone, one or two
+# wavefront groups per workgroup); P = 1, 2 are the e4m3 kernels.
+_BF16_ATTN = re.compile(r"attn_fwd_kernel<\s*\d+\s*,\s*\d+\s*,\s*[034]\s*>")
 # The backward's kernels and the sources of their launch sequence.
 BWD_SOURCES = [os.path.join(PKG, "csrc", name) for name in
                ("fm_attn_bwd.hip", "fm_internal.h", "fm_mfma.h", "fm_schedule.hip", "fm_intervals.hip",

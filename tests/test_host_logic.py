@@ -92,6 +92,9 @@ def test_counter_summary_calibrates_with_the_copy(tmp_path):
 
 def test_counter_kernel_filter():
     assert counters.kind_of("void fm::(anonymous namespace)::attn_fwd_kernel<64, 4, 0>(int)") == "attention"
+    # the small-problem launches' instances (one or two wavefront groups) are the same kernel
+    for prec in (3, 4):
+        assert counters.kind_of(f"void fm::(anonymous namespace)::attn_fwd_kernel<128, 2, {prec}>(int)") == "attention"
     for name in ("attn_fwd_kernel<128, 1, 1>", "attn_fwd_kernel<128, 2, 2>", "bwd_dq_kernel<128, 1>",
                  "prep_small_kernel<1>"):
         assert counters.kind_of(name) == ""
