@@ -12,22 +12,21 @@
 //
 // Two kernels, no atomics, deterministic:
 //   * bwd_dkdv_kernel: one workgroup per (b, h, block of kBwdKeys = 128 keys),
-//     4 wavefronts of 32 keys.  A wavefront keeps its K and V rows in registers
-//     as MFMA B operands and walks the query chunks (kBwdRows = 64 rows) whose
-//     non-skip ranges hold its key block: S = Q K^T and dP = dO V^T with Q and
-//     dO read from LDS; then dV^T += dO^T P and dK^T += Q^T dS with P and dS
-//     taken straight from the registers and Q^T, dO^T read with transposing
-//     LDS reads in the same row order.  Q and dO are loaded straight into LDS.
-//     A lane ends up holding one key's dK and dV row.
+//     four pairs of wavefronts, a pair per 32 keys, walking the query chunks
+//     (kBwdRows = 64 rows) whose non-skip ranges hold the key block.  One
+//     wavefront of a pair holds the keys' K rows (MFMA B operands) and dV^T:
+//     S = Q K^T, the masked P (to LDS), dV^T += dO^T P.  The other holds V and
+//     dK^T, one chunk behind: dS = P (dP - D) with P from LDS, dK^T += Q^T dS,
+//     and dP = dO V^T of the current chunk.  Q and dO are read from LDS, row
+//     by row or with transposing reads; they are loaded straight into LDS.
+//     Two wavefronts per SIMD.  A lane ends up holding one key's dK or dV row.
 //   * bwd_dq_kernel: one workgroup per (b, h, query block of kBr = 128 rows),
 //     the forward's structure: S^T = K Q^T and dP^T = V dO^T with Q and dO in
 //     registers, then dQ^T += K^T dS^T, walking the union of the non-skip key
 //     blocks.  K and V are loaded straight into LDS; K^T is read with
 //     transposing LDS reads.  Two workgroups per CU.  A lane ends up holding
 //     one query's dQ row.
-// Both double-buffer their operands through LDS (one barrier per step); the
-// dK/dV kernel runs one wavefront per SIMD (its live state fills the register
-// file; the dK/dV accumulators stay in the accumulation registers).  A key
+// Both buffer their operands through LDS with one barrier per step.  A key
 // block attended by far more query chunks than the others is split into
 // pieces over equal shares of its chunks (bwd_split_kernel); later pieces
 // write fp32 partial sums that bwd_reduce_kernel adds in piece order.
@@ -431,31 +430,10 @@ __device__ __forceinline__ void dq_product(const floatx16 (&dst)[kBc / 32], floa
     }
 }
 
-// Two-operand variant of wait_lds_tied (both arrays passed through).
-template <int CNT, int NP>
-__device__ __forceinline__ void wait_lds_tied2(v4s (&p)[NP], v4s (&q)[NP]) {
-    static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
-    if constexpr (NP == 8)
-        asm volatile("s_waitcnt lgkmcnt(%16)"
-                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
-                       "+v"(p[7]), "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
-                       "+v"(q[6]), "+v"(q[7])
-                     : "i"(CNT));
-    else if constexpr (NP == 4)
-        asm volatile("s_waitcnt lgkmcnt(%8)"
-                     : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(q[0]), "+v"(q[1]), "+v"(q[2]),
-                       "+v"(q[3])
-                     : "i"(CNT));
-    else
-        static_assert(NP == 8 || NP == 4, "d = 64 or 128");
-}
-
-// S = Q K^T and dP = dO V^T for one 32-query half QB of the chunk: read r
-// (r even: Q, odd: dO) holds head-dimension chunk r / 2 of the lane's query
-// row and feeds MFMA r.  The reads are issued as inline assembly and run
-// kAheadS ahead through a ring of registers (left to itself the compiler
-// hoists all of them, and the registers they hold push the dK/dV accumulators
-// out of the vector register file).
+// Row-major operand reads (ds_read_b128) are issued as inline assembly and
+// run kAheadS ahead of their MFMAs through a ring of registers (left to
+// itself the compiler hoists all of them, and the registers they hold push
+// the accumulators out of the vector register file).
 constexpr int kAheadS = 7;
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
@@ -469,38 +447,6 @@ __device__ __forceinline__ void wait_lds_one(u32x4& r) {
     static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt field");
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(CNT));
 }
-template <int D, int QB, int R>
-__device__ __forceinline__ u32x4 sdp_read(uint32_t qaddr, uint32_t gaddr) {
-    using SL = SegLayout<D>;
-    constexpr int off = QB * (32 / SL::kSegs) * SL::kRowBytes + (R / 2) * 32;
-    return lds_read_b128<off>(R % 2 == 0 ? qaddr : gaddr);
-}
-template <int D, int QB, int I = 0>
-__device__ __forceinline__ void sdp_issue(u32x4 (&ring)[kAheadS], uint32_t qaddr, uint32_t gaddr) {
-    if constexpr (I < kAheadS) {
-        ring[I] = sdp_read<D, QB, I>(qaddr, gaddr);
-        sdp_issue<D, QB, I + 1>(ring, qaddr, gaddr);
-    }
-}
-template <int D, int QB, int I = 0>
-__device__ __forceinline__ void sdp_products(floatx16& s1, floatx16& dp1, const bf16x8 (&kreg)[D / 16],
-                                             const bf16x8 (&vreg)[D / 16], uint32_t qaddr, uint32_t gaddr,
-                                             u32x4 (&ring)[kAheadS]) {
-    constexpr int kN = 2 * (D / 16);
-    static_assert(kN > kAheadS, "more MFMAs than reads in flight");
-    if constexpr (I < kN) {
-        constexpr int issued = I + kAheadS < kN ? I + kAheadS : kN;
-        wait_lds_one<issued - (I + 1)>(ring[I % kAheadS]);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, ring[I % kAheadS]);
-        if constexpr (I % 2 == 0)
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[I / 2], s1, 0, 0, 0);
-        else
-            dp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[I / 2], dp1, 0, 0, 0);
-        if constexpr (I + kAheadS < kN) ring[I % kAheadS] = sdp_read<D, QB, I + kAheadS>(qaddr, gaddr);
-        sdp_products<D, QB, I + 1>(s1, dp1, kreg, vreg, qaddr, gaddr, ring);
-    }
-}
-
 // S^T = K Q^T and dP^T = V dO^T of the dQ kernel for one key block: read r
 // = 4 cs + 2 jb + {0: K, 1: V} holds head-dimension chunk cs of key half jb
 // and feeds MFMA r; issued kAheadS ahead like the dK/dV kernel's reads.
@@ -537,61 +483,9 @@ __device__ __forceinline__ void dq_sdp_products(floatx16 (&st)[kBc / 32], floatx
     }
 }
 
-// dV^T += dO^T P and dK^T += Q^T dS over steps KS .. KEND-1 (16 queries each)
-// of one 32-query half of the chunk, whose P and dS are the tiles p, ds (step
-// KS uses their elements 8 (KS % 2) ..); gcur, qcur: step KS's transposing
-// reads of dO and Q.  Per step: the next step's dO reads are issued, then this
-// step's reads of both are waited for (they are older than those), the dV
-// products run, the next step's Q reads are issued, and the dK products run.
-template <int D, int KS, int KEND>
-__device__ __forceinline__ void dkv_products_half(const floatx16& p, const floatx16& ds, floatx16 (&dvacc)[D / 32],
-                                                  floatx16 (&dkacc)[D / 32], uint32_t gaddr, uint32_t qaddr,
-                                                  v4s (&gcur)[2 * D / 32], v4s (&qcur)[2 * D / 32]) {
-    constexpr int NP = 2 * D / 32;
-    if constexpr (KS < KEND) {
-        bf16x8 pb, sb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pb[e] = (__bf16)p[8 * (KS & 1) + e];
-            sb[e] = (__bf16)ds[8 * (KS & 1) + e];
-        }
-        v4s gnext[NP], qnext[NP];
-        if constexpr (KS + 1 < KEND) {
-            issue_kt_reads<D, KS + 1>(gnext, gaddr);
-            wait_lds_tied2<NP>(gcur, qcur);
-        } else {
-            wait_lds_tied2<0>(gcur, qcur);
-        }
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(gcur[2 * nb], gcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            dvacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, dvacc[nb], 0, 0, 0);
-        }
-        if constexpr (KS + 1 < KEND) issue_kt_reads<D, KS + 1>(qnext, qaddr);
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(qcur[2 * nb], qcur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            dkacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, dkacc[nb], 0, 0, 0);
-        }
-        dkv_products_half<D, KS + 1, KEND>(p, ds, dvacc, dkacc, gaddr, qaddr, gnext, qnext);
-    }
-}
-
 // ---------------------------------------------------------------- dK, dV
 
 static_assert(kBwdRows == kBc, "query chunks use the 64-row segment layout");
-
-template <int D, int NIV>
-struct alignas(16) DkvSmem {
-    alignas(16) uint8_t q[2][SegLayout<D>::kBytes];     // Q chunk, swizzled segments
-    alignas(16) uint8_t go[2][SegLayout<D>::kBytes];    // dO chunk, swizzled segments
-    alignas(16) float lse2[2][kBwdRows];                // LSE * log2 e (+inf past N)
-    alignas(16) float dd[2][kBwdRows];                  // D (0 past N)
-    alignas(16) int start[2][NIV][kBwdRows];
-    alignas(16) int width[2][NIV][kBwdRows];
-};
 
 // Per-row values of a chunk staged through registers (Q and dO go straight
 // into LDS), as loaded: they are scaled and clamped only when stored, at the
@@ -603,16 +497,12 @@ struct DkvStage {
     int cs[NIV], ce[NIV];
 };
 
-// Chunk starting at row0 into buffer buf: Q and dO straight into LDS (loff:
-// this lane's segment offset), the per-row values into registers.
+// The per-row values of the chunk starting at row0 into registers (thread
+// tid < kBwdRows takes row row0 + tid).
 template <int D, int NIV>
-__device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, DkvSmem<D, NIV>& sm, int buf,
-                                         __amdgpu_buffer_rsrc_t qrs, __amdgpu_buffer_rsrc_t grs, int loff,
-                                         int wave_u, const float* __restrict__ lse_bh,
-                                         const float* __restrict__ dd_bh, const int32_t* __restrict__ cs_b,
-                                         const int32_t* __restrict__ ce_b, int row0, int N, int tid) {
-    dma_rows<D, true>(&sm.q[buf][0], qrs, loff, row0, wave_u);
-    dma_rows<D, true>(&sm.go[buf][0], grs, loff, row0, wave_u);
+__device__ __forceinline__ void dkv_load_rows(DkvStage<D, NIV>& st, const float* __restrict__ lse_bh,
+                                              const float* __restrict__ dd_bh, const int32_t* __restrict__ cs_b,
+                                              const int32_t* __restrict__ ce_b, int row0, int N, int tid) {
     if (tid < kBwdRows) {
         const int row = row0 + tid;
         st.lse = 0.f;
@@ -631,9 +521,21 @@ __device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, DkvSmem<D, NIV>& 
     }
 }
 
-template <int D, int NIV>
-__device__ __forceinline__ void dkv_store(const DkvStage<D, NIV>& st, DkvSmem<D, NIV>& sm, int buf, int row0, int N,
-                                          int tid) {
+// Chunk starting at row0 into buffers qbuf (Q), gbuf (dO): straight into LDS (loff:
+// this lane's segment offset), the per-row values into registers.
+template <int D, int NIV, class SM>
+__device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, SM& sm, int qbuf, int gbuf,
+                                         __amdgpu_buffer_rsrc_t qrs, __amdgpu_buffer_rsrc_t grs, int loff,
+                                         int wave_u, const float* __restrict__ lse_bh,
+                                         const float* __restrict__ dd_bh, const int32_t* __restrict__ cs_b,
+                                         const int32_t* __restrict__ ce_b, int row0, int N, int tid) {
+    dma_rows<D, true>(&sm.q[qbuf][0], qrs, loff, row0, wave_u);
+    dma_rows<D, true>(&sm.go[gbuf][0], grs, loff, row0, wave_u);
+    dkv_load_rows<D, NIV>(st, lse_bh, dd_bh, cs_b, ce_b, row0, N, tid);
+}
+
+template <int D, int NIV, class SM>
+__device__ __forceinline__ void dkv_store(const DkvStage<D, NIV>& st, SM& sm, int buf, int row0, int N, int tid) {
     if (tid < kBwdRows) {
         const bool in = row0 + tid < N;
         sm.lse2[buf][tid] = in ? st.lse * kLog2e : INFINITY;   // P = 0 for rows past N
@@ -711,24 +613,6 @@ __device__ __forceinline__ int probe_resolve(const ChunkProbe<NIV>& pr, const Ti
     return next_live_chunk<NIV>(meta_c, meta_row, J, pr.cand + 1, last, full);
 }
 
-// Per-row values of the weights, read as inline assembly like the operands:
-// ordinary LDS reads here would make the compiler first wait for the next
-// chunk's loads into LDS, which are meant to run until the end of the step.
-// LSE and D of queries 32 QB + 8 g + 4 half .. +3 (bases: this lane's element
-// 4 half of the row arrays), issued LSE g, D g in order of g.
-template <int QB, int G = 0>
-__device__ __forceinline__ void row_vals_issue(u32x4 (&lr)[4], u32x4 (&dr)[4], uint32_t lbase, uint32_t dbase) {
-    if constexpr (G < 4) {
-        lr[G] = lds_read_b128<(QB * 32 + 8 * G) * 4>(lbase);
-        dr[G] = lds_read_b128<(QB * 32 + 8 * G) * 4>(dbase);
-        row_vals_issue<QB, G + 1>(lr, dr, lbase, dbase);
-    }
-}
-__device__ __forceinline__ void row_vals_wait(u32x4 (&lr)[4], u32x4 (&dr)[4]) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(lr[0]), "+v"(lr[1]), "+v"(lr[2]), "+v"(lr[3]), "+v"(dr[0]), "+v"(dr[1]), "+v"(dr[2]),
-                   "+v"(dr[3]));
-}
 // Start and width of the same four queries in every range (range k at
 // k kBwdRows entries), waited for at once.
 template <int NIV, int OFF, int K = 0>
@@ -747,8 +631,130 @@ __device__ __forceinline__ void range_rows_read(u32x4 (&sr)[NIV], u32x4 (&wr)[NI
     }
 }
 
+// ---- dK/dV.  Keeping K, V and both accumulators of 32 keys in one wavefront
+// fills the register file (one wavefront per SIMD), and its exponentials and
+// dS then run with no MFMA beside them.  Here a pair of wavefronts shares 32
+// keys, one chunk apart.  In step s the P wavefront (K and dV^T in registers)
+// computes S = Q K^T of chunk s, the masked P (written to LDS), and
+// dV^T += dO^T P; the dS wavefront (V and dK^T) takes P of chunk s-1 from LDS,
+// forms dS = P (dP - D) with the dP it kept from step s-1, accumulates
+// dK^T += Q^T dS over chunk s-1, and computes dP = dO V^T of chunk s.  Each
+// wavefront fits in half the registers, so two run per SIMD, and each role's
+// vector work (the exponentials; dS) has the other role's products beside it,
+// with one barrier per step.  Q is kept for three chunks (s-1 for dK, s, s+1
+// loading), dO and P for two.  Both products of a role come out in the same
+// tile layout (rows of the chunk by the pair's keys), so a lane of the dS
+// wavefront reads back exactly the P values the same lane of the P wavefront
+// wrote.  Each of dK and dV sums the same products in the same order as one
+// wavefront doing both would.
+
+// S = Q K^T (or dP = dO V^T) of both 32-query halves of a chunk: read I holds
+// head-dimension chunk I / 2 of query 32 (I % 2) + r32 of the lane and feeds
+// MFMA I; the halves alternate so that consecutive products are independent.
+template <int D, int I>
+__device__ __forceinline__ u32x4 rows_read(uint32_t addr) {
+    using SL = SegLayout<D>;
+    constexpr int off = (I % 2) * (32 / SL::kSegs) * SL::kRowBytes + (I / 2) * 32;
+    return lds_read_b128<off>(addr);
+}
+template <int D, int I = 0>
+__device__ __forceinline__ void rows_issue(u32x4 (&ring)[kAheadS], uint32_t addr) {
+    if constexpr (I < kAheadS) {
+        ring[I] = rows_read<D, I>(addr);
+        rows_issue<D, I + 1>(ring, addr);
+    }
+}
+template <int D, int I = 0>
+__device__ __forceinline__ void rows_products(floatx16 (&acc)[2], const bf16x8 (&b)[D / 16], uint32_t addr,
+                                              u32x4 (&ring)[kAheadS]) {
+    constexpr int kN = 2 * (D / 16);
+    static_assert(kN > kAheadS, "more MFMAs than reads in flight");
+    if constexpr (I < kN) {
+        constexpr int issued = I + kAheadS < kN ? I + kAheadS : kN;
+        wait_lds_one<issued - (I + 1)>(ring[I % kAheadS]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ring[I % kAheadS]);
+        acc[I % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[I / 2], acc[I % 2], 0, 0, 0);
+        if constexpr (I + kAheadS < kN) ring[I % kAheadS] = rows_read<D, I + kAheadS>(addr);
+        rows_products<D, I + 1>(acc, b, addr, ring);
+    }
+}
+
+// acc^T += X^T W over steps KS .. KEND-1 (16 queries each) of a chunk, X^T
+// read with transposing LDS reads (cur: step KS's), W the weights as MFMA B
+// operands (w[KS]: queries 16 KS .. of the lane's key).
+template <int D, int KS, int KEND>
+__device__ __forceinline__ void kt_products(const bf16x8 (&w)[kBwdRows / 16], floatx16 (&acc)[D / 32],
+                                            uint32_t addr, v4s (&cur)[2 * D / 32]) {
+    constexpr int NP = 2 * D / 32;
+    if constexpr (KS < KEND) {
+        v4s next[NP];
+        if constexpr (KS + 1 < KEND) {
+            issue_kt_reads<D, KS + 1>(next, addr);
+            wait_lds_tied<NP>(cur);
+        } else {
+            wait_lds_tied<0>(cur);
+        }
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(cur[2 * nb], cur[2 * nb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[KS], acc[nb], 0, 0, 0);
+        }
+        kt_products<D, KS + 1, KEND>(w, acc, addr, next);
+    }
+}
+
+// The dS wavefront's P (exchange slots I = 4 qb + g, 1 KB apart) and D
+// (queries 32 qb + 8 g + 4 half .. +3) reads, and the waits for them in issue
+// order (LDS reads complete in order; lgkmcnt counts up to 15).
+template <int I = 0>
+__device__ __forceinline__ void pair_weight_reads(u32x4 (&pr)[8], u32x4 (&dr)[8], uint32_t xaddr, uint32_t daddr) {
+    if constexpr (I < 8) {
+        pr[I] = lds_read_b128<I * 1024>(xaddr);
+        dr[I] = lds_read_b128<((I / 4) * 32 + 8 * (I % 4)) * 4>(daddr);
+        pair_weight_reads<I + 1>(pr, dr, xaddr, daddr);
+    }
+}
+template <int I = 0>
+__device__ __forceinline__ void pair_weight_waits(u32x4 (&pr)[8], u32x4 (&dr)[8]) {
+    if constexpr (I < 8) {
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(pr[I]), "+v"(dr[I]) : "i"(2 * (7 - I)));
+        pair_weight_waits<I + 1>(pr, dr);
+    }
+}
+
+// LSE of queries 32 QB + 8 g + 4 half .. +3, g = 0..3 (lbase: this lane's
+// element 4 half of the row array), as inline assembly.
+template <int QB, int G = 0>
+__device__ __forceinline__ void lse_issue(u32x4 (&lr)[4], uint32_t lbase) {
+    if constexpr (G < 4) {
+        lr[G] = lds_read_b128<(QB * 32 + 8 * G) * 4>(lbase);
+        lse_issue<QB, G + 1>(lr, lbase);
+    }
+}
+__device__ __forceinline__ void wait_lds4(u32x4 (&r)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, float4 v) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    const u32x4 bits = __builtin_bit_cast(u32x4, v);
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(bits), "i"(OFF) : "memory");
+}
+
 template <int D, int NIV>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+struct alignas(16) DkvSmem {
+    alignas(16) uint8_t q[3][SegLayout<D>::kBytes];     // Q of chunks s-1, s, s+1 (index chunk % 3)
+    alignas(16) uint8_t go[2][SegLayout<D>::kBytes];    // dO of chunks s, s+1 (index chunk % 2)
+    alignas(16) float lse2[3][kBwdRows];
+    alignas(16) float dd[3][kBwdRows];
+    alignas(16) int start[3][NIV][kBwdRows];
+    alignas(16) int width[3][NIV][kBwdRows];
+    alignas(16) float4 xch[2][kWaves][2][4][64];       // P of step s in [s % 2]: [pair][half][four queries][lane]
+};
+
+template <int D, int NIV>
+__global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end,
@@ -759,15 +765,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int kw = wave & (kWaves - 1);          // the pair's 32-key column block
+    const bool dsw = wave >= kWaves;             // dS wavefront (it also loads the chunks)
     const int half = lane >> 5;
     const int r32 = lane & 31;
 
     int h, slot;
     slot_to_item(xcd_heads, H, h, slot);
-    // With one interval set per head, head h reads set h: its key-block items
-    // are the segment [h Lk, h Lk + Lk) of the records, its pieces the segment
-    // [h Lp, h Lp + Lp) of the piece table and of the order.
-    const int Lp = gridDim.x / H;                // piece entries per head
+    const int Lp = gridDim.x / H;
     const int set = per_head ? h : 0;
     const int n_sets = per_head ? H : 1;
     const int pe = order[set * Lp + slot];
@@ -779,32 +784,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int J = local - b * n_kb;
 
     const int64_t bh = (int64_t)b * H + h;
-    const int key = J * kBwdKeys + wave * 32 + r32;     // this lane's key
-    const int kw0 = J * kBwdKeys + wave * 32;           // the wavefront's first key
+    const int key = J * kBwdKeys + kw * 32 + r32;
+    const int kw0 = J * kBwdKeys + kw * 32;
 
-    // K and V rows of this lane's key as MFMA B operands: [key][16 cs + 8 half .. +7].
-    bf16x8 kreg[D / 16], vreg[D / 16];
+    // K (P wavefront) or V (dS wavefront) of this lane's key as MFMA B
+    // operands: [key][16 cs + 8 half .. +7].
+    const uint16_t* kv_src = dsw ? V : K;
+    bf16x8 kv[D / 16];
 #pragma unroll
-    for (int cs = 0; cs < D / 16; ++cs) {
-        if (key < N) {
-            kreg[cs] = *reinterpret_cast<const bf16x8*>(K + (bh * N + key) * D + cs * 16 + half * 8);
-            vreg[cs] = *reinterpret_cast<const bf16x8*>(V + (bh * N + key) * D + cs * 16 + half * 8);
-        } else {
-            kreg[cs] = bf16x8{};
-            vreg[cs] = bf16x8{};
-        }
-    }
-    floatx16 dkacc[D / 32], dvacc[D / 32];
+    for (int cs = 0; cs < D / 16; ++cs)
+        kv[cs] = key < N ? *reinterpret_cast<const bf16x8*>(kv_src + (bh * N + key) * D + cs * 16 + half * 8)
+                         : bf16x8{};
+    floatx16 acc[D / 32];                        // dV^T (P wavefront) or dK^T (dS wavefront)
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) {
-        dkacc[nb] = floatx16{};
-        dvacc[nb] = floatx16{};
-        // Start the accumulators in the matrix unit's accumulation registers,
-        // where the products keep them.  Started as zeros in the vector
-        // registers, they were assigned across the chunk loop so that each
-        // chunk copied all 128 of them out and back (256 moves per chunk).
-        asm volatile("" : "+a"(dkacc[nb]), "+a"(dvacc[nb]));
-    }
+    for (int nb = 0; nb < D / 32; ++nb) acc[nb] = floatx16{};
 
     const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(Q + bh * N * D, N * D * 2);
     const __amdgpu_buffer_rsrc_t grs = slice_rsrc(dO + bh * N * D, N * D * 2);
@@ -814,142 +807,200 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int32_t* ce_b = col_end + ((int64_t)b * n_sets + set) * NIV * N;
     const int64_t meta_row = ((int64_t)set * (Lk / n_kb) + b) * n_qc;
 
-    // Lane offsets of the loads and of the operand reads (see SegLayout).
     using SL = SegLayout<D>;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wave_u = __builtin_amdgcn_readfirstlane(kw);
     const int loff = seg_lane_offset<D, true>(lane, wave_u);
     const int q_lane = k_segment<D>(r32 % SL::kSegs) * SL::kPitch + (r32 / SL::kSegs) * SL::kRowBytes + 16 * half;
     const int a4 = (lane & 15) >> 2;
     const int t_lane = (D == 128 ? 4 * a4 + half : 4 * half + a4) * SL::kPitch + 32 * ((lane >> 4) & 1) +
                        8 * (lane & 3);
+    const int ltid = dsw ? kBwdRows : tid;             // the P wavefronts stage the per-row values
 
-    // The first live chunk of the piece's range.
     bool full_t, full_next;
     int t = next_live_chunk<NIV>(meta_c, meta_row, J, piece.y, piece.z, full_t);
     if (t != INT_MAX) {
         int t_next = next_live_chunk<NIV>(meta_c, meta_row, J, t + 1, piece.z, full_next);
+        // The P wavefronts load Q and the per-row values, the dS wavefronts dO.
         DkvStage<D, NIV> stage;
-        dkv_load<D, NIV>(stage, sm, 0, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b, t * kBwdRows, N, tid);
-        dkv_store<D, NIV>(stage, sm, 0, t * kBwdRows, N, tid);
+        if (!dsw) {
+            dma_rows<D, true>(&sm.q[0][0], qrs, loff, t * kBwdRows, wave_u);
+            dkv_load_rows<D, NIV>(stage, lse_bh, dd_bh, cs_b, ce_b, t * kBwdRows, N, ltid);
+            dkv_store<D, NIV>(stage, sm, 0, t * kBwdRows, N, ltid);
+        } else {
+            dma_rows<D, true>(&sm.go[0][0], grs, loff, t * kBwdRows, wave_u);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int buf = 0;; buf ^= 1) {
-            const bool has_next = t_next != INT_MAX;
-            ChunkProbe<NIV> probe;
-            if (has_next) {
-                dkv_load<D, NIV>(stage, sm, buf ^ 1, qrs, grs, loff, wave_u, lse_bh, dd_bh, cs_b, ce_b,
-                                 t_next * kBwdRows, N, tid);
-                probe_issue<NIV>(probe, meta_c, meta_row, t_next + 1, piece.z);
-            }
+        // The dS wavefront's pending chunk (the previous step's): its dP tiles,
+        // whether it was skipped.
+        floatx16 dpp[2] = {};
+        bool pend = false, pend_skip = true;
+        for (int s = 0;; ++s) {
+            const bool has_cur = t != INT_MAX;
+            const bool has_next = has_cur && t_next != INT_MAX;
+            const int q3 = s % 3, qp3 = (s + 2) % 3, qn3 = (s + 1) % 3;   // chunk s, s-1, s+1 buffers
+            const int g2 = s & 1;
 
-            // Does some row of the chunk attend the wavefront's keys, and does
-            // one range cover them for every row?  Where one range covers the
-            // whole key block for every row (the chunk's records), every
-            // wavefront is FULL; otherwise lane l looks at row l.
+            // Does some row of chunk t attend the wavefront's keys, and does
+            // one range cover them for every row (both roles decide alike)?
             const int klo = kw0;
-            bool wave_skip = klo >= N, wave_full = true;   // every key of the wavefront past N: skip
-            if (!full_t) {
+            bool wave_skip = !has_cur || klo >= N, wave_full = true;
+            if (has_cur && !full_t) {
                 const int row0 = t * kBwdRows;
                 const int khi = min(kw0 + 31, N - 1);
                 bool skip = true, full = false;
 #pragma unroll
                 for (int k = 0; k < NIV; ++k) {
-                    const int4 rb =
-                        wave_row_bounds_dpp(sm.start[buf][k][lane], sm.width[buf][k][lane], row0 + lane < N);
+                    const int4 rb = wave_row_bounds(sm.start[q3][k][lane], sm.width[q3][k][lane], row0 + lane < N);
                     skip &= khi < rb.x || klo > rb.y;
                     full |= klo >= rb.z && khi <= rb.w;
                 }
                 wave_skip |= skip;
                 wave_full = full;
             }
-            if (!wave_skip) {
-                // The chunk in two halves of 32 queries, each taken through S, dP,
-                // the weights and its share of the dV / dK products before the
-                // next: only one half's S and dP tiles are live at a time.
-                const uint32_t gaddr = lds_address(&sm.go[buf][0]) + t_lane;
-                const uint32_t qaddr = lds_address(&sm.q[buf][0]) + t_lane;
-                auto chunk_half = [&](auto qbc, auto fullc) {
-                    constexpr int qb = decltype(qbc)::value;
-                    constexpr bool kFull = decltype(fullc)::value;   // one range covers every row's keys
-                    // ---- S = Q K^T, dP = dO V^T: lane holds [query 32 qb + 8 (v/4) + 4 half + v%4][key]
-                    // the half's LSE and D, issued first: the operand reads'
-                    // waits below also see them complete
-                    u32x4 lr[4], dr[4];
-                    row_vals_issue<qb>(lr, dr, lds_address(&sm.lse2[buf][4 * half]),
-                                       lds_address(&sm.dd[buf][4 * half]));
-                    floatx16 s1 = {}, dp1 = {};
-                    {
-                        const uint32_t qrow = lds_address(&sm.q[buf][0]) + q_lane;
-                        const uint32_t grow = lds_address(&sm.go[buf][0]) + q_lane;
-                        u32x4 ring[kAheadS];
-                        sdp_issue<D, qb>(ring, qrow, grow);
-                        sdp_products<D, qb>(s1, dp1, kreg, vreg, qrow, grow, ring);
-                    }
-                    row_vals_wait(lr, dr);
-                    // transposing reads of the half's first product step, issued
-                    // now so that their latency overlaps the weights
-                    v4s gpart[2 * D / 32], qpart[2 * D / 32];
-                    issue_kt_reads<D, 2 * qb>(gpart, gaddr);
-                    issue_kt_reads<D, 2 * qb>(qpart, qaddr);
-                    // ---- P = exp(scale s - LSE) inside the ranges, dS = P (dP - D)
-                    const uint32_t sbase = lds_address(&sm.start[buf][0][4 * half]);
-                    const uint32_t wbase = lds_address(&sm.width[buf][0][4 * half]);
-                    auto weights = [&](auto gc) {
-                        constexpr int g = decltype(gc)::value;
-                        const float4 l4 = __builtin_bit_cast(float4, lr[g]);
-                        const float4 d4 = __builtin_bit_cast(float4, dr[g]);
-                        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-                        bool ok[4] = {true, true, true, true};
-                        if constexpr (!kFull) {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) ok[q] = false;
-                            u32x4 sr[NIV], wr[NIV];
-                            range_rows_read<NIV, (qb * 32 + 8 * g) * 4>(sr, wr, sbase, wbase);
-#pragma unroll
-                            for (int k = 0; k < NIV; ++k) {
-                                const int4 s4 = __builtin_bit_cast(int4, sr[k]);
-                                const int4 w4 = __builtin_bit_cast(int4, wr[k]);
-                                ok[0] |= (uint32_t)(key - s4.x) <= (uint32_t)w4.x;
-                                ok[1] |= (uint32_t)(key - s4.y) <= (uint32_t)w4.y;
-                                ok[2] |= (uint32_t)(key - s4.z) <= (uint32_t)w4.z;
-                                ok[3] |= (uint32_t)(key - s4.w) <= (uint32_t)w4.w;
-                            }
-                        }
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int v = 4 * g + q;
-                            const float p = __builtin_amdgcn_exp2f(fmaf(s1[v], c, -lv[q]));
-                            const float pm = kFull || ok[q] ? p : 0.f;
-                            s1[v] = pm;
-                            dp1[v] = pm * (dp1[v] - dv4[q]);
-                        }
-                    };
-                    weights(std::integral_constant<int, 0>{});
-                    weights(std::integral_constant<int, 1>{});
-                    weights(std::integral_constant<int, 2>{});
-                    weights(std::integral_constant<int, 3>{});
-                    // ---- dV^T += dO^T P, dK^T += Q^T dS over the half's 32 queries
-                    dkv_products_half<D, 2 * qb, 2 * qb + 2>(s1, dp1, dvacc, dkacc, gaddr, qaddr, gpart, qpart);
-                };
-                static_assert(kBwdRows == 64, "two halves of 32 queries");
-                if (wave_full) {
-                    chunk_half(std::integral_constant<int, 0>{}, std::true_type{});
-                    chunk_half(std::integral_constant<int, 1>{}, std::true_type{});
+
+            ChunkProbe<NIV> probe;
+            if (has_next) {
+                if (!dsw) {
+                    dma_rows<D, true>(&sm.q[qn3][0], qrs, loff, t_next * kBwdRows, wave_u);
+                    dkv_load_rows<D, NIV>(stage, lse_bh, dd_bh, cs_b, ce_b, t_next * kBwdRows, N, ltid);
                 } else {
-                    chunk_half(std::integral_constant<int, 0>{}, std::false_type{});
-                    chunk_half(std::integral_constant<int, 1>{}, std::false_type{});
+                    dma_rows<D, true>(&sm.go[g2 ^ 1][0], grs, loff, t_next * kBwdRows, wave_u);
                 }
+                probe_issue<NIV>(probe, meta_c, meta_row, t_next + 1, piece.z);
             }
+
+            if (!dsw) {
+                if (!wave_skip) {
+                    // ---- S of chunk s: lane holds [query 32 qb + 8 (v/4) + 4 half + v%4][key] in x[qb][v]
+                    floatx16 x[2] = {};
+                    {
+                        const uint32_t rows = lds_address(&sm.q[q3][0]) + q_lane;
+                        u32x4 ring[kAheadS];
+                        rows_issue<D>(ring, rows);
+                        rows_products<D>(x, kv, rows, ring);
+                    }
+                    // ---- P = exp(scale s - LSE) inside the ranges, to LDS and as operands.
+                    // LSE, the intervals and the exchange slots are read and written
+                    // as inline assembly: ordinary LDS accesses here would make the
+                    // compiler first wait for this wavefront's loads of chunk s+1.
+                    const uint32_t lbase = lds_address(&sm.lse2[q3][4 * half]);
+                    const uint32_t sbase = lds_address(&sm.start[q3][0][4 * half]);
+                    const uint32_t wbase = lds_address(&sm.width[q3][0][4 * half]);
+                    const uint32_t xbase = lds_address(&sm.xch[g2][kw][0][0][lane]);
+                    auto weights = [&](auto qbc, auto fullc) {
+                        constexpr int qb = decltype(qbc)::value;
+                        constexpr bool kFull = decltype(fullc)::value;
+                        u32x4 lr[4];
+                        lse_issue<qb>(lr, lbase);
+                        wait_lds4(lr);
+                        auto group = [&](auto gc) {
+                            constexpr int g = decltype(gc)::value;
+                            const float4 l4 = __builtin_bit_cast(float4, lr[g]);
+                            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                            bool ok[4] = {true, true, true, true};
+                            if constexpr (!kFull) {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) ok[q] = false;
+                                u32x4 sr[NIV], wr[NIV];
+                                range_rows_read<NIV, (qb * 32 + 8 * g) * 4>(sr, wr, sbase, wbase);
+#pragma unroll
+                                for (int k = 0; k < NIV; ++k) {
+                                    const int4 s4 = __builtin_bit_cast(int4, sr[k]);
+                                    const int4 w4 = __builtin_bit_cast(int4, wr[k]);
+                                    ok[0] |= (uint32_t)(key - s4.x) <= (uint32_t)w4.x;
+                                    ok[1] |= (uint32_t)(key - s4.y) <= (uint32_t)w4.y;
+                                    ok[2] |= (uint32_t)(key - s4.z) <= (uint32_t)w4.z;
+                                    ok[3] |= (uint32_t)(key - s4.w) <= (uint32_t)w4.w;
+                                }
+                            }
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int v = 4 * g + q;
+                                const float p = __builtin_amdgcn_exp2f(fmaf(x[qb][v], c, -lv[q]));
+                                x[qb][v] = kFull || ok[q] ? p : 0.f;
+                            }
+                            lds_write_b128<(qb * 4 + g) * 1024>(
+                                xbase, make_float4(x[qb][4 * g], x[qb][4 * g + 1], x[qb][4 * g + 2], x[qb][4 * g + 3]));
+                        };
+                        group(std::integral_constant<int, 0>{});
+                        group(std::integral_constant<int, 1>{});
+                        group(std::integral_constant<int, 2>{});
+                        group(std::integral_constant<int, 3>{});
+                    };
+                    if (wave_full) {
+                        weights(std::integral_constant<int, 0>{}, std::true_type{});
+                        weights(std::integral_constant<int, 1>{}, std::true_type{});
+                    } else {
+                        weights(std::integral_constant<int, 0>{}, std::false_type{});
+                        weights(std::integral_constant<int, 1>{}, std::false_type{});
+                    }
+                    bf16x8 w[kBwdRows / 16];
+#pragma unroll
+                    for (int ks = 0; ks < kBwdRows / 16; ++ks)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w[ks][e] = (__bf16)x[ks >> 1][8 * (ks & 1) + e];
+                    // ---- dV^T += dO^T P over chunk s
+                    const uint32_t taddr = lds_address(&sm.go[g2][0]) + t_lane;
+                    v4s cur[2 * D / 32];
+                    issue_kt_reads<D, 0>(cur, taddr);
+                    kt_products<D, 0, kBwdRows / 16>(w, acc, taddr, cur);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // P is in LDS before the barrier
+                }
+            } else {
+                if (pend && !pend_skip) {
+                    // ---- dS = P (dP - D) of chunk s-1, P and D read as inline
+                    // assembly (the compiler would first wait for this
+                    // wavefront's loads of chunk s+1, which write other LDS)
+                    u32x4 pr[8], dr[8];
+                    pair_weight_reads(pr, dr, lds_address(&sm.xch[g2 ^ 1][kw][0][0][lane]),
+                                      lds_address(&sm.dd[qp3][4 * half]));
+                    pair_weight_waits(pr, dr);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const float4 p4 = __builtin_bit_cast(float4, pr[4 * qb + g]);
+                            const float4 d4 = __builtin_bit_cast(float4, dr[4 * qb + g]);
+                            dpp[qb][4 * g] = p4.x * (dpp[qb][4 * g] - d4.x);
+                            dpp[qb][4 * g + 1] = p4.y * (dpp[qb][4 * g + 1] - d4.y);
+                            dpp[qb][4 * g + 2] = p4.z * (dpp[qb][4 * g + 2] - d4.z);
+                            dpp[qb][4 * g + 3] = p4.w * (dpp[qb][4 * g + 3] - d4.w);
+                        }
+                    }
+                    bf16x8 w[kBwdRows / 16];
+#pragma unroll
+                    for (int ks = 0; ks < kBwdRows / 16; ++ks)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w[ks][e] = (__bf16)dpp[ks >> 1][8 * (ks & 1) + e];
+                    // ---- dK^T += Q^T dS over chunk s-1
+                    const uint32_t taddr = lds_address(&sm.q[qp3][0]) + t_lane;
+                    v4s cur[2 * D / 32];
+                    issue_kt_reads<D, 0>(cur, taddr);
+                    kt_products<D, 0, kBwdRows / 16>(w, acc, taddr, cur);
+                }
+                if (!wave_skip) {
+                    // ---- dP of chunk s, kept for the next step
+                    dpp[0] = floatx16{};
+                    dpp[1] = floatx16{};
+                    const uint32_t rows = lds_address(&sm.go[g2][0]) + q_lane;
+                    u32x4 ring[kAheadS];
+                    rows_issue<D>(ring, rows);
+                    rows_products<D>(dpp, kv, rows, ring);
+                }
+                pend = has_cur;
+                pend_skip = wave_skip;
+            }
+
             int t_after = INT_MAX;
             bool full_after = false;
             if (has_next) {
-                dkv_store<D, NIV>(stage, sm, buf ^ 1, t_next * kBwdRows, N, tid);
+                if (!dsw) dkv_store<D, NIV>(stage, sm, qn3, t_next * kBwdRows, N, ltid);
                 __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads have landed
                 t_after = probe_resolve<NIV>(probe, meta_c, meta_row, J, piece.z, full_after);
             }
             __syncthreads();
-            if (!has_next) break;
+            if (!has_cur) break;                 // that step finished the dS wavefront's last chunk
             t = t_next;
             full_t = full_next;
             t_next = t_after;
@@ -957,27 +1008,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         }
     }
 
-    // ---- epilogue: lane holds dK, dV of its key at d = 32 nb + 8 g + 4 half + (0..3).
-    // Piece 0 writes dK, dV; a later piece of a split block its partial sums.
+    // ---- epilogue: lane holds dV (P wavefront) or dK (dS wavefront) of its key
+    // at d = 32 nb + 8 g + 4 half + (0..3); a later piece of a split block
+    // writes its partial sums.
     if (key < N) {
-        float* dk_row = dK + (bh * N + key) * D;
-        float* dv_row = dV + (bh * N + key) * D;
+        float* row = (dsw ? dK : dV) + (bh * N + key) * D;
         if ((piece.w >> 16) != 0) {
             float* pb = part + ((int64_t)pslot[pe] * H + h) * (kBwdKeys * D * 2);
-            dk_row = pb + (key - J * kBwdKeys) * D;
-            dv_row = dk_row + kBwdKeys * D;
+            row = pb + (key - J * kBwdKeys) * D + (dsw ? 0 : kBwdKeys * D);
         }
+        const float f = dsw ? scale : 1.f;
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = nb * 32 + 8 * g + 4 * half;
-                *reinterpret_cast<float4*>(dk_row + col) =
-                    make_float4(scale * dkacc[nb][4 * g], scale * dkacc[nb][4 * g + 1], scale * dkacc[nb][4 * g + 2],
-                                scale * dkacc[nb][4 * g + 3]);
-                *reinterpret_cast<float4*>(dv_row + col) =
-                    make_float4(dvacc[nb][4 * g], dvacc[nb][4 * g + 1], dvacc[nb][4 * g + 2], dvacc[nb][4 * g + 3]);
-            }
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4*>(row + nb * 32 + 8 * g + 4 * half) =
+                    make_float4(f * acc[nb][4 * g], f * acc[nb][4 * g + 1], f * acc[nb][4 * g + 2],
+                                f * acc[nb][4 * g + 3]);
         }
     }
 }
@@ -1223,7 +1270,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
     return dispatch_ranges(n_iv, [&](auto niv) {
         constexpr int NIV = decltype(niv)::value;
         auto kernel = d == 128 ? bwd_dkdv_kernel<128, NIV> : bwd_dkdv_kernel<64, NIV>;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(2 * kThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                            static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), lse, dd, col_start,
                            col_end, meta_c, pieces, pslot, order, (int)H, (int)N, (int)n_qc, (int)n_kb,

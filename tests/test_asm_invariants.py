@@ -10,7 +10,7 @@ cross-compiles; no GPU involved).
   operation returns.)
 * No packed fp32 arithmetic (v_pk_add/mul/fma_f32) anywhere.
 * No scratch (register spills) in the attention kernels.
-* The dK/dV kernel keeps its accumulators in AGPRs across the chunk loop (no copies).
+* The dK/dV kernel runs two wavefronts per SIMD: at most 256 registers, no AGPR moves.
 """
 import os
 import re
@@ -100,15 +100,30 @@ def test_no_scratch(device_asm, src):
         assert not any(l.startswith("scratch_") for l in ins), name
 
 
-def test_dkdv_accumulators_stay_in_accumulation_registers(device_asm):
-    """The dK/dV kernel's 2·d/32 accumulator tiles live in AGPRs for the whole chunk loop:
-    no instantiation writes AGPRs from VGPRs (a copy-out/copy-back of the accumulators
-    around each chunk showed up as hundreds of v_accvgpr_write and cost 7-12 %)."""
+def _kernel_metadata(asm):
+    """Per kernel symbol: its register and LDS figures from the code object's metadata."""
+    out = {}
+    for blk in re.findall(r"- \.agpr_count:.*?(?=\n  - \.agpr_count:|\n\.end_amdgpu_metadata)", asm, re.S):
+        name = re.search(r"\.name:\s+(\S+)", blk).group(1)
+        get = lambda key: int(re.search(r"\." + key + r":\s+(\d+)", blk).group(1))
+        out[name] = {"vgpr": get("vgpr_count"), "agpr": get("agpr_count"), "lds": get("group_segment_fixed_size")}
+    return out
+
+
+def test_dkdv_two_wavefronts_per_simd(device_asm):
+    """The dK/dV kernel's pairs of wavefronts (512 threads) run two per SIMD: every
+    instantiation fits in 256 registers (vector and accumulation together) and in the CU's
+    160 KB of LDS, and none moves values between the two register files."""
+    asm = device_asm["fm_attn_bwd.hip"]
+    meta = _kernel_metadata(asm)
     seen = 0
-    for name, ins in _kernels(device_asm["fm_attn_bwd.hip"]):
+    for name, ins in _kernels(asm):
         if "bwd_dkdv_kernel" not in name:
             continue
         seen += 1
-        writes = sum(1 for l in ins if l.startswith("v_accvgpr_write"))
-        assert writes <= 4, f"{name}: {writes} v_accvgpr_write"
+        m = meta[name]
+        assert m["vgpr"] <= 256, f"{name}: {m['vgpr']} registers"
+        assert m["lds"] <= 160 * 1024, f"{name}: {m['lds']} bytes of LDS"
+        moves = sum(1 for l in ins if l.startswith("v_accvgpr"))
+        assert moves == 0, f"{name}: {moves} accumulation-register moves"
     assert seen == 8, seen            # d in {64, 128} x 1..4 ranges
