@@ -261,7 +261,10 @@ FM_API int fm_tile_schedule_multi(const int32_t* col_start, const int32_t* col_e
  * row and head plus 40 B per query block and, with one interval set for all
  * heads, the split pieces' partial sums, 32 * H * 128 * d * 8 bytes (128 MiB
  * at H = 32, d = 128); the buffer is kept until the process ends.  Inputs must
- * not alias the outputs.
+ * not alias the outputs.  On mid-sized problems the dQ part runs on a second
+ * stream that the library keeps per (device, stream), forked from `stream`
+ * after its first kernel and joined back into it before the call returns:
+ * everything the call queues is still ordered on `stream` as a whole.
  */
 FM_API int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                        const float* lse, const int32_t* col_start, const int32_t* col_end,

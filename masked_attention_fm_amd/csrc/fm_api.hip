@@ -63,6 +63,15 @@ struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
     unsigned* counters = nullptr;   // fm::kSplitCounters arrival counters, zero between calls
+    // The backward's second stream (default priority) and its fork/join
+    // events: its dQ chain runs beside the dK/dV chain and joins the caller's
+    // stream before the call's last launch.
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+struct SideStream {
+    hipStream_t stream;
+    hipEvent_t fork, join;
 };
 std::mutex g_ws_map_mutex;    // guards the map itself (its nodes never move)
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
@@ -72,7 +81,7 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 // With `counters`, also the stream's split-arrival counters, allocated and
 // zero-filled on first use (the kernels that use them leave them zero).
 hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out, std::unique_lock<std::mutex>& hold,
-                         unsigned** counters = nullptr) {
+                         unsigned** counters = nullptr, SideStream* side = nullptr) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -109,6 +118,30 @@ hipError_t get_workspace(hipStream_t stream, size_t bytes, void** out, std::uniq
             if (e != hipSuccess) return e;
         }
         *counters = w->counters;
+    }
+    if (side != nullptr) {
+        if (w->side == nullptr) {
+            e = hipStreamCreateWithFlags(&w->side, hipStreamNonBlocking);
+            if (e != hipSuccess) {
+                w->side = nullptr;
+                return e;
+            }
+        }
+        if (w->fork == nullptr) {
+            e = hipEventCreateWithFlags(&w->fork, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                w->fork = nullptr;
+                return e;
+            }
+        }
+        if (w->join == nullptr) {
+            e = hipEventCreateWithFlags(&w->join, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                w->join = nullptr;
+                return e;
+            }
+        }
+        *side = SideStream{w->side, w->fork, w->join};
     }
     *out = w->ptr;
     return hipSuccess;
@@ -463,14 +496,25 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     const size_t o_part = o_dd + al((size_t)(B * H * N) * sizeof(float));
     const size_t part_floats = n_sets == 1 ? (size_t)fm::kBwdExtraPieces * H * fm::kBwdKeys * d * 2 : 0;
     const int64_t n_kv = (N + fm::kBc - 1) / fm::kBc;
-    // scheduler scratch, used by the two orders one after the other
-    const int64_t sched_ints = std::max(fm::schedule_scratch_ints(Mq, B * n_q, fm::schedule_shift(Mq), (int)n_kv),
-                                        fm::schedule_scratch_ints(Mp, Lp, 0, (int)n_qc));
+    // scheduler scratch of the two orders (they run at the same time, on two streams)
+    const int64_t sched_q_ints = fm::schedule_scratch_ints(Mq, B * n_q, fm::schedule_shift(Mq), (int)n_kv);
+    const int64_t sched_k_ints = fm::schedule_scratch_ints(Mp, Lp, 0, (int)n_qc);
     const size_t o_sched = o_part + al(part_floats * sizeof(float));
-    const size_t total = o_sched + al((size_t)sched_ints * sizeof(int32_t));
+    const size_t o_sched_k = o_sched + al((size_t)sched_q_ints * sizeof(int32_t));
+    const size_t total = o_sched_k + al((size_t)sched_k_ints * sizeof(int32_t));
+    // The dQ chain and the dK/dV chain read the same inputs and write
+    // different outputs.  Where the dK/dV grid runs a few rounds on the 256
+    // CUs, the dQ chain goes to a second stream, forked after D and joined
+    // before the return, so that it fills the CUs that the dK/dV grid's last
+    // round leaves idle (C2 -6 %).  A long grid has no such tail and the two
+    // kernels then only contend for the L2 (C5 +1.5 %), and on a tiny call the
+    // fork and join cost more than they save (C1 +6 %).
+    const int64_t dkdv_groups = H * Lp;
+    const bool two_streams = dkdv_groups >= 2 * 256 && dkdv_groups <= 24 * 256;
     void* ws = nullptr;
     std::unique_lock<std::mutex> ws_hold;       // held until the last launch below is queued
-    FM_HIP(get_workspace(stream, total, &ws, ws_hold));
+    SideStream side{stream, nullptr, nullptr};
+    FM_HIP(get_workspace(stream, total, &ws, ws_hold, nullptr, two_streams ? &side : nullptr));
     char* w = static_cast<char*>(ws);
     auto* meta_q = reinterpret_cast<fm::TileMeta*>(w);
     auto* work_q = reinterpret_cast<int32_t*>(w + o_work_q);
@@ -485,31 +529,58 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     auto* splits = reinterpret_cast<int4*>(w + o_splits);
     auto* dd = reinterpret_cast<float*>(w + o_dd);
     auto* part = reinterpret_cast<float*>(w + o_part);
-    auto* sched = reinterpret_cast<int32_t*>(w + o_sched);
+    auto* sched_q = reinterpret_cast<int32_t*>(w + o_sched);
+    auto* sched_k = reinterpret_cast<int32_t*>(w + o_sched_k);
 
     FM_HIP(fm::launch_bwd_rowdot(out, dout, B * H * N, d, dd, stream));
-    // dQ: the forward's query blocks, key blocks and longest-first order
-    if (Mq <= fm::kPrepSmallMax) {
-        FM_HIP(fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, order_q,
-                                     stream, (int)n_sets));
-    } else {
-        FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q, nullptr,
-                                     stream, (int)n_sets));
-        FM_HIP(fm::launch_schedule(work_q, Mq, order_q, stream, B * n_q, fm::schedule_shift(Mq), (int)n_kv, sched));
+    if (two_streams) {
+        FM_HIP(hipEventRecord(side.fork, stream));
+        FM_HIP(hipStreamWaitEvent(side.stream, side.fork, 0));
     }
+#define FM_TRY(call)                           \
+    do {                                       \
+        const hipError_t e_ = (call);          \
+        if (e_ != hipSuccess) return e_;       \
+    } while (0)
+    // dQ: the forward's query blocks, key blocks and longest-first order
+    const hipError_t e_q = [&]() -> hipError_t {
+        if (Mq <= fm::kPrepSmallMax) {
+            FM_TRY(fm::launch_prep_small(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q,
+                                         order_q, side.stream, (int)n_sets));
+        } else {
+            FM_TRY(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBr, fm::kBc, meta_q, work_q,
+                                         nullptr, side.stream, (int)n_sets));
+            FM_TRY(fm::launch_schedule(work_q, Mq, order_q, side.stream, B * n_q, fm::schedule_shift(Mq), (int)n_kv,
+                                       sched_q));
+        }
+        return fm::launch_bwd_dq(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_q, order_q, B, H, N, d,
+                                 scale, dq, side.stream, (int)n_sets);
+    }();
+    // (recorded and waited for whatever happened above, so that nothing
+    // queued on the second stream outlives the call's stream order)
+    const hipError_t e_join = two_streams ? hipEventRecord(side.join, side.stream) : hipSuccess;
     // dK, dV: query chunks per key block, long key blocks split into pieces,
     // pieces longest first (within each set)
-    FM_HIP(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBwdRows, fm::kBwdKeys, meta_c, nullptr,
-                                 nullptr, stream, (int)n_sets));
-    FM_HIP(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream, (int)n_sets));
-    const int min_chunks = g_bwd_min_chunks > 0 ? g_bwd_min_chunks : (1 << 30);
-    FM_HIP(fm::launch_bwd_split(kvr, B * n_kb, (int)n_sets, min_chunks, pieces, pslot, pwork, splits, stream));
-    FM_HIP(fm::launch_schedule(pwork, Mp, order_k, stream, Lp, 0, (int)n_qc, sched));
-    FM_HIP(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, pieces, pslot, order_k,
-                               B, H, N, d, scale, dk, dv, part, stream, (int)n_sets));
-    FM_HIP(fm::launch_bwd_dq(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_q, order_q, B, H, N, d,
-                             scale, dq, stream, (int)n_sets));
-    if (n_sets == 1) FM_HIP(fm::launch_bwd_reduce(splits, part, H, N, d, n_kb, dk, dv, stream));
+    const hipError_t e_k = [&]() -> hipError_t {
+        FM_TRY(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBwdRows, fm::kBwdKeys, meta_c,
+                                     nullptr, nullptr, stream, (int)n_sets));
+        FM_TRY(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream, (int)n_sets));
+        const int min_chunks = g_bwd_min_chunks > 0 ? g_bwd_min_chunks : (1 << 30);
+        FM_TRY(fm::launch_bwd_split(kvr, B * n_kb, (int)n_sets, min_chunks, pieces, pslot, pwork, splits, stream));
+        FM_TRY(fm::launch_schedule(pwork, Mp, order_k, stream, Lp, 0, (int)n_qc, sched_k));
+        FM_TRY(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, pieces, pslot,
+                                   order_k, B, H, N, d, scale, dk, dv, part, stream, (int)n_sets));
+        if (n_sets == 1) FM_TRY(fm::launch_bwd_reduce(splits, part, H, N, d, n_kb, dk, dv, stream));
+        return hipSuccess;
+    }();
+#undef FM_TRY
+    const hipError_t e_wait = !two_streams ? hipSuccess
+                              : e_join == hipSuccess ? hipStreamWaitEvent(stream, side.join, 0)
+                                                     : e_join;
+    FM_HIP(e_q);
+    FM_HIP(e_join);
+    FM_HIP(e_k);
+    FM_HIP(e_wait);
     return FM_OK;
 }
 
