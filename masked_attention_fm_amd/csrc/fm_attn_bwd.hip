@@ -521,19 +521,6 @@ __device__ __forceinline__ void dkv_load_rows(DkvStage<D, NIV>& st, const float*
     }
 }
 
-// Chunk starting at row0 into buffers qbuf (Q), gbuf (dO): straight into LDS (loff:
-// this lane's segment offset), the per-row values into registers.
-template <int D, int NIV, class SM>
-__device__ __forceinline__ void dkv_load(DkvStage<D, NIV>& st, SM& sm, int qbuf, int gbuf,
-                                         __amdgpu_buffer_rsrc_t qrs, __amdgpu_buffer_rsrc_t grs, int loff,
-                                         int wave_u, const float* __restrict__ lse_bh,
-                                         const float* __restrict__ dd_bh, const int32_t* __restrict__ cs_b,
-                                         const int32_t* __restrict__ ce_b, int row0, int N, int tid) {
-    dma_rows<D, true>(&sm.q[qbuf][0], qrs, loff, row0, wave_u);
-    dma_rows<D, true>(&sm.go[gbuf][0], grs, loff, row0, wave_u);
-    dkv_load_rows<D, NIV>(st, lse_bh, dd_bh, cs_b, ce_b, row0, N, tid);
-}
-
 template <int D, int NIV, class SM>
 __device__ __forceinline__ void dkv_store(const DkvStage<D, NIV>& st, SM& sm, int buf, int row0, int N, int tid) {
     if (tid < kBwdRows) {
