@@ -274,9 +274,13 @@ def load_counters(key):
 
 def attn_kernel_name(res):
     """The bf16 attention kernel instance the default options launch: <d, ranges per row, 0>
-    after the preprocessor; a problem of at most 256 query-block workgroups runs alone as
-    <.., 3>, or <.., 4> (two wavefront groups) at d = 128 with at least 32 key blocks."""
+    after the preprocessor; a problem of at most 256 query-block workgroups runs alone, as
+    the 32-row slice kernel when it has at most 512 slices, else as <.., 3>, or <.., 4>
+    (two wavefront groups) at d = 128 with at least 32 key blocks."""
     items = res["B"] * res["H"] * -(-res["N"] // 128)
+    slices = res["B"] * res["H"] * -(-res["N"] // 32)
+    if items <= 256 and slices <= 512:
+        return f"attn_fwd_rows_kernel<{res['d']}, {res['ranges_per_row']}>"
     prec = 0
     if items <= 256:
         prec = 4 if res["d"] == 128 and -(-res["N"] // 64) >= 32 else 3

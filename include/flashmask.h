@@ -319,7 +319,7 @@ enum {
                                    workgroup reducing its own query block's key range; 0 always
                                    queues the interval preprocessor and the work ordering first.
                                    Results are identical either way when FM_OPT_SPLIT_KEYS is 0. */
-    FM_OPT_SPLIT_KEYS = 4       /* forward, bf16 single launches (above): 1 (default) cuts each query
+    FM_OPT_SPLIT_KEYS = 4,      /* forward, bf16 single launches (above): 1 (default) cuts each query
                                    block's long key ranges into pieces.  At d = 128, ranges of at
                                    least 32 key blocks go first to two groups of four wavefronts in
                                    each workgroup, combined through LDS; then, up to 8 pieces of at
@@ -328,6 +328,13 @@ enum {
                                    0: neither.  The results differ from the unsplit ones only by the
                                    order of fp32 additions.  fm_attn_fwd_noalloc uses the groups
                                    but never splits over workgroups. */
+    FM_OPT_ROW_SLICES = 5       /* forward, bf16 single launches with FM_OPT_SPLIT_KEYS on: problems of
+                                   at most this many slices of 32 query rows (B * H * ceil(N/32);
+                                   default 512, 0: never) run one workgroup per slice, whose
+                                   wavefronts share the slice's key blocks and combine their partial
+                                   softmax states through LDS (no workspace; fm_attn_fwd_noalloc
+                                   too).  Differs from the other launches only by the order of fp32
+                                   additions. */
 };
 FM_API int fm_set_option(int option, int64_t value);
 

@@ -43,8 +43,10 @@ MFMA_FLOPS = 2 * 32 * 32 * 16
 
 # The bf16 attention kernel: attn_fwd_kernel<d, ranges, P> with P = 0 (launched
 # after the preprocessor) or 3, 4 (small problems launched alone, one or two
-# wavefront groups per workgroup); P = 1, 2 are the e4m3 kernels.
-_BF16_ATTN = re.compile(r"attn_fwd_kernel<\s*\d+\s*,\s*\d+\s*,\s*[034]\s*>")
+# wavefront groups per workgroup), or attn_fwd_rows_kernel<d, ranges> (small
+# problems launched alone, one workgroup per 32-row slice); P = 1, 2 are the
+# e4m3 kernels.
+_BF16_ATTN = re.compile(r"attn_fwd_kernel<\s*\d+\s*,\s*\d+\s*,\s*[034]\s*>|attn_fwd_rows_kernel<\s*\d+\s*,\s*\d+\s*>")
 # The backward's kernels and the sources of their launch sequence.
 BWD_SOURCES = [os.path.join(PKG, "csrc", name) for name in
                ("fm_attn_bwd.hip", "fm_internal.h", "fm_mfma.h", "fm_schedule.hip", "fm_intervals.hip",

@@ -41,6 +41,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int g_schedule_mode = 0;   // 0 longest first, 1 natural order
 int g_single_launch = 1;   // 1: small problems run the attention kernel alone
 int g_split_keys = 1;      // 1: single launches split long key ranges over several workgroups
+int64_t g_row_slices = 512;  // single launches of at most this many 32-row slices run the slice kernel
 int g_bwd_min_chunks = 32; // smallest piece of a split key block (query chunks); 0: never split
 
 // ---------------------------------------------------------------- workspace
@@ -198,6 +199,11 @@ FM_API int fm_set_option(int option, int64_t value) {
         g_split_keys = (int)value;
         return FM_OK;
     }
+    if (option == FM_OPT_ROW_SLICES) {
+        if (value < 0 || value > (1 << 20)) return FM_ERR_INVALID_ARG;
+        g_row_slices = value;
+        return FM_OK;
+    }
     if (option == FM_OPT_BWD_SPLIT_CHUNKS) {
         if (value < 0 || value > (1 << 20)) return FM_ERR_INVALID_ARG;
         g_bwd_min_chunks = (int)value;
@@ -330,7 +336,7 @@ int fwd_check(const fm::FwdArgs& a) {
 int attn_fwd_impl(const fm::FwdArgs& a) {
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
-    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1, true);
+    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1, true, g_row_slices);
     void* ws = nullptr;
     unsigned* counters = nullptr;
     std::unique_lock<std::mutex> ws_hold;       // held until the launches below are queued
@@ -442,7 +448,7 @@ FM_API int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, cons
     const int st = fwd_check(a);
     if (st != FM_OK) return st;
     // (no split key ranges here: they need arrival counters that start at zero)
-    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1, false);
+    const fm::FwdPlan p = fm::fwd_plan(a, g_single_launch == 1, g_split_keys == 1, false, g_row_slices);
     if (p.total() > (size_t)FM_NOALLOC_SCRATCH_BYTES) return FM_ERR_TOO_LARGE;
     void* ws = nullptr;
     FM_HIP(scratch_address(&ws));

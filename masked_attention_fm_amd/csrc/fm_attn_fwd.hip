@@ -1105,6 +1105,248 @@ void attn_fwd_kernel(
     if (qrow < N && half == 0) LSE[bh * N + qrow] = l > 0.f ? fmaf(m_run - kW8Shift, kLn2, logf(l)) : -INFINITY;
 }
 
+// ---------------------------------------------------------------- small problems
+//
+// With a few dozen query blocks, the kernel above leaves most CUs idle while
+// each workgroup walks its key blocks one after another, one wavefront per
+// SIMD, with nothing beside it to hide the latency of each block's chain of
+// products and exponentials.  For such problems a workgroup takes one slice
+// of 32 query rows of one (b, h), and its kRowWaves wavefronts share the
+// slice's key blocks: wavefront w walks the w-th contiguous share of them
+// (in increasing order) through its own LDS buffer, with the same block body
+// as above.  The wavefronts then leave their running states in their
+// buffers and combine them against the largest reference maximum, as the
+// wavefront groups above do, each combining its own columns of the output.
+// No records and no workspace: every wavefront reduces the slice's key range
+// from the intervals it loads itself.
+template <int D>
+constexpr int kRowWaves = D == 64 ? 8 : 4;
+
+template <int D>
+struct alignas(16) RowsWaveBuf {
+    alignas(16) uint8_t k[Direct<D>::kKBytes];
+    alignas(16) uint8_t v[Direct<D>::kVBytes];
+};
+
+// Every segment of one key block, loaded by one wavefront (off: the lane's
+// offset for segment 0, direct_lane_offset with wave 0, plus the block's).
+template <int D, int SEG = 0>
+__device__ __forceinline__ void load_block_wave(RowsWaveBuf<D>& wb, __amdgpu_buffer_rsrc_t krs,
+                                                __amdgpu_buffer_rsrc_t vrs, int off) {
+    using L = Direct<D>;
+    if constexpr (SEG < L::kSegs) {
+        const int row_off = off + SEG * L::kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)&wb.k[SEG * L::kKPitch], 16, row_off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)&wb.v[SEG * L::kVPitch], 16, row_off, 0, 0, 0);
+        load_block_wave<D, SEG + 1>(wb, krs, vrs, off);
+    }
+}
+
+template <int D, int NIV>
+__global__ __launch_bounds__(64 * kRowWaves<D>)
+void attn_fwd_rows_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, const int32_t* __restrict__ col_start,
+                          const int32_t* __restrict__ col_end, int H, int N, int n_slices, float c, int per_head,
+                          uint16_t* __restrict__ O, float* __restrict__ LSE) {
+    constexpr int W = kRowWaves<D>;
+    constexpr int kChunks = D / 8 + 1;            // float4 chunks of a lane's state (last: m, l, l16)
+    static_assert(sizeof(float4) * kChunks * 64 <= sizeof(RowsWaveBuf<D>), "a state fits its buffer");
+    __shared__ RowsWaveBuf<D> wbuf[W];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+    // workgroup (b n_slices + t) H + h: slice t of batch element b, head h
+    const int h = blockIdx.x % H;
+    const int bt = blockIdx.x / H;
+    const int b = bt / n_slices;
+    const int t = bt - b * n_slices;
+    const int set = per_head ? h : 0;
+    const int n_sets = per_head ? H : 1;
+    const int64_t bh = (int64_t)b * H + h;
+    const int qrow = t * kRowsPerWave + r32;
+
+    // Q rows of this lane as MFMA B operands: Q[row][16 cs + 8 half .. +7]
+    bf16x8 qreg[D / 16];
+#pragma unroll
+    for (int cs = 0; cs < D / 16; ++cs)
+        qreg[cs] = qrow < N ? *reinterpret_cast<const bf16x8*>(Q + (bh * N + qrow) * D + cs * 16 + half * 8)
+                            : bf16x8{};
+
+    // This lane's row intervals, clamped to [0, N), and the slice's bounds
+    // per range (both halves hold the same rows).
+    int my_s[NIV], my_w[NIV];
+    int w_min_s[NIV], w_max_e[NIV], w_max_s[NIV], w_min_e[NIV];
+    TileMeta tm[NIV];
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) {
+        int s = kEmptyStart, w = 0;
+        if (qrow < N) {
+            const int64_t at = (((int64_t)b * n_sets + set) * NIV + k) * N + qrow;
+            const int sc = max(col_start[at], 0);
+            const int ec = min(col_end[at], N - 1);
+            if (sc <= ec) {
+                s = sc;
+                w = ec - sc;
+            }
+        }
+        my_s[k] = s;
+        my_w[k] = w;
+        const bool any = s != kEmptyStart;
+        w_min_s[k] = wave_min(any ? s : INT_MAX);
+        w_max_e[k] = wave_max(any ? s + w : INT_MIN);
+        w_max_s[k] = wave_max(any ? s : (qrow < N ? INT_MAX : INT_MIN));
+        w_min_e[k] = wave_min(any ? s + w : (qrow < N ? INT_MIN : INT_MAX));
+        tm[k] = w_max_e[k] >= w_min_s[k] ? make_int4(w_min_s[k] / kBc, w_max_e[k] / kBc, 0, -1)
+                                         : make_int4(0, -1, 0, -1);
+    }
+
+    // This wavefront's share of the union of the non-skip key blocks.
+    const int n = union_blocks<NIV>(tm);
+    const int lo = wave * n / W;
+    int left = (wave + 1) * n / W - lo;
+    int j = union_next<NIV>(tm, -1);
+    for (int s = 0; s < lo; ++s) j = union_next<NIV>(tm, j);
+
+    RowsWaveBuf<D>& wb = wbuf[wave];
+    const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + bh * N * D, N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + bh * N * D, N * D * 2);
+    const int loff = direct_lane_offset<D>(lane, 0);
+    if (left > 0) load_block_wave<D>(wb, krs, vrs, loff + j * kBc * Direct<D>::kRowBytes);
+
+    const int k_lane = (r32 % Direct<D>::kSegs) * Direct<D>::kKPitch + (r32 / Direct<D>::kSegs) * Direct<D>::kRowBytes +
+                       16 * half;
+    const int v_lane = (4 * (lane >> 5) + ((lane & 15) >> 2)) * Direct<D>::kVPitch + 32 * ((lane >> 4) & 1) +
+                       8 * (lane & 3);
+    floatx16 oacc[D / 32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) oacc[nb] = floatx16{};
+    float m_run = -INFINITY;   // running row maximum, in log2 units
+    float l_run = 0.f;         // this lane's share of the row sum of the fp32 weights -> LSE
+    float l16_run = 0.f;       // the same over the bf16-rounded weights -> O
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    for (; left > 0; --left) {
+        __builtin_amdgcn_s_waitcnt(0);             // block j is in this wavefront's buffer
+        asm volatile("" ::: "memory");
+        const int klo = j * kBc;
+        const int khi = min(klo + kBc, N) - 1;
+        bool wave_skip = true, wave_full = false;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            wave_skip &= khi < w_min_s[k] || klo > w_max_e[k];
+            wave_full |= klo >= w_max_s[k] && khi <= w_min_e[k];
+        }
+        if (!wave_skip) {
+            floatx16 st[kBc / 32];
+#pragma unroll
+            for (int jb = 0; jb < kBc / 32; ++jb) st[jb] = floatx16{};
+            u32x4 ring[kAheadK];
+            const uint32_t kaddr = lds_address(&wb.k[0]) + k_lane;
+            issue_k_reads<D>(ring, kaddr);
+            score_direct<D>(st, qreg, kaddr, ring);
+            if (!((klo + kBc <= N) && wave_full)) {
+                int base[NIV];
+#pragma unroll
+                for (int k = 0; k < NIV; ++k) base[k] = klo + 4 * half - my_s[k];
+#pragma unroll
+                for (int jb = 0; jb < kBc / 32; ++jb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int off = jb * 32 + 8 * (v >> 2) + (v & 3);
+                        bool ok = false;
+#pragma unroll
+                        for (int k = 0; k < NIV; ++k) ok |= (uint32_t)(base[k] + off) <= (uint32_t)my_w[k];
+                        st[jb][v] = ok ? st[jb][v] : -INFINITY;
+                    }
+            }
+            float mx = st[0][0];
+#pragma unroll
+            for (int jb = 0; jb < kBc / 32; ++jb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[jb][v]);
+            // lazy rescaling, as above: the reference may trail the running
+            // maximum by up to 8 in log2 units
+            const float m_blk = halves_max(mx) * c;
+            if (__builtin_amdgcn_ballot_w64(m_blk > m_run + 8.f) != 0) {
+                const bool grow = m_blk > m_run;
+                const float m_new = grow ? m_blk : m_run;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+                l_run *= alpha;
+                l16_run *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < D / 32; ++nb) oacc[nb] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            v4s vpart[2 * D / 32];
+            const uint32_t vaddr = lds_address(&wb.v[0]) + v_lane;
+            issue_v_reads<D, 0>(vpart, vaddr, m_use);
+            float rs = 0.f, rs16 = 0.f;
+            pv_direct<D, 0>(st, oacc, vaddr, c, m_use, rs, rs16, ones, vpart);
+            l_run += rs;
+            l16_run += rs16;
+        }
+        j = union_next<NIV>(tm, j);
+        if (left > 1) {
+            // every read of the buffer has completed (the products waited for them)
+            asm volatile("" ::: "memory");
+            load_block_wave<D>(wb, krs, vrs, loff + j * kBc * Direct<D>::kRowBytes);
+        }
+    }
+
+    // Every wavefront's state into its own buffer (no load into it is in flight).
+    float4* const mine = reinterpret_cast<float4*>(&wb);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            mine[(nb * 4 + g) * 64 + lane] =
+                make_float4(oacc[nb][4 * g], oacc[nb][4 * g + 1], oacc[nb][4 * g + 2], oacc[nb][4 * g + 3]);
+    mine[(kChunks - 1) * 64 + lane] = make_float4(m_run, l_run, l16_run, 0.f);
+    __syncthreads();
+
+    // Combination against the largest reference: O_acc = sum_w 2^(m_w - m) O_acc,w
+    // and the same for both sums, in wavefront order.
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+        m = fmaxf(m, reinterpret_cast<const float4*>(&wbuf[w])[(kChunks - 1) * 64 + lane].x);
+    float wgt[W];
+    float l = 0.f, l16 = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const float4 s4 = reinterpret_cast<const float4*>(&wbuf[w])[(kChunks - 1) * 64 + lane];
+        wgt[w] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s4.x - m);
+        l = fmaf(wgt[w], s4.y, l);
+        l16 = fmaf(wgt[w], s4.z, l16);
+    }
+    l = halves_sum(l);
+    l16 = halves_sum(l16);
+    const float inv = l16 > 0.f ? 1.f / l16 : 0.f;
+    // Wavefront `wave` writes chunks wave, wave + W, ...: chunk nb 4 + g holds
+    // columns 32 nb + 8 g + 4 half .. +3 of row qrow (the MFMA result layout).
+    uint16_t* const orow = O + (bh * N + qrow) * D;
+#pragma unroll
+    for (int ch = wave; ch < D / 8; ch += W) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float4 x = reinterpret_cast<const float4*>(&wbuf[w])[ch * 64 + lane];
+            acc.x = fmaf(wgt[w], x.x, acc.x);
+            acc.y = fmaf(wgt[w], x.y, acc.y);
+            acc.z = fmaf(wgt[w], x.z, acc.z);
+            acc.w = fmaf(wgt[w], x.w, acc.w);
+        }
+        const bf16x4 o4 = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv),
+                           (__bf16)(acc.w * inv)};
+        const int col = 32 * (ch / 4) + 8 * (ch % 4) + 4 * half;
+        if (qrow < N) *reinterpret_cast<bf16x4*>(orow + col) = o4;
+    }
+    if (wave == 0 && qrow < N && half == 0) LSE[bh * N + qrow] = l > 0.f ? fmaf(m, kLn2, logf(l)) : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t launch_attention(const void* q, const void* k, const void* v, const int32_t* col_start,
@@ -1152,6 +1394,28 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                                   Vp, col_start, col_end, meta, order, (int)H, (int)N, (int)n_q, c, v_scale,
                                   xcd_heads, n_sets > 1 ? 1 : 0, Op, lse, split, part, counters);
         }
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_attention_rows(const void* q, const void* k, const void* v, const int32_t* col_start,
+                                 const int32_t* col_end, int n_iv, int64_t B, int64_t H, int64_t N, int64_t d,
+                                 float scale, void* out, float* lse, hipStream_t stream, hipEvent_t start,
+                                 hipEvent_t stop, int n_sets) {
+    if (d != 64 && d != 128) return hipErrorInvalidValue;
+    const int64_t n_slices = (N + kRowsPerWave - 1) / kRowsPerWave;
+    const int64_t grid = B * H * n_slices;
+    const float c = scale * kLog2e;
+    const auto* Qp = static_cast<const uint16_t*>(q);
+    const auto* Kp = static_cast<const uint16_t*>(k);
+    const auto* Vp = static_cast<const uint16_t*>(v);
+    auto* Op = static_cast<uint16_t*>(out);
+    return dispatch_ranges(n_iv, [&](auto niv) {
+        constexpr int NIV = decltype(niv)::value;
+        auto kernel = d == 128 ? attn_fwd_rows_kernel<128, NIV> : attn_fwd_rows_kernel<64, NIV>;
+        const int threads = 64 * (d == 128 ? kRowWaves<128> : kRowWaves<64>);
+        hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, stream, start, stop, 0, Qp, Kp, Vp,
+                              col_start, col_end, (int)H, (int)N, (int)n_slices, c, n_sets > 1 ? 1 : 0, Op, lse);
         return hipGetLastError();
     });
 }

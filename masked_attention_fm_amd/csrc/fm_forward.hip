@@ -12,7 +12,8 @@
 
 namespace fm {
 
-FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys, bool across_workgroups) {
+FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys, bool across_workgroups,
+                 int64_t row_slices_max) {
     FwdPlan p;
     p.n_q = (a.N + kBr - 1) / kBr;
     p.n_kv = (a.N + kBc - 1) / kBc;
@@ -27,7 +28,8 @@ FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys, bool acr
     p.split = 1;
     p.groups = 1;
     p.part_bytes = 0;
-    if (p.single && split_keys) {
+    p.rows = p.single && split_keys && a.B * a.H * ((a.N + 31) / 32) <= row_slices_max;
+    if (p.single && split_keys && !p.rows) {
         // Small problems: a query block's key blocks run one after another
         // in one workgroup while most CUs idle, so long ranges are cut into
         // pieces that run side by side: at d = 128 first over two wavefront
@@ -62,6 +64,9 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream) {
 
 hipError_t fwd_launch(const FwdArgs& a, const FwdPlan& p, void* ws, unsigned* counters, bool natural,
                       hipEvent_t ev_start, hipEvent_t ev_stop) {
+    if (p.rows)
+        return launch_attention_rows(a.q, a.k, a.v, a.col_start, a.col_end, a.n_ranges, a.B, a.H, a.N, a.d, a.scale,
+                                     a.out, a.lse, a.stream, ev_start, ev_stop, (int)p.n_sets);
     if (p.single)
         return launch_attention(a.q, a.k, a.v, a.col_start, a.col_end, a.n_ranges, nullptr, nullptr, a.B, a.H, a.N,
                                 a.d, a.scale, a.out, a.lse, a.stream, ev_start, ev_stop, a.fp8_scales, (int)p.n_sets,

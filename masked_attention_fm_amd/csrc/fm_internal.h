@@ -99,6 +99,14 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, const i
                             const float* fp8_scales = nullptr, int n_sets = 1, bool fp8_weights = false,
                             int split = 1, float* part = nullptr, unsigned* counters = nullptr, int groups = 1);
 
+// Small problems: one workgroup per 32 query rows of one (b, h), whose
+// wavefronts share the rows' key blocks and combine their states in LDS
+// (bf16; no records, no workspace).
+hipError_t launch_attention_rows(const void* q, const void* k, const void* v, const int32_t* col_start,
+                                 const int32_t* col_end, int n_iv, int64_t B, int64_t H, int64_t N, int64_t d,
+                                 float scale, void* out, float* lse, hipStream_t stream, hipEvent_t start,
+                                 hipEvent_t stop, int n_sets = 1);
+
 // The forward pass's launch sequence (fm_forward.hip).
 struct FwdArgs {
     const void *q, *k, *v;
@@ -120,10 +128,11 @@ struct FwdPlan {
     int64_t n_q, n_kv, n_sets, M;
     size_t meta_bytes, int_bytes, sched_bytes;
     bool single;               // the attention kernel alone (no records, no order)
+    bool rows;                 // single, as the 32-row slice kernel
     int split;                 // pieces per work item's key range (single launches only; 1: none)
     int groups;                // wavefront groups sharing each workgroup's range (single launches; 1: none)
     size_t part_bytes;         // the pieces' partial states
-    size_t total() const { return single ? part_bytes : meta_bytes + 2 * int_bytes + sched_bytes; }
+    size_t total() const { return single ? (rows ? 0 : part_bytes) : meta_bytes + 2 * int_bytes + sched_bytes; }
 };
 
 // Splitting the key ranges of small single launches: a power of two of pieces
@@ -147,7 +156,10 @@ inline size_t split_part_bytes(int64_t items, int64_t split, int64_t d) {
 }
 // split_keys: cut small single launches' key ranges (groups, and with
 // across_workgroups also workgroups, which need the workspace and counters).
-FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys, bool across_workgroups);
+// row_slices_max: single launches of at most this many 32-row slices
+// (B * H * ceil(N/32)) run the slice kernel (0: never).
+FwdPlan fwd_plan(const FwdArgs& a, bool single_launch, bool split_keys, bool across_workgroups,
+                 int64_t row_slices_max);
 
 // Queues the preprocessor, the scheduler (unless natural order) and the
 // attention kernel on a.stream, with ws (p.total() bytes of device memory) as

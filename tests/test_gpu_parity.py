@@ -225,14 +225,34 @@ def small_intervals(mask, B, N, rng):
     raise ValueError(mask)
 
 
+class row_slices:
+    """Sets FM_OPT_ROW_SLICES for a block of calls (the 32-row slice kernel of small single
+    launches: 0 turns it off) and restores the library default afterwards."""
+
+    DEFAULT = 512
+
+    def __init__(self, value):
+        self.value = value
+
+    def __enter__(self):
+        fm.fm_set_option(fm.FM_OPT_ROW_SLICES, self.value)
+
+    def __exit__(self, *exc):
+        fm.fm_set_option(fm.FM_OPT_ROW_SLICES, self.DEFAULT)
+
+
+@pytest.mark.parametrize("launch", ["slices", "blocks"])
 @pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_attention_small(case):
+def test_attention_small(case, launch):
+    """Every small case both ways: one workgroup per 32-row slice (the default for problems
+    this small) and one per 128-row query block."""
     B, H, N, d, mask = case
     rng = np.random.default_rng(N * 7 + d)
     s, e = small_intervals(mask, B, N, rng)
     q, k, v = inputs.make_qkv(B, H, N, d, seed=N + d)
-    log(f"attention small {case}")
-    check_case(q, k, v, s, e, inputs.default_scale(d), f"small {case}")
+    log(f"attention small {case} {launch}")
+    with row_slices(row_slices.DEFAULT if launch == "slices" else 0):
+        check_case(q, k, v, s, e, inputs.default_scale(d), f"small {case} {launch}")
 
 
 def test_q_zero_closed_form():
@@ -448,15 +468,16 @@ def test_split_key_ranges(case):
     q, k, v = inputs.make_qkv(B, H, N, d, seed=N + 3)
     scale = inputs.default_scale(d)
     log(f"split key ranges {case}")
-    check_case(q, k, v, s, e, scale, f"split {case}")
     args = to_dev(q, k, v, np.ascontiguousarray(s), np.ascontiguousarray(e))
-    o1, l1 = fm.fm_attn_fwd(*args, scale)
-    o2, l2 = fm.fm_attn_fwd(*args, scale)
-    try:
-        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 0)
-        o3, l3 = fm.fm_attn_fwd(*args, scale)
-    finally:
-        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 1)
+    with row_slices(0):                                 # the 128-row kernel's pieces
+        check_case(q, k, v, s, e, scale, f"split {case}")
+        o1, l1 = fm.fm_attn_fwd(*args, scale)
+        o2, l2 = fm.fm_attn_fwd(*args, scale)
+        try:
+            fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 0)
+            o3, l3 = fm.fm_attn_fwd(*args, scale)
+        finally:
+            fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2), "a repeated split call changed its result"
     dO = (o1.float() - o3.float()).abs().max().item()
@@ -465,4 +486,49 @@ def test_split_key_ranges(case):
     dL = (l1[fin] - l3[fin]).abs().max().item() if fin.any() else 0.0
     log(f"  split vs unsplit: max|dO| {dO:.3e} (bf16 output), max|dLSE| {dL:.3e}")
     # at most one bf16 ulp of the output (a different fp32 sum can round the other way)
+    assert dO <= 2 ** -7 * max(1.0, o3.float().abs().max().item()) and dL <= 1e-5
+
+
+ROW_SLICE_CASES = [
+    # (B, H, N, d, kind): small single launches run as one workgroup per 32-row slice,
+    # whose wavefronts (8 at d = 64, 4 at d = 128) share the slice's key blocks
+    (1, 2, 512, 64, "causal"),          # the tiny causal workload's shape: up to 8 key blocks
+    (1, 1, 100, 64, "causal"),          # fewer key blocks than wavefronts, ragged slice
+    (1, 1, 1000, 128, "random_empty"),  # ragged tail, empty rows, wavefronts with no block
+    (2, 3, 333, 64, "docs"),            # several documents per slice
+    (1, 2, 1024, 128, "sliding"),       # boundary blocks on both sides
+    (1, 1, 2048, 64, "causal"),         # 32 key blocks: four per wavefront
+    (2, 2, 600, 128, "prefix"),
+    (1, 1, 300, 128, "out_of_range"),   # the dense-mask meaning of any int32 values
+]
+
+
+@pytest.mark.parametrize("case", ROW_SLICE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_row_slices(case):
+    """The slice kernel against the oracle to the usual bars, against the unsplit 128-row
+    launch to fp32 rounding (the wavefronts' states are combined exactly up to the order of
+    additions), and the same bits on a repeated call."""
+    B, H, N, d, kind = case
+    rng = np.random.default_rng(N + 5 * d + H)
+    s, e = small_intervals(kind, B, N, rng)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=N + 11)
+    scale = inputs.default_scale(d)
+    log(f"row slices {case}")
+    args = to_dev(q, k, v, np.ascontiguousarray(s), np.ascontiguousarray(e))
+    with row_slices(row_slices.DEFAULT):
+        check_case(q, k, v, s, e, scale, f"row slices {case}")
+        o1, l1 = fm.fm_attn_fwd(*args, scale)
+        o2, l2 = fm.fm_attn_fwd(*args, scale)
+    try:
+        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 0)     # one workgroup per 128-row query block
+        o3, l3 = fm.fm_attn_fwd(*args, scale)
+    finally:
+        fm.fm_set_option(fm.FM_OPT_SPLIT_KEYS, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "a repeated call changed its result"
+    fin = torch.isfinite(l3)
+    assert torch.equal(fin, torch.isfinite(l1)), "slices and blocks disagree on empty rows"
+    dO = (o1.float() - o3.float()).abs().max().item()
+    dL = (l1[fin] - l3[fin]).abs().max().item() if fin.any() else 0.0
+    log(f"  slices vs blocks: max|dO| {dO:.3e} (bf16 output), max|dLSE| {dL:.3e}")
     assert dO <= 2 ** -7 * max(1.0, o3.float().abs().max().item()) and dL <= 1e-5

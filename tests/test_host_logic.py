@@ -95,6 +95,8 @@ def test_counter_kernel_filter():
     # the small-problem launches' instances (one or two wavefront groups) are the same kernel
     for prec in (3, 4):
         assert counters.kind_of(f"void fm::(anonymous namespace)::attn_fwd_kernel<128, 2, {prec}>(int)") == "attention"
+    # and so is the 32-row slice kernel of the smallest problems
+    assert counters.kind_of("void fm::(anonymous namespace)::attn_fwd_rows_kernel<64, 1>(int)") == "attention"
     for name in ("attn_fwd_kernel<128, 1, 1>", "attn_fwd_kernel<128, 2, 2>", "bwd_dq_kernel<128, 1>",
                  "prep_small_kernel<1>"):
         assert counters.kind_of(name) == ""
