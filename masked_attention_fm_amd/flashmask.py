@@ -109,9 +109,10 @@ def _require_scale(scale):
 
 
 def _dev_tensor(x: torch.Tensor, name: str, dtype: torch.dtype):
+    # (dtypes are singletons: `is` is the exact test and the cheapest one)
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if x.dtype != dtype:
+    if x.dtype is not dtype:
         raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
     if not x.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -126,7 +127,7 @@ def fm_attn_tile_shape(d: int) -> Tuple[int, int]:
 def _intervals(col_start: torch.Tensor, col_end: torch.Tensor, shape: Tuple[int, ...], what: str):
     _dev_tensor(col_start, "col_start", torch.int32)
     _dev_tensor(col_end, "col_end", torch.int32)
-    if tuple(col_start.shape) != shape or tuple(col_end.shape) != shape:
+    if col_start.shape != shape or col_end.shape != shape:
         raise ValueError(f"col_start / col_end must be {what}, got {tuple(col_start.shape)} "
                          f"and {tuple(col_end.shape)}")
 
@@ -218,9 +219,9 @@ def _attn(func: str, q, k, v, col_start, col_end, n_ranges: Optional[int], scale
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
         _dev_tensor(lse, "lse", torch.float32)
-        if tuple(lse.shape) != (B, H, N):
+        if lse.shape != (B, H, N):
             raise ValueError("lse must be [B, H, N]")
-    L = lib()
+    L = _lib if _lib is not None else lib()
     if n_ranges is None:
         status = L.fm_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), col_start.data_ptr(),
                                col_end.data_ptr(), B, H, N, d, float(scale), out.data_ptr(), lse.data_ptr(),
@@ -234,8 +235,9 @@ def _attn(func: str, q, k, v, col_start, col_end, n_ranges: Optional[int], scale
 
 
 def _qkv(q, k, v):
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        _dev_tensor(x, name, torch.bfloat16)
+    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(k, "k", torch.bfloat16)
+    _dev_tensor(v, "v", torch.bfloat16)
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
     return q.shape
