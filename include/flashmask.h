@@ -328,6 +328,11 @@ enum {
                                    0: neither.  The results differ from the unsplit ones only by the
                                    order of fp32 additions.  fm_attn_fwd_noalloc uses the groups
                                    but never splits over workgroups. */
+    FM_OPT_BWD_FUSED_PREP = 6,  /* backward: 1 (default) prepares both gradient kernels' tile records in
+                                   one launch on small problems whose key blocks cannot split (at most
+                                   FM_OPT_BWD_SPLIT_CHUNKS query chunks of 64 rows, at most 1024 chunks in
+                                   all, one stream); 0: always the separate preprocessing launches.
+                                   Results are identical either way. */
     FM_OPT_ROW_SLICES = 5       /* forward, bf16 single launches with FM_OPT_SPLIT_KEYS on: problems of
                                    at most this many slices of 32 query rows (B * H * ceil(N/32);
                                    default 512, 0: never) run one workgroup per slice, whose

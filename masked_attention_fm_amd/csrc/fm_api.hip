@@ -43,6 +43,7 @@ int g_single_launch = 1;   // 1: small problems run the attention kernel alone
 int g_split_keys = 1;      // 1: single launches split long key ranges over several workgroups
 int64_t g_row_slices = 512;  // single launches of at most this many 32-row slices run the slice kernel
 int g_bwd_min_chunks = 32; // smallest piece of a split key block (query chunks); 0: never split
+int g_bwd_fused_prep = 1;  // 1: small backward problems prepare both kernels' records in one launch
 
 // ---------------------------------------------------------------- workspace
 //
@@ -202,6 +203,11 @@ FM_API int fm_set_option(int option, int64_t value) {
     if (option == FM_OPT_ROW_SLICES) {
         if (value < 0 || value > (1 << 20)) return FM_ERR_INVALID_ARG;
         g_row_slices = value;
+        return FM_OK;
+    }
+    if (option == FM_OPT_BWD_FUSED_PREP) {
+        if (value != 0 && value != 1) return FM_ERR_INVALID_ARG;
+        g_bwd_fused_prep = (int)value;
         return FM_OK;
     }
     if (option == FM_OPT_BWD_SPLIT_CHUNKS) {
@@ -539,6 +545,20 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
     auto* sched_k = reinterpret_cast<int32_t*>(w + o_sched_k);
 
     FM_HIP(fm::launch_bwd_rowdot(out, dout, B * H * N, d, dd, stream));
+    // Small problems whose key blocks cannot split (no block sees more query
+    // chunks than the smallest piece holds, so the split would leave every
+    // block whole): one launch prepares both kernels' records, the dQ kernel
+    // runs in natural order and no reduction follows.  Same results.
+    const int min_chunks = g_bwd_min_chunks > 0 ? g_bwd_min_chunks : (1 << 30);
+    if (g_bwd_fused_prep == 1 && !two_streams && n_qc <= min_chunks && Mc <= fm::kBwdFusedMaxChunks) {
+        FM_HIP(fm::launch_bwd_prep_fused(col_start, col_end, n_ranges, B, N, (int)n_sets, meta_q, meta_c, pieces, pslot,
+                                         order_k, stream));
+        FM_HIP(fm::launch_bwd_dq(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_q, nullptr, B, H, N, d,
+                                 scale, dq, stream, (int)n_sets));
+        FM_HIP(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, pieces, pslot,
+                                   order_k, B, H, N, d, scale, dk, dv, part, stream, (int)n_sets));
+        return FM_OK;
+    }
     if (two_streams) {
         FM_HIP(hipEventRecord(side.fork, stream));
         FM_HIP(hipStreamWaitEvent(side.stream, side.fork, 0));
@@ -571,7 +591,6 @@ int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, 
         FM_TRY(fm::launch_preprocess(col_start, col_end, n_ranges, B, N, fm::kBwdRows, fm::kBwdKeys, meta_c,
                                      nullptr, nullptr, stream, (int)n_sets));
         FM_TRY(fm::launch_kv_ranges(meta_c, n_ranges, B, N, kvr, work_k, stream, (int)n_sets));
-        const int min_chunks = g_bwd_min_chunks > 0 ? g_bwd_min_chunks : (1 << 30);
         FM_TRY(fm::launch_bwd_split(kvr, B * n_kb, (int)n_sets, min_chunks, pieces, pslot, pwork, splits, stream));
         FM_TRY(fm::launch_schedule(pwork, Mp, order_k, stream, Lp, 0, (int)n_qc, sched_k));
         FM_TRY(fm::launch_bwd_dkdv(q, k, v, dout, lse, dd, col_start, col_end, n_ranges, meta_c, pieces, pslot,

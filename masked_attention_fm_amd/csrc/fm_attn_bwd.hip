@@ -1202,6 +1202,100 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
 }
 
+// ---------------------------------------------------------------- small problems: one preparation launch
+//
+// When no key block can be split (no block sees more query chunks than the
+// smallest piece holds) and the problem is small, the records of both
+// gradient kernels come from one workgroup instead of five launches: the
+// query blocks' records of the dQ kernel (run in natural order), the query
+// chunks' records, each key block's first and last live chunk, and the
+// one-piece table with the identity order of the dK/dV kernel.  They are the
+// numbers the separate launches produce (the preprocessor's rule, the chunk
+// scan of kv_ranges_kernel, bwd_split_kernel with nothing to split); only
+// the order of the gradient kernels' workgroups differs, which changes no
+// result.  The chunk records are kept in LDS for the chunk scan.
+constexpr int kPrepFusedThreads = 1024;
+template <int NIV>
+__global__ __launch_bounds__(kPrepFusedThreads) void bwd_prep_fused_kernel(
+    const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_end, int N, int B, int n_sets,
+    TileMeta* __restrict__ meta_q, TileMeta* __restrict__ meta_c, int4* __restrict__ pieces,
+    int32_t* __restrict__ pslot, int32_t* __restrict__ order_k, int Lp) {
+    __shared__ TileMeta chunk_meta[kBwdFusedMaxChunks * NIV];
+    constexpr int kWv = kPrepFusedThreads / 64;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int n_q = (N + kBr - 1) / kBr, n_kv = (N + kBc - 1) / kBc;
+    const int n_qc = (N + kBwdRows - 1) / kBwdRows, n_kb = (N + kBwdKeys - 1) / kBwdKeys;
+    const int Mq = n_sets * B * n_q, Mc = n_sets * B * n_qc, Mk = n_sets * B * n_kb;
+    // records: query blocks (kBr rows, kBc keys) then query chunks (kBwdRows
+    // rows, kBwdKeys keys), one wavefront each, items of one interval set
+    // contiguous (as preprocess_kernel numbers them)
+    for (int item = wv; item < Mq + Mc; item += kWv) {
+        const bool chunk = item >= Mq;
+        const int it = chunk ? item - Mq : item;
+        const int nt = chunk ? n_qc : n_q;
+        const int g = it / (B * nt);
+        const int rem = it - g * (B * nt);
+        const int b = rem / nt;
+        const int t = rem - b * nt;
+        TileMeta m[NIV];
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) {
+            const int64_t off = (((int64_t)b * n_sets + g) * NIV + k) * N;
+            int inv = 0;
+            m[k] = chunk ? query_block_meta(col_start + off, col_end + off, t, N, kBwdRows, kBwdKeys, n_kb, lane, &inv)
+                         : query_block_meta(col_start + off, col_end + off, t, N, kBr, kBc, n_kv, lane, &inv);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                if (chunk) {
+                    meta_c[it * NIV + k] = m[k];
+                    chunk_meta[it * NIV + k] = m[k];
+                } else {
+                    meta_q[it * NIV + k] = m[k];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // key-block items (set B + b) n_kb + J: first and last chunk whose
+    // non-skip ranges hold J, as one piece
+    for (int item = wv; item < Mk; item += kWv) {
+        const int sb = item / n_kb;
+        const int J = item - sb * n_kb;
+        int lo = INT_MAX, hi = INT_MIN, count = 0;
+        for (int t = lane; t < n_qc; t += 64) {
+            bool live = false;
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+                const TileMeta m = chunk_meta[(sb * n_qc + t) * NIV + k];
+                live |= m.x <= J && J <= m.y;
+            }
+            if (live) {
+                lo = min(lo, t);
+                hi = max(hi, t);
+                ++count;
+            }
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        count = wave_sum(count);
+        if (lane == 0) {
+            pieces[item] = make_int4(item, count > 0 ? lo : 0, count > 0 ? hi : -1, 1);
+            pslot[item] = -1;
+        }
+    }
+    // the places of extra pieces (one interval set) stay unused; identity order
+    for (int e = threadIdx.x; e < n_sets * Lp; e += kPrepFusedThreads) {
+        order_k[e] = e;
+        if (e >= Mk) {
+            pieces[e] = make_int4(-1, 0, -1, 0);
+            pslot[e] = -1;
+        }
+    }
+}
+
 int use_xcd_heads(int64_t H, int64_t items_per_head) { return (H % 8 == 0 && items_per_head >= 128) ? 1 : 0; }
 
 }  // namespace
@@ -1234,6 +1328,20 @@ hipError_t launch_bwd_split(const int4* kvr, int64_t items, int n_sets, int min_
     hipLaunchKernelGGL(bwd_split_kernel, dim3(1), dim3(kSplitThreads), 0, stream, kvr, (int)items, n_sets,
                        min_chunks, pieces, pslot, pwork, splits);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep_fused(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B, int64_t N,
+                                 int n_sets, TileMeta* meta_q, TileMeta* meta_c, int4* pieces, int32_t* pslot,
+                                 int32_t* order_k, hipStream_t stream) {
+    const int64_t n_qc = (N + kBwdRows - 1) / kBwdRows;
+    if (n_sets * B * n_qc > kBwdFusedMaxChunks) return hipErrorInvalidValue;
+    const int64_t Lp = bwd_piece_entries(B * ((N + kBwdKeys - 1) / kBwdKeys), n_sets);
+    return dispatch_ranges(n_iv, [&](auto niv) {
+        hipLaunchKernelGGL(bwd_prep_fused_kernel<decltype(niv)::value>, dim3(1), dim3(kPrepFusedThreads), 0, stream,
+                           col_start, col_end, (int)N, (int)B, n_sets, meta_q, meta_c, pieces, pslot, order_k,
+                           (int)Lp);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_bwd_reduce(const int4* splits, const float* part, int64_t H, int64_t N, int64_t d, int64_t n_kb,

@@ -219,6 +219,14 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            const TileMeta* meta_c, const int4* pieces, const int32_t* pslot, const int32_t* order,
                            int64_t B, int64_t H, int64_t N, int64_t d, float scale, float* dk, float* dv,
                            float* part, hipStream_t stream, int n_sets = 1);
+// Small problems whose key blocks cannot split: the dQ kernel's query-block
+// records (natural order), the query chunks' records and the dK/dV kernel's
+// one-piece table with the identity order, from one workgroup (at most
+// kBwdFusedMaxChunks query chunks in all).
+constexpr int kBwdFusedMaxChunks = 1024;
+hipError_t launch_bwd_prep_fused(const int32_t* col_start, const int32_t* col_end, int n_iv, int64_t B, int64_t N,
+                                 int n_sets, TileMeta* meta_q, TileMeta* meta_c, int4* pieces, int32_t* pslot,
+                                 int32_t* order_k, hipStream_t stream);
 // Adds the partial sums of split key blocks to dK, dV.
 hipError_t launch_bwd_reduce(const int4* splits, const float* part, int64_t H, int64_t N, int64_t d, int64_t n_kb,
                              float* dk, float* dv, hipStream_t stream);

@@ -23,6 +23,7 @@ FM_OPT_BWD_SPLIT_CHUNKS = 2
 FM_OPT_SINGLE_LAUNCH = 3
 FM_OPT_SPLIT_KEYS = 4
 FM_OPT_ROW_SLICES = 5
+FM_OPT_BWD_FUSED_PREP = 6
 FM_MAX_RANGES = 4
 FM_FP8_SCORES, FM_FP8_ALL = 0, 1
 

@@ -120,6 +120,8 @@ def test_options_and_strings(L):
     assert L.fm_set_option(fmb.FM_OPT_ROW_SLICES, -1) == fmb.FM_ERR_INVALID_ARG
     assert L.fm_set_option(fmb.FM_OPT_ROW_SLICES, (1 << 20) + 1) == fmb.FM_ERR_INVALID_ARG
     assert L.fm_set_option(fmb.FM_OPT_ROW_SLICES, 512) == fmb.FM_OK
+    assert L.fm_set_option(fmb.FM_OPT_BWD_FUSED_PREP, 2) == fmb.FM_ERR_INVALID_ARG
+    assert L.fm_set_option(fmb.FM_OPT_BWD_FUSED_PREP, 1) == fmb.FM_OK
     for s in range(5):
         assert L.fm_status_string(s)
     assert b"unknown" in L.fm_status_string(42)

@@ -284,3 +284,69 @@ def test_bwd_split_sinks_window_workload_heads():
     ref = oracle_bwd_by_head(q, k, v, do, spec.col_start, spec.col_end, scale)
     worst = compare_grads(a, ref, "bwd S1 four heads (split) vs oracle")
     log(f"bwd S1: worst relative error {worst:.3e}")
+
+
+FUSED_PREP_CASES = [
+    # (B, H, N, d, kind, ranges): small problems whose key blocks cannot split, prepared by one
+    # launch; the same bits as the separate preprocessing launches
+    (1, 2, 512, 64, "causal", 1),       # the tiny causal workload's shape
+    (2, 3, 333, 128, "random", 1),      # ragged tail
+    (1, 2, 515, 128, "random_empty", 1),
+    (1, 1, 300, 64, "out_of_range", 1),
+    (2, 1, 1500, 128, "prefix", 1),
+    (1, 2, 700, 64, "random", 3),       # several ranges per row
+    (1, 1, 40, 128, "causal", 1),       # one query chunk, one key block
+]
+
+
+@pytest.mark.parametrize("case", FUSED_PREP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_fused_preparation_matches_separate_launches(case):
+    B, H, N, d, kind, K = case
+    rng = np.random.default_rng(N + 17 * K)
+    if K == 1:
+        s, e = small_intervals(kind, B, N, rng)
+    else:
+        s, e = inputs.random_multi_intervals(rng, B, K, N, empty_frac=0.1, max_width=N // 3)
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=N + 5)
+    do = dout_for(q.shape, N)
+    scale = inputs.default_scale(d)
+    log(f"bwd fused preparation {case}")
+    fused = run_bwd(q, k, v, do, s, e, scale, K > 1)
+    try:
+        fm.fm_set_option(fm.FM_OPT_BWD_FUSED_PREP, 0)
+        separate = run_bwd(q, k, v, do, s, e, scale, K > 1)
+    finally:
+        fm.fm_set_option(fm.FM_OPT_BWD_FUSED_PREP, 1)
+    for name, a, b in zip(("dQ", "dK", "dV"), fused, separate):
+        assert np.array_equal(a, b), f"{case}: {name} differs between the fused and separate preparation"
+    if K == 1:
+        ref = oracle.attention_bwd(*(x.float().numpy() for x in (q, k, v, do)), s, e, scale)
+        compare_grads(fused, ref, f"bwd fused preparation {case}")
+
+
+def test_bwd_fused_preparation_per_head_sets():
+    """One interval set per head: the fused records are numbered by set like the separate ones."""
+    B, H, N, d = 2, 3, 400, 64
+    rng = np.random.default_rng(41)
+    s, e = inputs.random_multi_intervals(rng, B * H, 2, N, empty_frac=0.1, max_width=150)
+    s, e = np.ascontiguousarray(s.reshape(B, H, 2, N)), np.ascontiguousarray(e.reshape(B, H, 2, N))
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=43)
+    do = dout_for(q.shape, 44)
+    scale = inputs.default_scale(d)
+    qd, kd, vd, dod, sd, ed = to_dev(q, k, v, do, s, e)
+    out, lse = fm.fm_attn_fwd_per_head(qd, kd, vd, sd, ed, scale)
+
+    def grads():
+        g = [torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV) for _ in range(3)]
+        fm.fm_attn_bwd_per_head(qd, kd, vd, out, dod, lse, sd, ed, scale, dq=g[0], dk=g[1], dv=g[2])
+        torch.cuda.synchronize()
+        return g
+
+    fused = grads()
+    try:
+        fm.fm_set_option(fm.FM_OPT_BWD_FUSED_PREP, 0)
+        separate = grads()
+    finally:
+        fm.fm_set_option(fm.FM_OPT_BWD_FUSED_PREP, 1)
+    for a, b in zip(fused, separate):
+        assert torch.equal(a, b)

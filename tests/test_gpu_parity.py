@@ -500,6 +500,8 @@ ROW_SLICE_CASES = [
     (1, 1, 2048, 64, "causal"),         # 32 key blocks: four per wavefront
     (2, 2, 600, 128, "prefix"),
     (1, 1, 300, 128, "out_of_range"),   # the dense-mask meaning of any int32 values
+    (1, 16, 1024, 64, "causal"),        # exactly 512 slices: the largest problem the slice kernel takes
+    (1, 16, 1025, 64, "causal"),        # 528 slices: the 128-row kernel again (one ragged query block)
 ]
 
 
