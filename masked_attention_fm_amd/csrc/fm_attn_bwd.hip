@@ -268,29 +268,6 @@ __device__ __forceinline__ int4 wave_row_bounds(int s, int w, bool in_seq) {
                      wave_min(any ? s + w : (in_seq ? INT_MIN : INT_MAX)));
 }
 
-// Minimum or maximum over the wavefront with DPP moves (VALU latency, where
-// the swizzle butterfly makes five LDS round trips): the quad permutations
-// [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors, reduce each row
-// of 16 lanes; the four rows are combined from lanes 0, 16, 32 and 48.
-template <bool MAX>
-__device__ __forceinline__ int wave_reduce_dpp(int v) {
-    auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
-    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
-    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
-    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
-    v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
-    return op(op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-              op(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
-// wave_row_bounds for the per-chunk test of the dK/dV kernels.
-__device__ __forceinline__ int4 wave_row_bounds_dpp(int s, int w, bool in_seq) {
-    const bool any = s != kEmptyStart;
-    return make_int4(wave_reduce_dpp<false>(any ? s : INT_MAX), wave_reduce_dpp<true>(any ? s + w : INT_MIN),
-                     wave_reduce_dpp<true>(any ? s : (in_seq ? INT_MAX : INT_MIN)),
-                     wave_reduce_dpp<false>(any ? s + w : (in_seq ? INT_MIN : INT_MAX)));
-}
-
 // Blocks of 64 rows (keys for dQ, query rows for dK/dV) loaded straight from
 // global memory into LDS (buffer loads with an LDS destination: one
 // instruction writes lane l's 16 bytes to M0 + 16 l, a 1 KB segment per

@@ -68,7 +68,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = kBr / kWaves;     // 32
-constexpr int kVPad = 8;                       // bf16 padding per V^T row in LDS (16 B), FP8 inputs
 
 static_assert(kRowsPerWave == 32, "one 32x32 MFMA column block per wavefront");
 static_assert(kBc % 32 == 0 && kBc % 16 == 0, "key block is a multiple of the MFMA shapes");

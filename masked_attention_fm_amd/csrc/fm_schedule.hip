@@ -64,6 +64,7 @@ constexpr int kMaxPerThread = kSortSmall / kSortThreads;   // 16
 
 template <int E>
 __device__ __forceinline__ void bitonic_sort_regs(uint32_t (&v)[E], uint32_t* s) {
+    static_assert(E >= 1 && E <= kMaxPerThread && (E & (E - 1)) == 0, "a power of two, at most kMaxPerThread");
     constexpr int n = E * kSortThreads;
     const int t = threadIdx.x;
     for (int k = 2; k <= n; k <<= 1) {
