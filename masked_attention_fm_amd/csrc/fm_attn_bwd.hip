@@ -974,22 +974,33 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
 
     // ---- epilogue: lane holds dV (P wavefront) or dK (dS wavefront) of its key
     // at d = 32 nb + 8 g + 4 half + (0..3); a later piece of a split block
-    // writes its partial sums.
-    if (key < N) {
-        float* row = (dsw ? dK : dV) + (bh * N + key) * D;
-        if ((piece.w >> 16) != 0) {
-            float* pb = part + ((int64_t)pslot[pe] * H + h) * (kBwdKeys * D * 2);
-            row = pb + (key - J * kBwdKeys) * D + (dsw ? 0 : kBwdKeys * D);
-        }
-        const float f = dsw ? scale : 1.f;
+    // writes its partial sums.  The rows go out through LDS, idle after the
+    // last step's barrier (each wavefront stages its own 32 rows), so that
+    // every store writes whole rows: straight from the MFMA layout one store
+    // instruction would write 32-byte pieces of 32 rows.
+    constexpr int kOPitch = 4 * D + 16;                  // bytes per staged row (rows 4 banks apart)
+    constexpr int kLanesPerRow = 4 * D / 16;             // 16 bytes per lane
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    static_assert(2 * kWaves * 32 * kOPitch <= (int)sizeof(DkvSmem<D, NIV>), "the staged rows fit in LDS");
+    uint8_t* const ost = reinterpret_cast<uint8_t*>(&sm) + wave * 32 * kOPitch;
+    const float f = dsw ? scale : 1.f;
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
+    for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<float4*>(row + nb * 32 + 8 * g + 4 * half) =
-                    make_float4(f * acc[nb][4 * g], f * acc[nb][4 * g + 1], f * acc[nb][4 * g + 2],
-                                f * acc[nb][4 * g + 3]);
-        }
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(ost + r32 * kOPitch + 4 * (nb * 32 + 8 * g + 4 * half)) =
+                make_float4(f * acc[nb][4 * g], f * acc[nb][4 * g + 1], f * acc[nb][4 * g + 2], f * acc[nb][4 * g + 3]);
+    float* rows = (dsw ? dK : dV) + (bh * N + kw0) * D;  // the row of key kw0
+    if ((piece.w >> 16) != 0) {
+        float* pb = part + ((int64_t)pslot[pe] * H + h) * (kBwdKeys * D * 2);
+        rows = pb + (kw0 - J * kBwdKeys) * D + (dsw ? 0 : kBwdKeys * D);
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / kRowsPerStore; ++i) {
+        const int r = i * kRowsPerStore + lane / kLanesPerRow;
+        const int cb = 16 * (lane % kLanesPerRow);
+        const float4 v = *reinterpret_cast<const float4*>(ost + r * kOPitch + cb);
+        if (kw0 + r < N) *reinterpret_cast<float4*>(reinterpret_cast<uint8_t*>(rows + r * D) + cb) = v;
     }
 }
 
@@ -1165,16 +1176,43 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
 
     // ---- epilogue: lane holds dQ of its query at d = 32 nb + 8 g + 4 half + (0..3).
-    if (qrow < N) {
-        float* dq_row = dQ + (bh * N + qrow) * D;
+    // The rows go out through LDS so that every store writes whole rows (as in
+    // the dK/dV kernel), each wavefront staging its own rows; where the
+    // buffers cannot hold all 128 rows at once (d = 64) they go in two passes
+    // of 16 rows per wavefront (LDS operations of one wavefront take effect in
+    // issue order, so a pass may overwrite what the previous one read).  The
+    // barrier keeps the staging clear of another wavefront's reads of the
+    // staged intervals on a query block with no key blocks.
+    __syncthreads();
+    constexpr int kOPitch = 4 * D + 16;                  // bytes per staged row (rows 4 banks apart)
+    constexpr int kOPasses = kWaves * 32 * kOPitch <= (int)sizeof(DqSmem<D, NIV>) ? 1 : 2;
+    static_assert(kWaves * 32 * kOPitch <= kOPasses * (int)sizeof(DqSmem<D, NIV>), "the staged rows fit in LDS");
+    constexpr int kPassRows = 32 / kOPasses;
+    constexpr int kLanesPerRow = 4 * D / 16;             // 16 bytes per lane
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    static_assert(kPassRows % kRowsPerStore == 0, "whole stores per pass");
+    uint8_t* const ost = reinterpret_cast<uint8_t*>(&sm) + wave * kPassRows * kOPitch;
+    float* const rows = dQ + (bh * N + row0 + wave * 32) * D;   // the wavefront's first row
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
+    for (int pass = 0; pass < kOPasses; ++pass) {
+        if (r32 / kPassRows == pass) {
+            uint8_t* const orow = ost + (r32 - pass * kPassRows) * kOPitch;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                *reinterpret_cast<float4*>(dq_row + nb * 32 + 8 * g + 4 * half) =
-                    make_float4(scale * dqacc[nb][4 * g], scale * dqacc[nb][4 * g + 1], scale * dqacc[nb][4 * g + 2],
-                                scale * dqacc[nb][4 * g + 3]);
-            }
+            for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<float4*>(orow + 4 * (nb * 32 + 8 * g + 4 * half)) =
+                        make_float4(scale * dqacc[nb][4 * g], scale * dqacc[nb][4 * g + 1],
+                                    scale * dqacc[nb][4 * g + 2], scale * dqacc[nb][4 * g + 3]);
+        }
+#pragma unroll
+        for (int i = 0; i < kPassRows / kRowsPerStore; ++i) {
+            const int r = i * kRowsPerStore + lane / kLanesPerRow;
+            const int cb = 16 * (lane % kLanesPerRow);
+            const float4 v = *reinterpret_cast<const float4*>(ost + r * kOPitch + cb);
+            const int rr = pass * kPassRows + r;
+            if (row0 + wave * 32 + rr < N)
+                *reinterpret_cast<float4*>(reinterpret_cast<uint8_t*>(rows + rr * D) + cb) = v;
         }
     }
 }
