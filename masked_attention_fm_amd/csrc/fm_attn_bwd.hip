@@ -706,6 +706,15 @@ __device__ __forceinline__ void lds_write_b128(uint32_t addr, float4 v) {
     asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(bits), "i"(OFF) : "memory");
 }
 
+// One 1 KB slab into LDS: lane l's 16 bytes from byte src of the tensor to
+// dst + 16 l.
+template <typename Ptr>
+__device__ __forceinline__ void dma_kv_slab(__amdgpu_buffer_rsrc_t rs, Ptr dst, int src) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the LDS address-space cast exists in the device pass only
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, src, 0, 0, 0);
+#endif
+}
+
 template <int D, int NIV>
 struct alignas(16) DkvSmem {
     alignas(16) uint8_t q[3][SegLayout<D>::kBytes];     // Q of chunks s-1, s, s+1 (index chunk % 3)
@@ -751,14 +760,34 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const int key = J * kBwdKeys + kw * 32 + r32;
     const int kw0 = J * kBwdKeys + kw * 32;
 
-    // K (P wavefront) or V (dS wavefront) of this lane's key as MFMA B
-    // operands: [key][16 cs + 8 half .. +7].
-    const uint16_t* kv_src = dsw ? V : K;
-    bf16x8 kv[D / 16];
+    // The key block's K and V rows go into the P exchange buffer (idle until
+    // the first step) in whole-kilobyte pieces, the P wavefronts loading K and
+    // the dS wavefronts V; below, each lane reads its key's row from there
+    // (K for the P wavefront, V for the dS wavefront) as MFMA B operands,
+    // [key][16 cs + 8 half .. +7].  Loaded straight into registers, each
+    // instruction would fetch 32-byte pieces of 32 rows.  Rows are stored
+    // whole, their 16-byte chunks permuted (chunk c of row R in slot
+    // c ^ (R mod chunks per row)) so that the 32 rows of one read meet no bank
+    // conflict; rows past N arrive as zeros (the buffer range check).
+    constexpr int kKvRow = 2 * D;                         // bytes per row
+    constexpr int kKvChunks = kKvRow / 16;
+    constexpr int kKvSlabs = 2 * kBwdKeys * kKvRow / 1024;  // K then V, 1 KB per load instruction
+    constexpr int kKvSlabsPerWave = kKvSlabs / (2 * kWaves);
+    static_assert(2 * kBwdKeys * kKvRow <= (int)sizeof(sm.xch), "K and V of a key block fit the exchange buffer");
+    static_assert(kKvSlabs % (2 * kWaves) == 0 && kKvChunks <= 64, "whole slabs per wavefront");
+    uint8_t* const kvst = reinterpret_cast<uint8_t*>(&sm.xch[0][0][0][0][0]);
+    {
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const __amdgpu_buffer_rsrc_t trs = slice_rsrc((wv >= kWaves ? V : K) + bh * N * D, N * D * 2);
 #pragma unroll
-    for (int cs = 0; cs < D / 16; ++cs)
-        kv[cs] = key < N ? *reinterpret_cast<const bf16x8*>(kv_src + (bh * N + key) * D + cs * 16 + half * 8)
-                         : bf16x8{};
+        for (int u = 0; u < kKvSlabsPerWave; ++u) {
+            const int m = wv * kKvSlabsPerWave + u;               // slab: rows of K (m < kKvSlabs / 2), then V
+            const int R = (m % (kKvSlabs / 2)) * (1024 / kKvRow) + lane / kKvChunks;
+            const int c = (lane % kKvChunks) ^ (R % kKvChunks);
+            dma_kv_slab(trs, kvst + m * 1024, (J * kBwdKeys + R) * kKvRow + 16 * c);
+        }
+    }
+    bf16x8 kv[D / 16];
     floatx16 acc[D / 32];                        // dV^T (P wavefront) or dK^T (dS wavefront)
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) acc[nb] = floatx16{};
@@ -795,6 +824,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        {
+            const uint8_t* rowp = kvst + (dsw ? kBwdKeys * kKvRow : 0) + (kw * 32 + r32) * kKvRow;
+            const int rsw = (kw * 32 + r32) % kKvChunks;
+#pragma unroll
+            for (int cs = 0; cs < D / 16; ++cs)
+                kv[cs] = *reinterpret_cast<const bf16x8*>(rowp + 16 * ((2 * cs + half) ^ rsw));
+        }
+        __syncthreads();   // every K/V row is in registers before the first P is written there
         // The dS wavefront's pending chunk (the previous step's): its dP tiles,
         // whether it was skipped.
         floatx16 dpp[2] = {};
@@ -978,6 +1015,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     // last step's barrier (each wavefront stages its own 32 rows), so that
     // every store writes whole rows: straight from the MFMA layout one store
     // instruction would write 32-byte pieces of 32 rows.
+    // (A piece with no live chunk skipped the steps: its K/V loads are waited
+    // for here, so that none lands in the staged rows.)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     constexpr int kOPitch = 4 * D + 16;                  // bytes per staged row (rows 4 banks apart)
     constexpr int kLanesPerRow = 4 * D / 16;             // 16 bytes per lane
     constexpr int kRowsPerStore = 64 / kLanesPerRow;
