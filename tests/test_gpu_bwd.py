@@ -77,6 +77,32 @@ def test_bwd_small(case):
     check_bwd(q, k, v, s, e, inputs.default_scale(d), f"bwd {case}", seed=N)
 
 
+@pytest.mark.parametrize("d,fused", [(64, 1), (128, 1), (128, 0)])
+def test_bwd_key_blocks_no_query_attends(d, fused):
+    """Key blocks that no query attends: every row of batch element 0 attends keys [0, 100]
+    only, and every row of batch element 1 attends nothing.  Their key blocks have no live
+    query chunk (the kernel's start issues their K and V loads, then skips the steps), so
+    dK and dV there are exactly 0 and everything else matches the oracle; on both
+    preparation paths."""
+    B, H, N = 2, 2, 700
+    s = np.zeros((B, N), np.int32)
+    e = np.full((B, N), 100, np.int32)
+    s[1], e[1] = 5, 4                      # empty ranges
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=31 + d)
+    do = dout_for(q.shape, 77)
+    log(f"bwd unattended key blocks d={d} fused={fused}")
+    fm.fm_set_option(fm.FM_OPT_BWD_FUSED_PREP, fused)
+    try:
+        got = run_bwd(q, k, v, do, s, e, inputs.default_scale(d), False)
+    finally:
+        fm.fm_set_option(fm.FM_OPT_BWD_FUSED_PREP, 1)
+    for g in got[1:]:
+        assert np.all(g[0, :, 101:] == 0.0) and np.all(g[1] == 0.0), "unattended keys must get zero gradients"
+    assert np.all(got[0][1] == 0.0), "rows that attend nothing must get dQ = 0"
+    ref = oracle.attention_bwd(*(x.float().numpy() for x in (q, k, v, do)), s, e, inputs.default_scale(d))
+    compare_grads(got, ref, f"bwd unattended key blocks d={d} fused={fused}")
+
+
 BWD_MULTI_CASES = [
     (1, 2, 1000, 128, 2, "sinks"),
     (2, 1, 700, 64, 3, "random"),
